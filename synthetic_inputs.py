@@ -1,0 +1,121 @@
+"""Seeded synthetic workloads shared by the tests, the bench and the oracle runs.
+
+This module only names shapes and draws random numbers; it holds none of the
+attention arithmetic. Both the HIP path and the CPU oracle are fed the same
+tensors from here.
+
+Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws Q, K, V
+and then dO, in that order, as float32 standard normals, each rounded to
+bfloat16 (round to nearest even). Layout is contiguous [B, H, N, d].
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    backward: bool
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to float32, the scale every workload uses."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32))
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def pairs(self) -> int:
+        """(query, key) pairs per (b, hq): N^2, or N(N+1)/2 under the causal mask."""
+        return self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+
+    def fwd_flops(self) -> float:
+        """Algorithmic forward flops: two matmuls of 2*d flops per allowed pair."""
+        return 4.0 * self.d * self.pairs() * self.B * self.Hq
+
+    def bwd_flops(self) -> float:
+        """Algorithmic backward flops: five such matmuls (2.5x the forward)."""
+        return 2.5 * self.fwd_flops()
+
+    def fwd_bytes(self) -> float:
+        """Read Q, K, V once, write O (bf16) and LSE (fp32) once."""
+        q = self.B * self.Hq * self.N * self.d * 2
+        kv = 2 * self.B * self.Hkv * self.N * self.d * 2
+        return q + kv + q + self.B * self.Hq * self.N * 4
+
+    def bwd_bytes(self) -> float:
+        """Read Q, K, V, O, dO, LSE; write dQ, dK, dV; D row term written once, read twice."""
+        q = self.B * self.Hq * self.N * self.d * 2
+        kv = self.B * self.Hkv * self.N * self.d * 2
+        rows = self.B * self.Hq * self.N * 4
+        return 3 * q + 2 * kv + rows + (q + 2 * kv) + 3 * rows
+
+
+def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note=""):
+    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note)
+
+
+# The five workload families (index k gives seed 1000 + k; the sequence sweep
+# adds N). Shapes and distributions as named in the project's headline
+# configuration list; the YOLO-like case flattens a 20x20 feature map, as in
+# the lpnh.cn YOLO11 article, section 1.2.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        _w("c1_yolo_n400", 1, 8, 8, 400, 64, False, False, 1001,
+           "YOLO C2PSA-like, 20x20 map flattened"),
+        *[
+            _w(f"c2_mha_n{n}", 4, 16, 16, n, 64, False, False, 1002 + n,
+               "non-causal MHA sequence sweep")
+            for n in (512, 1024, 2048, 4096)
+        ],
+        _w("c3_causal_7b", 2, 32, 32, 4096, 128, True, False, 1003, "7B-like"),
+        _w("c4_gqa_70b", 1, 64, 8, 8192, 128, True, False, 1004, "70B-like GQA, G=8"),
+        _w("c4_mqa_70b", 1, 64, 1, 8192, 128, True, False, 1004, "MQA, G=64"),
+        _w("c5_bwd_d128", 1, 16, 16, 16384, 128, True, True, 1005, "fwd+bwd"),
+        _w("c5_bwd_d80", 1, 16, 16, 4096, 80, True, True, 1005, "fwd+bwd, d=80"),
+    ]
+}
+
+
+def make_inputs(B, Hq, Hkv, N, d, seed, with_do=False):
+    """Draw bf16 Q [B,Hq,N,d], K, V [B,Hkv,N,d] (and dO like Q) on the CPU."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    out = {"q": q, "k": k, "v": v}
+    if with_do:
+        out["do"] = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, with_do=w.backward)
+
+
+def to_f64(t: torch.Tensor):
+    """Exact float64 numpy copy of a (bf16) CPU or GPU tensor."""
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def score_matrix_bytes(B, H, N, elem_bytes):
+    """Bytes of one materialised N x N score (or probability) matrix per head,
+    over B * H heads: what standard attention writes to memory and the fused
+    kernel never does."""
+    return B * H * N * N * elem_bytes

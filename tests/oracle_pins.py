@@ -1,0 +1,335 @@
+"""Pins for the fp64 oracle: checks that tie it to something other than itself.
+
+Each check takes the forward / backward implementation as arguments so that the
+same checks can be run against deliberately broken copies (see
+``test_oracle_mutants.py``) to show that a plausible mistake fails at least one.
+
+Sources of the pinned facts:
+* definition of softmax and standard attention: [CANN-FA] (hwcomputing.csdn.net)
+  sections on the standard formula/code and on online softmax;
+* GQA = MHA on repeat_interleave'd K and V: [FA-GQA] (yunthe.com), GQA class;
+* causal mask = current and earlier positions: [CANN-FA] mask modes;
+* closed forms and invariants follow from those definitions by algebra.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+RTOL_EXACT = 1e-12
+
+
+def rng_arrays(seed, B, Hq, Hkv, N, d, with_do=True, scale_v=1.0):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, Hq, N, d))
+    k = r.standard_normal((B, Hkv, N, d))
+    v = r.standard_normal((B, Hkv, N, d)) * scale_v
+    do = r.standard_normal((B, Hq, N, d)) if with_do else None
+    return q, k, v, do
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_force_fwd(q, k, v, scale, causal):
+    """Scalar loops straight from the definitions, no max subtraction.
+
+    softmax(x)_j = e^{x_j} / sum_j' e^{x_j'} ([CANN-FA] softmax definition),
+    KV head of query head hq = hq // (Hq // Hkv) ([FA-GQA] repeat_interleave).
+    Inputs must be small enough that exp() does not overflow.
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, N, d))
+    L = np.zeros((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            for i in range(N):
+                weights = []
+                for j in range(N):
+                    if causal and j > i:
+                        weights.append(0.0)
+                        continue
+                    s = 0.0
+                    for c in range(d):
+                        s += float(q[b, h, i, c]) * float(k[b, kv, j, c])
+                    weights.append(math.exp(scale * s))
+                den = math.fsum(weights)
+                L[b, h, i] = math.log(den)
+                for c in range(d):
+                    O[b, h, i, c] = math.fsum(
+                        weights[j] * float(v[b, kv, j, c]) for j in range(N)) / den
+    return O, L
+
+
+def check_brute_force(fwd, seed, B, Hq, Hkv, N, d, causal, scale=0.7):
+    q, k, v, _ = rng_arrays(seed, B, Hq, Hkv, N, d, with_do=False)
+    O, L = fwd(q, k, v, scale, causal)
+    Ob, Lb = brute_force_fwd(q, k, v, scale, causal)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L, Lb, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------- hand-worked 2 x 2
+
+E = math.e
+P_HI = E / (E + 1.0)          # 0.7310585786300049
+P_LO = 1.0 / (E + 1.0)        # 0.2689414213699951
+DS = 2.0 * E / (E + 1.0) ** 2  # 0.3932238664829637
+
+
+def hand_2x2_inputs():
+    q = np.eye(2)[None, None]
+    k = np.eye(2)[None, None]
+    v = np.array([[1.0, 2.0], [3.0, 4.0]])[None, None]
+    return q, k, v
+
+
+def check_hand_2x2_fwd(fwd):
+    """N=2, d=2, scale=1, Q=K=I, V=[[1,2],[3,4]], worked by hand.
+
+    Scores are the identity, so row 0 weights keys (e, 1)/(e+1) and row 1
+    weights (1, e)/(e+1); LSE = ln(e+1). Causal row 0 sees only key 0:
+    O_0 = v_0, LSE_0 = s_00 = 1.
+    """
+    q, k, v = hand_2x2_inputs()
+    O, L = fwd(q, k, v, 1.0, False)
+    want_o = np.array([[P_HI * 1 + P_LO * 3, P_HI * 2 + P_LO * 4],
+                       [P_LO * 1 + P_HI * 3, P_LO * 2 + P_HI * 4]])
+    np.testing.assert_allclose(O[0, 0], want_o, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(want_o[0], [1.5378828427399902, 2.5378828427399904], atol=1e-15)
+    np.testing.assert_allclose(L[0, 0], [math.log(E + 1)] * 2, rtol=0, atol=1e-15)
+    Oc, Lc = fwd(q, k, v, 1.0, True)
+    np.testing.assert_allclose(Oc[0, 0, 0], [1.0, 2.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(Lc[0, 0, 0], 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(Oc[0, 0, 1], want_o[1], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(Lc[0, 0, 1], math.log(E + 1), rtol=0, atol=1e-15)
+
+
+def check_hand_2x2_bwd(bwd):
+    """Same inputs, no mask, dO = [[1,0],[0,0]], worked by hand.
+
+    dV_0 = (P_00, 0), dV_1 = (P_01, 0); dP_0 = (1, 3) so the row term is
+    P_00 + 3 P_01 and dS_00 = -dS_01 = -2e/(e+1)^2; dQ_0 = dS_0 K = (dS_00,
+    dS_01), dQ_1 = 0; dK_j = dS_0j q_0.
+    """
+    q, k, v = hand_2x2_inputs()
+    do = np.array([[1.0, 0.0], [0.0, 0.0]])[None, None]
+    dQ, dK, dV = bwd(q, k, v, do, 1.0, False)
+    np.testing.assert_allclose(dV[0, 0], [[P_HI, 0.0], [P_LO, 0.0]], atol=1e-15)
+    np.testing.assert_allclose(dQ[0, 0], [[-DS, DS], [0.0, 0.0]], atol=1e-15)
+    np.testing.assert_allclose(dK[0, 0], [[-DS, 0.0], [DS, 0.0]], atol=1e-15)
+
+
+# ------------------------------------------------------------- closed forms
+
+def check_zero_queries(fwd, causal):
+    """Q = 0: every allowed key gets the same weight, so O_i is the mean of
+    the allowed v_j and LSE_i = ln |A_i|."""
+    _, k, v, _ = rng_arrays(3, 1, 2, 2, 9, 4, with_do=False)
+    q = np.zeros((1, 2, 9, 4))
+    O, L = fwd(q, k, v, 0.5, causal)
+    for i in range(9):
+        n = i + 1 if causal else 9
+        np.testing.assert_allclose(O[0, :, i], v[0, :, :n].mean(axis=1), atol=1e-14)
+        np.testing.assert_allclose(L[0, :, i], math.log(n), atol=1e-14)
+
+
+def check_causal_first_row(fwd):
+    """Causal row 0 sees only key 0: O_0 = v_0 and LSE_0 = scale <q_0, k_0>."""
+    q, k, v, _ = rng_arrays(4, 2, 4, 2, 7, 5, with_do=False)
+    O, L = fwd(q, k, v, 0.3, True)
+    for b in range(2):
+        for h in range(4):
+            kv = h // 2
+            np.testing.assert_allclose(O[b, h, 0], v[b, kv, 0], atol=1e-14)
+            np.testing.assert_allclose(L[b, h, 0], 0.3 * q[b, h, 0] @ k[b, kv, 0], atol=1e-14)
+
+
+def check_single_key(fwd):
+    """N = 1: O = V and LSE = scale <q, k>."""
+    q, k, v, _ = rng_arrays(5, 1, 3, 3, 1, 6, with_do=False)
+    for causal in (False, True):
+        O, L = fwd(q, k, v, 0.9, causal)
+        np.testing.assert_allclose(O, v, atol=1e-15)
+        np.testing.assert_allclose(L[..., 0], 0.9 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                                   atol=1e-14)
+
+
+def check_identical_keys(fwd):
+    """All keys equal: weights are uniform whatever the queries are."""
+    q, k, v, _ = rng_arrays(6, 1, 2, 1, 8, 3, with_do=False)
+    k[:] = k[:, :, :1]
+    O, _ = fwd(q, k, v, 1.0, False)
+    np.testing.assert_allclose(O[0, 0], np.broadcast_to(v[0, 0].mean(0), (8, 3)), atol=1e-14)
+
+
+def check_gqa_is_repeated_mha(fwd, bwd, G, Hkv=2, causal=True):
+    """[FA-GQA]: GQA equals MHA on K, V repeat_interleave'd n_rep = G times
+    along the head axis; the K/V gradients of GQA are the sums of the MHA
+    gradients over each group of G heads."""
+    Hq = G * Hkv
+    q, k, v, do = rng_arrays(7 + G, 2, Hq, Hkv, 11, 4)
+    O, L = fwd(q, k, v, 0.6, causal)
+    kr = np.repeat(k, G, axis=1)
+    vr = np.repeat(v, G, axis=1)
+    Om, Lm = fwd(q, kr, vr, 0.6, causal)
+    np.testing.assert_allclose(O, Om, atol=1e-14)
+    np.testing.assert_allclose(L, Lm, atol=1e-14)
+    dQ, dK, dV = bwd(q, k, v, do, 0.6, causal)
+    dQm, dKm, dVm = bwd(q, kr, vr, do, 0.6, causal)
+    np.testing.assert_allclose(dQ, dQm, atol=1e-13)
+    np.testing.assert_allclose(dK, dKm.reshape(2, Hkv, G, 11, 4).sum(2), atol=1e-13)
+    np.testing.assert_allclose(dV, dVm.reshape(2, Hkv, G, 11, 4).sum(2), atol=1e-13)
+
+
+def check_library_softmax(fwd, causal):
+    """Special case of a library routine: torch float64 on the CPU of the
+    standard attention code ([CANN-FA]), softmax(Q K^T * scale + mask) V."""
+    import torch
+    q, k, v, _ = rng_arrays(8, 2, 4, 4, 33, 16, with_do=False)
+    O, L = fwd(q, k, v, 0.25, causal)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    s = torch.matmul(tq, tk.transpose(-2, -1).contiguous()) * 0.25
+    if causal:
+        s = s.masked_fill(torch.ones(33, 33, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), tv)
+    np.testing.assert_allclose(O, o.numpy(), atol=1e-13)
+    np.testing.assert_allclose(L, torch.logsumexp(s, dim=-1).numpy(), atol=1e-13)
+
+
+# --------------------------------------------------------------- invariants
+
+def check_key_shift(fwd, causal):
+    """Adding c to every k_j leaves O unchanged and shifts LSE_i by
+    scale <q_i, c> (every score of row i moves by the same amount)."""
+    q, k, v, _ = rng_arrays(9, 1, 2, 2, 13, 5, with_do=False)
+    c = np.random.default_rng(10).standard_normal(5)
+    O, L = fwd(q, k, v, 0.4, causal)
+    O2, L2 = fwd(q, k + c, v, 0.4, causal)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2 - L, 0.4 * q @ c, atol=1e-13)
+
+
+def check_value_shift(fwd, causal):
+    """Adding c to every v_j adds c to every O_i (weights sum to 1)."""
+    q, k, v, _ = rng_arrays(11, 1, 2, 2, 13, 5, with_do=False)
+    c = np.arange(5.0) - 2
+    O, _ = fwd(q, k, v, 0.4, causal)
+    O2, _ = fwd(q, k, v + c, 0.4, causal)
+    np.testing.assert_allclose(O2, O + c, atol=1e-13)
+
+
+def check_convex_hull(fwd, causal):
+    """Each O_ic lies between min and max of v_jc over the allowed keys."""
+    q, k, v, _ = rng_arrays(12, 1, 2, 1, 17, 4, with_do=False)
+    O, _ = fwd(q, k, v, 2.0, causal)
+    for i in range(17):
+        n = i + 1 if causal else 17
+        lo = v[0, 0, :n].min(0)
+        hi = v[0, 0, :n].max(0)
+        assert np.all(O[0, :, i] >= lo - 1e-14) and np.all(O[0, :, i] <= hi + 1e-14)
+
+
+def check_key_permutation(fwd):
+    """No mask: permuting keys together with values changes nothing."""
+    q, k, v, _ = rng_arrays(13, 1, 2, 2, 15, 4, with_do=False)
+    perm = np.random.default_rng(14).permutation(15)
+    O, L = fwd(q, k, v, 0.5, False)
+    O2, L2 = fwd(q, k[:, :, perm], v[:, :, perm], 0.5, False)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L, atol=1e-13)
+
+
+def check_rows_sum_to_one(fwd_head, causal):
+    """Every row of the materialised P sums to 1 and is 0 off the mask."""
+    q, k, v, _ = rng_arrays(15, 1, 1, 1, 20, 6, with_do=False)
+    _, _, S, P = fwd_head(q[0, 0], k[0, 0], v[0, 0], 0.8, causal, 0, True)
+    np.testing.assert_allclose(P.sum(1), 1.0, atol=1e-14)
+    if causal:
+        assert np.all(P[np.triu_indices(20, 1)] == 0.0)
+
+
+def check_bwd_identities(bwd, causal):
+    """Gradient identities of the definition:
+    * sum_j dK_j = 0 per (b, hkv): shifting every key by c leaves O unchanged;
+    * sum_j dV_j = sum over the group's query heads and rows of dO_i
+      (rows of P sum to 1);
+    * the gradients are linear in dO."""
+    q, k, v, do = rng_arrays(16, 2, 4, 2, 12, 5)
+    dQ, dK, dV = bwd(q, k, v, do, 0.7, causal)
+    np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dV.sum(axis=2), do.reshape(2, 2, 2, 12, 5).sum(axis=(2, 3)),
+                               atol=1e-12)
+    do2 = np.random.default_rng(17).standard_normal(do.shape)
+    g1 = bwd(q, k, v, do2, 0.7, causal)
+    g12 = bwd(q, k, v, 2.0 * do - 3.0 * do2, 0.7, causal)
+    for a, b_, c in zip((dQ, dK, dV), g1, g12):
+        np.testing.assert_allclose(c, 2.0 * a - 3.0 * b_, atol=1e-12)
+
+
+def check_finite_differences(fwd, bwd, causal, seed=18, B=1, Hq=2, Hkv=1, N=5, d=3):
+    """Central differences of L = sum(O * dO) for every element of Q, K, V."""
+    scale = 0.9
+    q, k, v, do = rng_arrays(seed, B, Hq, Hkv, N, d)
+    dQ, dK, dV = bwd(q, k, v, do, scale, causal)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        O, _ = fwd(qq, kk, vv, scale, causal)
+        return float(np.sum(O * do))
+
+    for arr, grad, which in ((q, dQ, 0), (k, dK, 1), (v, dV, 2)):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.linalg.norm(num - grad) / np.linalg.norm(grad)
+        assert err < 1e-7, f"finite-difference mismatch on input {which}: rel err {err:.3e}"
+
+
+def check_blockwise_equals_plain(blockwise, fwd_head, causal, N=70, d=8):
+    """The blockwise online-softmax loop equals the materialising definition
+    for any block sizes ([YOLO11-FA2] section 2.2, [CANN-FA] online softmax:
+    the result is exact up to summation order)."""
+    q, k, v, _ = rng_arrays(19, 1, 1, 1, N, d, with_do=False)
+    q, k, v = q[0, 0] * 2.0, k[0, 0], v[0, 0]
+    O, L = fwd_head(q, k, v, 0.5, causal)
+    for br, bc in ((1, 1), (7, 7), (64, 64), (N, N), (16, 5)):
+        Ob, Lb = blockwise(q, k, v, 0.5, causal, br, bc)
+        np.testing.assert_allclose(Ob, O, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(Lb, L, rtol=0, atol=1e-12)
+
+
+def all_forward_checks(fwd):
+    """Every forward pin that needs only the [B,H,N,d] forward entry point."""
+    check_brute_force(fwd, 1, 1, 2, 1, 5, 3, False)
+    check_brute_force(fwd, 2, 2, 4, 2, 6, 4, True)
+    check_hand_2x2_fwd(fwd)
+    for causal in (False, True):
+        check_zero_queries(fwd, causal)
+        check_key_shift(fwd, causal)
+        check_value_shift(fwd, causal)
+        check_convex_hull(fwd, causal)
+        check_library_softmax(fwd, causal)
+    check_causal_first_row(fwd)
+    check_single_key(fwd)
+    check_identical_keys(fwd)
+    check_key_permutation(fwd)
+
+
+def all_backward_checks(fwd, bwd):
+    check_hand_2x2_bwd(bwd)
+    for causal in (False, True):
+        check_bwd_identities(bwd, causal)
+        check_finite_differences(fwd, bwd, causal)
+    for G in (1, 2, 3):
+        check_gqa_is_repeated_mha(fwd, bwd, G)

@@ -1,0 +1,72 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Each mutant is a one-spot text edit of ``oracle/attention.py`` (a dropped term,
+a wrong sign or index, a transposed operand, a wrong mask), loaded as a
+separate module on the CPU. The pin suite of ``tests/oracle_pins.py`` is run
+against it and is expected to reject it.
+"""
+
+import importlib.util
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "attention.py")
+
+MUTANTS = {
+    "scale_dropped": ("S = (q @ k.T) * scale", "S = (q @ k.T)"),
+    "gqa_modulo_mapping": ("return hq // (Hq // Hkv)", "return hq % Hkv"),
+    "causal_excludes_diagonal": ("return j <= i", "return j < i"),
+    "causal_transposed": ("return j <= i", "return j >= i"),
+    "lse_without_max": ("safe_m + np.log(den)", "np.log(den)"),
+    "softmax_not_normalised": ("E / den[:, None]", "E"),
+    "pv_transposed": ("O = P @ v", "O = P.T @ v[: P.shape[0]]"),
+    "row_term_dropped": ("dS = P * (dP - row_term[:, None])", "dS = P * dP"),
+    "row_term_sign": ("dS = P * (dP - row_term[:, None])", "dS = P * (dP + row_term[:, None])"),
+    "dk_scale_dropped": ("dK += scale * (dS.T @ qc)", "dK += (dS.T @ qc)"),
+    "dq_sign": ("dQ[g, r0:r1] = scale * (dS @ k)", "dQ[g, r0:r1] = -scale * (dS @ k)"),
+    "dv_uses_scores": ("dV += P.T @ doc", "dV += np.where(np.isfinite(_s), _s, 0).T @ doc"),
+    "dk_not_group_summed": ("dK += scale * (dS.T @ qc)", "dK = scale * (dS.T @ qc) if g == G - 1 else dK"),
+    "dp_transposed_v": ("dP = doc @ v.T", "dP = doc @ v[::-1].T"),
+    "online_l_not_rescaled": ("l[i0:i1] *= corr", "pass"),
+    "online_o_not_rescaled": ("O[i0:i1] *= corr[:, None]", "pass"),
+    "online_uses_old_max": ("np.exp(scores - m_new[:, None])",
+                            "np.exp(scores - np.where(np.isfinite(m_old), m_old, m_new)[:, None])"),
+    "online_drops_lse_max": ("m + np.log(l)", "np.log(l)"),
+}
+
+
+def load_mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    src = src.replace(old, new)
+    if "_s" in new:
+        src = src.replace("_, _, _, P = ref_fwd_head(", "_, _, _s, P = ref_fwd_head(")
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def run_all_pins(mod):
+    fwd = lambda q, k, v, s, c: mod.ref_fwd(q, k, v, s, c, chunk=4)
+    bwd = lambda q, k, v, do, s, c: mod.ref_bwd(q, k, v, do, s, c, chunk=4)
+    pins.all_forward_checks(fwd)
+    pins.all_backward_checks(fwd, bwd)
+    for causal in (False, True):
+        pins.check_rows_sum_to_one(mod.ref_fwd_head, causal)
+        pins.check_blockwise_equals_plain(mod.blockwise_online_fwd, mod.ref_fwd_head, causal)
+
+
+def test_unmutated_copy_passes():
+    run_all_pins(load_mutant("DEFAULT_CHUNK = 1024", "DEFAULT_CHUNK = 1024"))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = load_mutant(*MUTANTS[name])
+    with pytest.raises(Exception):
+        run_all_pins(mod)
