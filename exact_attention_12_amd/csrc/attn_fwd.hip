@@ -1,0 +1,297 @@
+// attn_fwd.hip - fused tiled attention forward for gfx950.
+//
+// What it computes (per batch b, query head h, with KV head h / G):
+//   O_i   = sum_j softmax_j(scale * <q_i, k_j>) v_j   over allowed keys j
+//   LSE_i = ln sum_j exp(scale * <q_i, k_j>)
+// following the blockwise online softmax of the CANN ops-transformer
+// FlashAttention page (section on online softmax): for each block of keys the
+// running row maximum m is raised, the partial output and running sum l are
+// rescaled by exp(m_old - m_new), and the block's exp(s - m_new) is
+// accumulated; O is divided by l at the end. The lpnh.cn FlashAttention-2
+// article (sections 2.1, 2.4) gives the tiling and the parallelisation over
+// (batch, head, query block); the yunthe.com GQA page gives the KV-head
+// sharing (query head h reads KV head h / (Hq/Hkv)).
+//
+// Mapping onto the CDNA4 compute unit (4 waves per workgroup, 32 query rows
+// per wave, BLOCK_KV keys per step):
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand,
+//    the wave's 32 query rows (kept in registers for the whole loop) are the
+//    B operand. The result puts one query per lane (lane % 32) and 16 keys
+//    per lane in registers, so the row maximum is a register reduction plus a
+//    single permlane32 swap, and m, l live in one lane pair.
+//  * O^T += V^T P^T: the probabilities, converted to bf16, are already laid
+//    out as the B operand (a lane holds 8 keys of its query); V^T is read as
+//    the A operand straight from the row-major V tile with the transposing
+//    LDS read. O^T keeps one query per lane, so the rescale by
+//    exp(m_old - m_new) needs no data movement.
+//  * The row sum l is accumulated in fp32 from the unrounded probabilities
+//    (only the matrix-product operand is rounded to bf16), so LSE carries no
+//    bf16 rounding bias even for rows with few keys.
+//  * Scores are kept in the log2 domain: exp(scale*s - m) = exp2(c*s - m')
+//    with c = scale * log2(e).
+//  * K/V tiles are double buffered in LDS: the next tile's global loads are
+//    issued before the current tile's math and written to the other buffer
+//    after it, one barrier per step.
+//  * Causal: key blocks after the workgroup's last query are never loaded; a
+//    wave skips the math of blocks after its own last query; the diagonal
+//    blocks are masked per element. Heavy (late) query blocks are launched
+//    first.
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
+void fwd_kernel(FwdParams p) {
+    constexpr int NW = FwdTile<D>::WAVES;
+    constexpr int T = NW * 64;
+    constexpr int BQ = NW * 32;
+    constexpr int BC = FwdTile<D>::BLOCK_KV;
+    constexpr int KS = D / 16;            // contraction steps of S^T = K Q^T
+    constexpr int NDT = (D + 31) / 32;    // 32-row tiles of O^T
+    constexpr int NKT = BC / 32;          // 32-key tiles of S^T
+    constexpr int PVS = BC / 16;          // contraction steps of O^T += V^T P^T
+    constexpr int KP = k_pitch(D);
+    constexpr int VP = v_pitch(D);
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
+    constexpr int CHUNKS = BC * CPR;
+    constexpr int NCH = (CHUNKS + T - 1) / T;
+    constexpr int BUF = BC * (KP + VP);
+
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int N = p.N;
+
+    // Workgroup -> (query block, batch*head). Under the causal mask the
+    // latest (heaviest) query blocks come first.
+    const int bid = blockIdx.x;
+    const int bh = bid % p.BH;
+    const int qb = CAUSAL ? (p.nqb - 1 - bid / p.BH) : (bid / p.BH);
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hkv = hq / p.G;
+
+    const bf16* Qh = static_cast<const bf16*>(p.q) + (size_t)bh * N * D;
+    const bf16* Kh = static_cast<const bf16*>(p.k) + (size_t)(b * p.Hkv + hkv) * N * D;
+    const bf16* Vh = static_cast<const bf16*>(p.v) + (size_t)(b * p.Hkv + hkv) * N * D;
+
+    const int q0 = qb * BQ;
+    const int qw0 = q0 + wave * 32;
+    const int qrow = qw0 + l32;
+
+    // Columns d .. padded width of the V tiles are read by the last O^T tile
+    // and must be zero; the loaders never write them.
+    if constexpr (NDT * 32 > D) {
+        constexpr int PADC = NDT * 32 - D;
+        for (int i = tid; i < 2 * BC * PADC; i += T) {
+            const int row = i / PADC;
+            const int col = D + i % PADC;
+            const int bufi = row / BC;
+            smem[bufi * BUF + BC * KP + (row % BC) * VP + col] = (bf16)0.0f;
+        }
+    }
+
+    // Q operand (B of S^T = K Q^T): lane holds query qrow, dims 16*ks + 8*h .. +7.
+    bf16x8 qf[KS];
+    if (qrow < N) {
+        const bf16* qp = Qh + (size_t)qrow * D + h * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8{};
+    }
+
+    const int nkb = (N + BC - 1) / BC;
+    const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
+
+    uint4 kreg[NCH], vreg[NCH];
+    auto load_tile = [&](int kv0) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * T;
+            if (CHUNKS % T == 0 || c < CHUNKS) {
+                const int row = c / CPR;
+                const int col = c - row * CPR;
+                const int key = kv0 + row;
+                if (key < N) {
+                    kreg[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + col * 8);
+                    vreg[i] = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + col * 8);
+                } else {
+                    kreg[i] = zero4();
+                    vreg[i] = zero4();
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int bufi) {
+        bf16* Ks = smem + bufi * BUF;
+        bf16* Vs = Ks + BC * KP;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * T;
+            if (CHUNKS % T == 0 || c < CHUNKS) {
+                const int row = c / CPR;
+                const int col = c - row * CPR;
+                *reinterpret_cast<uint4*>(Ks + row * KP + col * 8) = kreg[i];
+                *reinterpret_cast<uint4*>(Vs + row * VP + col * 8) = vreg[i];
+            }
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+    float m = -__builtin_huge_valf();  // running max of c*s (log2 domain)
+    float l = 0.0f;                    // this lane's share of the running sum
+    const float c = p.c;
+
+    // Per-lane constant parts of the LDS addresses.
+    const int g16 = lane >> 4;          // 16-lane group
+    const int j16 = lane & 15;
+    const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
+    const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
+
+    for (int kb = 0; kb < kb_end; ++kb) {
+        const int bufi = kb & 1;
+        const bool has_next = kb + 1 < kb_end;
+        if (has_next) load_tile((kb + 1) * BC);
+
+        const int kv0 = kb * BC;
+        const bf16* Ks = smem + bufi * BUF;
+        const bf16* Vs = Ks + BC * KP;
+        const bool active = !CAUSAL || kv0 <= qw0 + 31;
+        if (active) {
+            f32x16 s[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                s[kt] = f32x16{};
+                const bf16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32(lds_read8(kp + ks * 16), qf[ks], s[kt]);
+            }
+            const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
+            if (need_mask) {
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + kt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                        const bool masked = (key >= N) || (CAUSAL && key > qrow);
+                        s[kt][r] = masked ? -__builtin_huge_valf() : s[kt][r];
+                    }
+            }
+            float mx = s[0][0];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = max_across_halves(mx);
+            const float m_new = fmaxf(m, mx * c);
+            const float alpha = fast_exp2(m - m_new);
+            m = m_new;
+
+            bf16x8 pb[PVS];
+            float lsum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < PVS; ++u) {
+                const int kt = u >> 1;
+                const int r0 = (u & 1) * 8;
+                bf16x2 pr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a0 = fast_exp2(fmaf(s[kt][r0 + 2 * e], c, -m_new));
+                    const float a1 = fast_exp2(fmaf(s[kt][r0 + 2 * e + 1], c, -m_new));
+                    pr[e] = to_bf16x2(a0, a1);
+                    lsum += a0 + a1;
+                }
+                pb[u] = cat8(pr[0], pr[1], pr[2], pr[3]);
+            }
+            l = fmaf(l, alpha, lsum);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+
+#pragma unroll
+            for (int u = 0; u < PVS; ++u) {
+                const bf16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const bf16x8 a = join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32));
+                    oacc[dt] = mfma32(a, pb[u], oacc[dt]);
+                }
+            }
+        }
+        if (has_next) store_tile(bufi ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: combine the two half-row sums, normalise, store O and LSE.
+    const float lt = sum_across_halves(l);
+    const float inv = 1.0f / lt;
+    if (qrow < N) {
+        bf16* orow = static_cast<bf16*>(p.o) + ((size_t)bh * N + qrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = dt * 32 + g4 * 8 + h * 4;
+                if (d < D)
+                    store_bf16x4(orow + d, oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv,
+                                 oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv);
+            }
+        if (h == 0) p.lse[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+    }
+}
+
+template <int D>
+static hipError_t launch_fwd_d(const FwdParams& p, bool causal, long long wgs, hipStream_t stream) {
+    constexpr int T = FwdTile<D>::WAVES * 64;
+    if (causal)
+        hipLaunchKernelGGL((fwd_kernel<D, true>), dim3((unsigned)wgs), dim3(T), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<D, false>), dim3((unsigned)wgs), dim3(T), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
+    constexpr int BQ = FwdTile<D>::WAVES * 32;
+    constexpr int BC = FwdTile<D>::BLOCK_KV;
+    plan->block_q = BQ;
+    plan->block_kv = BC;
+    plan->threads = FwdTile<D>::WAVES * 64;
+    plan->workgroups = (long long)((N + BQ - 1) / BQ) * B * Hq;
+    plan->lds_bytes = 2 * BC * (k_pitch(D) + v_pitch(D)) * 2;
+}
+
+bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan) {
+    switch (d) {
+        case 64: plan_d<64>(B, Hq, N, plan); return true;
+        case 80: plan_d<80>(B, Hq, N, plan); return true;
+        case 128: plan_d<128>(B, Hq, N, plan); return true;
+        case 256: plan_d<256>(B, Hq, N, plan); return true;
+        default: return false;
+    }
+}
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, long long wgs, hipStream_t stream) {
+    switch (d) {
+        case 64: return launch_fwd_d<64>(p, causal, wgs, stream);
+        case 80: return launch_fwd_d<80>(p, causal, wgs, stream);
+        case 128: return launch_fwd_d<128>(p, causal, wgs, stream);
+        case 256: return launch_fwd_d<256>(p, causal, wgs, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn
