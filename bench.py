@@ -42,6 +42,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="rough CPU budget for the oracle leg (it times whole heads)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=256,
+                    help="size of the plain copy kernel run once after timing (its HBM counters "
+                         "calibrate the byte counters of the attention kernels); 0 disables")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
+                         "into a traffic summary file and exit")
     return ap.parse_args()
 
 
@@ -60,6 +66,114 @@ def kernel_flop_credit(w):
         "bwd_dkdv": 6.0 * w.d * pairs,
         "bwd_dq": 4.0 * w.d * pairs,
     }
+
+
+KERNEL_SOURCES = {
+    "fwd_kernel": ["attn_fwd.hip", "attn_device.h", "attn_kernels.h"],
+    "bwd_dkdv_kernel": ["attn_bwd.hip", "attn_device.h", "attn_kernels.h"],
+    "bwd_dq_kernel": ["attn_bwd.hip", "attn_device.h", "attn_kernels.h"],
+    "bwd_pre_kernel": ["attn_bwd.hip", "attn_device.h", "attn_kernels.h"],
+}
+CALIBRATION_KERNEL = "neg_kernel"
+
+
+def source_hash(kernel):
+    """sha256 over the sources a kernel is built from (traffic numbers are
+    only reported for the source they were measured on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_attention_12_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was measured on other source."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash(kernel):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def summarize_pmc(fetch_dir, write_dir, out_dir, workload, mib):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two
+    rocprofv3 --pmc runs, scaled by what the same counters read for the
+    calibration copy (which moves a known number of bytes each way)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        acc = {}
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                acc.setdefault(name, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def find(d, key):
+        hits = [k for k in d if key in k]
+        if not hits:
+            raise SystemExit(f"kernel {key} not found in counters: {sorted(d)[:6]}")
+        return hits[0]
+
+    cal_f = fetch[find(fetch, CALIBRATION_KERNEL)]
+    cal_w = write[find(write, CALIBRATION_KERNEL)]
+    # The calibration kernel reads and writes `mib` MiB each (float32 negate).
+    known_kib = mib * 1024.0
+    sf, sw = known_kib / cal_f, known_kib / cal_w
+    os.makedirs(out_dir, exist_ok=True)
+    written = []
+    for kernel in ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel"):
+        try:
+            kf, kw = find(fetch, f"{kernel}<"), find(write, f"{kernel}<")
+        except SystemExit:
+            continue
+        fb = fetch[kf] * sf * 1024.0
+        wb = write[kw] * sw * 1024.0
+        path = traffic_file(kernel, workload)
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of {kernel} on {workload}, from rocprofv3 counters.\n")
+            f.write(f"# Commands (run from the repository root on the MI355X box):\n")
+            f.write(f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d <fetch_dir> -- python bench.py "
+                    f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+            f.write(f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d <write_dir> -- python bench.py "
+                    f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+            f.write(f"#   python bench.py --workload {workload} --summarize-pmc <fetch_dir> <write_dir> profiles\n")
+            f.write(f"kernel_symbol = {kf}\n")
+            f.write(f"fetch_size_kib_per_dispatch = {fetch[kf]:.1f}\n")
+            f.write(f"write_size_kib_per_dispatch = {write[kw]:.1f}\n")
+            f.write(f"calibration_kernel = {CALIBRATION_KERNEL} ({mib} MiB read + {mib} MiB written)\n")
+            f.write(f"calibration_fetch_kib = {cal_f:.1f}\n")
+            f.write(f"calibration_write_kib = {cal_w:.1f}\n")
+            f.write(f"fetch_scale = {sf:.4f}\n")
+            f.write(f"write_scale = {sw:.4f}\n")
+            f.write(f"hbm_read_bytes_per_launch = {fb:.0f}\n")
+            f.write(f"hbm_write_bytes_per_launch = {wb:.0f}\n")
+            f.write(f"hbm_bytes_per_launch = {fb + wb:.0f}\n")
+            f.write(f"source_sha256 = {source_hash(kernel)}\n")
+        written.append(path)
+    print("\n".join(written))
 
 
 def time_loop(fn, steps, stream):
@@ -144,6 +258,9 @@ def parity_sample(w, inputs, o, lse):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.workload, args.calibration_copy_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
@@ -193,33 +310,60 @@ def main():
     print(f"[bench] {args.steps} steps of {w.name}: {ms_step:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
-    # Per-pass timings (same stream, HIP events) for the roofline and the breakdown.
+    # Per-kernel timings: each kernel launched alone through its own entry
+    # point, bracketed by HIP events on the stream it runs on.
     credit = kernel_flop_credit(w)
-    ms_fwd = time_loop(run_fwd, args.steps, stream)
-    passes = {"fwd": {"ms": ms_fwd, "tflops": credit["fwd"] / ms_fwd / 1e9}}
+    kernels = {"fwd_kernel": {"ms": time_loop(run_fwd, args.steps, stream), "flops": credit["fwd"],
+                              "bytes": w.fwd_bytes()}}
     if w.backward:
+        def bwd_pass(name):
+            return lambda: ea.bwd_passes(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, ws,
+                                         scale=w.scale, causal=w.causal, passes=(name,))
+        rows = w.B * w.Hq * w.N
+        kernels["bwd_pre_kernel"] = {"ms": time_loop(bwd_pass("pre"), args.steps, stream), "flops": 0.0,
+                                     "bytes": 2 * rows * w.d * 2 + 4 * rows}
+        kernels["bwd_dkdv_kernel"] = {"ms": time_loop(bwd_pass("dkdv"), args.steps, stream),
+                                      "flops": credit["bwd_dkdv"]}
+        kernels["bwd_dq_kernel"] = {"ms": time_loop(bwd_pass("dq"), args.steps, stream),
+                                    "flops": credit["bwd_dq"]}
         ms_bwd = time_loop(run_bwd, args.steps, stream)
-        passes["bwd"] = {"ms": ms_bwd, "tflops": w.bwd_flops() / ms_bwd / 1e9}
-    for p in passes.values():
-        p["pct_of_bf16_peak"] = 100.0 * p["tflops"] / PEAK_BF16_TFLOPS
-        p["ms"] = round(p["ms"], 4)
-        p["tflops"] = round(p["tflops"], 2)
-        p["pct_of_bf16_peak"] = round(p["pct_of_bf16_peak"], 2)
-    print(f"[bench] passes: {passes}", file=sys.stderr, flush=True)
+    for k in kernels.values():
+        k["tflops"] = round(k["flops"] / k["ms"] / 1e9, 2)
+        k["pct_of_bf16_peak"] = round(100.0 * k["tflops"] / PEAK_BF16_TFLOPS, 2)
+        k["ms"] = round(k["ms"], 4)
+    print(f"[bench] kernels: {kernels}", file=sys.stderr, flush=True)
+    passes = {"fwd": {"ms": kernels["fwd_kernel"]["ms"], "tflops": kernels["fwd_kernel"]["tflops"],
+                      "pct_of_bf16_peak": kernels["fwd_kernel"]["pct_of_bf16_peak"]}}
+    if w.backward:
+        tf = w.bwd_flops() / ms_bwd / 1e9
+        passes["bwd"] = {"ms": round(ms_bwd, 4), "tflops": round(tf, 2),
+                         "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
 
     step_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     value = step_flops / (ms_step * 1e-3) / 1e12
 
-    # Roofline of the forward kernel (one kernel per attn_fwd call, timed with
-    # HIP events on the stream it runs on).
-    if w.fwd_flops() / w.fwd_bytes() >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = {"kernel": "fwd_kernel", "bound": "mfma", "achieved": round(credit["fwd"] / ms_fwd / 1e9, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": "fwd_kernel", "bound": "hbm", "achieved": round(w.fwd_bytes() / ms_fwd / 1e6, 1),
+    # Roofline of the kernel that takes the most time per step.
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm_bound = dom == "bwd_pre_kernel" or (dom == "fwd_kernel" and w.fwd_flops() / w.fwd_bytes() < ridge)
+    if hbm_bound:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(kd["bytes"] / kd["ms"] / 1e6, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": kd["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["avg_launch_ms"] = kd["ms"]
+    roof["traffic"] = read_traffic(dom, w.name)
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     run_fwd()
     torch.cuda.synchronize()
@@ -249,6 +393,7 @@ def main():
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "passes": passes,
+        "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_sample": par,

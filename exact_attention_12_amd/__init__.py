@@ -72,6 +72,12 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+    L.attn_bwd_preprocess.restype = i
+    L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_dkdv.restype = i
+    L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_dq.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_status_string.argtypes = [i]
@@ -194,6 +200,38 @@ def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, workspace=None, dq=Non
                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device)))
+    return dq, dk, dv
+
+
+def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal=False,
+               passes=("pre", "dkdv", "dq")):
+    """Run selected backward passes through their own entry points (same
+    arguments and checks as bwd(); outputs must be preallocated)."""
+    import torch
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    if scale is None:
+        scale = default_scale(d)
+    for name, t in (("o", o), ("do", do), ("dq", dq)):
+        _require(t, name, torch.bfloat16, 4)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _require(t, name, torch.bfloat16, 4)
+    _require(lse, "lse", torch.float32, 3)
+    L = lib()
+    ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = _stream_ptr(q.device)
+    for p in passes:
+        if p == "pre":
+            _check(L.attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, st))
+        elif p == "dkdv":
+            _check(L.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                   dk.data_ptr(), dv.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, float(scale),
+                                   int(bool(causal)), st))
+        elif p == "dq":
+            _check(L.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                 dq.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, float(scale),
+                                 int(bool(causal)), st))
+        else:
+            raise ValueError(f"unknown backward pass {p!r}")
     return dq, dk, dv
 
 

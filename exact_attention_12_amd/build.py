@@ -23,8 +23,12 @@ ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
 
-# Packed fp32 VALU forms are turned off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are turned off for all device code. MFMA results
+# and accumulators are kept in the VGPR form: otherwise, above 256 live
+# registers, the backend places the score tiles in AGPRs and shuttles the
+# gradient accumulators between AGPRs and VGPRs on every loop step.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 

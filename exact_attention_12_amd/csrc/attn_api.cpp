@@ -91,22 +91,34 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
     return (bytes + 255) & ~(size_t)255;
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                     const float* lse, const void* dout,
-                     void* dq, void* dk, void* dv,
-                     void* workspace, size_t workspace_bytes,
-                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+namespace {
+
+// Shared validation and dispatch of attn_bwd and its three pass entry points.
+// Only the pointers the selected passes read or write are checked; the
+// others are NULL and never dereferenced.
+attn_status bwd_common(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       const void* workspace, size_t workspace_bytes,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                       void* stream, int passes) {
+    const bool pre = passes & attn::kBwdPre, kv = passes & attn::kBwdDkDv, qq = passes & attn::kBwdDq;
+    const bool main = kv || qq;
+    const void* used[] = {pre ? o : dout, dout, main ? q : dout, main ? k : dout,
+                          main ? v : dout, main ? static_cast<const void*>(lse) : dout,
+                          qq ? dq : dout, kv ? dk : dout, kv ? dv : dout};
+    for (const void* ptr : used)
+        if (!ptr) return ATTN_ERR_NULL;
     attn_status st = check_shape(B, Hq, Hkv, N, d);
     if (st != ATTN_OK) return st;
-    st = check_scale(scale);
-    if (st != ATTN_OK) return st;
+    if (main) {
+        st = check_scale(scale);
+        if (st != ATTN_OK) return st;
+    }
     if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
         return ATTN_ERR_WORKSPACE;
-    const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
-    for (const void* ptr : ptrs)
+    for (const void* ptr : used)
         if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
 
     attn::BwdParams p;
     p.q = q;
@@ -118,7 +130,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
-    p.delta = static_cast<float*>(workspace);
+    p.delta = static_cast<float*>(const_cast<void*>(workspace));
     p.N = N;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -127,7 +139,44 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     p.scale = scale;
     p.c = scale * kLog2eHost;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_bwd(p, d, causal != 0, static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_bwd(p, d, causal != 0, passes, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     void* stream) {
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
+                      d, scale, causal, stream, attn::kBwdAll);
+}
+
+attn_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                                size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                                void* stream) {
+    return bwd_common(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
+                      workspace, workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, stream, attn::kBwdPre);
+}
+
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                          const void* dout, void* dk, void* dv,
+                          const void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                          void* stream) {
+    return bwd_common(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B, Hq,
+                      Hkv, N, d, scale, causal, stream, attn::kBwdDkDv);
+}
+
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dq,
+                        const void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                        void* stream) {
+    return bwd_common(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes, B,
+                      Hq, Hkv, N, d, scale, causal, stream, attn::kBwdDq);
 }
 
 const char* attn_status_string(attn_status status) {

@@ -15,8 +15,8 @@
 // Three kernels on one stream, no atomics (bitwise deterministic):
 //  1. bwd_pre: D_i for every query row (memory bound).
 //  2. bwd_dkdv: one workgroup per (batch, KV head, 128-key block); each wave
-//     owns 32 keys with K and V held as MFMA operands in registers and dK^T,
-//     dV^T accumulated in registers, looping over the G query heads of the
+//     owns 32 keys with K and V held as MFMA operands in VGPRs and dK^T,
+//     dV^T accumulated in AGPRs, looping over the G query heads of the
 //     group and their 64-row query blocks (under the causal mask only the
 //     blocks at or after the keys). Per step: S = Q K^T and dP = dO V^T with
 //     Q, dO from LDS (one key per lane, 16 queries per lane in registers);
@@ -26,6 +26,8 @@
 //     forward's orientation: S^T = K Q^T and dP^T = V dO^T put one query per
 //     lane, so LSE_i and D_i are per-lane scalars; dQ^T += K^T dS^T with K^T
 //     read transposed from the K tile.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -219,8 +221,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 
         const int g = it / nq_iter;
         const int q0 = (qb_start + (it - g * nq_iter)) * BQ;
-        const bool active = !CAUSAL || q0 + BQ - 1 >= kw0;
-        if (active) {
+        // Every step runs for every wave (no data-dependent branch in the
+        // loop body): a wave whose keys all lie after this query block just
+        // contributes zeros through the mask.
+        {
             const bf16* Qs = qtile(bufi);
             const bf16* dOs = dotile(bufi);
             const float* Ls = lsetile(bufi);
@@ -238,41 +242,68 @@ void bwd_dkdv_kernel(BwdParams p) {
                     dp[qt] = mfma32(lds_read8(gp + ks * 16), vf[ks], dp[qt]);
                 }
             }
-            const bool need_mask = CAUSAL && q0 < kw0 + 31;
+            // P = exp2(c*S - LSE2) and dS = P (dP - D), packed to bf16 in the
+            // B-operand order of the dV/dK products. Under the causal mask the
+            // query of register r (local offset qoff(r) + 4h) is masked for
+            // this lane's key when key - q0 - 4h > qoff(r): one compare with a
+            // constant per element.
             bf16x8 pb[PVS], dsb[PVS];
+            {
+                const int kq = key - q0 - 4 * h;
 #pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-                const int qt = u >> 1;
-                const int r0 = (u & 1) * 8;
-                bf16x2 pp[4], dd[4];
+                for (int u = 0; u < PVS; ++u) {
+                    const int qt = u >> 1;
+                    const int r0 = (u & 1) * 8;
+                    bf16x2 pp[4], dd[4];
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float pv[2], dv[2];
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        float pv[2], dv[2];
 #pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        const int r = r0 + 2 * e2 + w;
-                        const int ql = qt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
-                        if (need_mask && key > q0 + ql) pe = 0.0f;
-                        pv[w] = pe;
-                        dv[w] = pe * (dp[qt][r] - Ds[ql]);
+                        for (int w = 0; w < 2; ++w) {
+                            const int r = r0 + 2 * e2 + w;
+                            const int qoff = qt * 32 + (r >> 2) * 8 + (r & 3);
+                            const int ql = qoff + h * 4;
+                            float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
+                            if (CAUSAL && kq > qoff) pe = 0.0f;
+                            pv[w] = pe;
+                            dv[w] = pe * (dp[qt][r] - Ds[ql]);
+                        }
+                        pp[e2] = to_bf16x2(pv[0], pv[1]);
+                        dd[e2] = to_bf16x2(dv[0], dv[1]);
                     }
-                    pp[e2] = to_bf16x2(pv[0], pv[1]);
-                    dd[e2] = to_bf16x2(dv[0], dv[1]);
+                    pb[u] = cat8(pp[0], pp[1], pp[2], pp[3]);
+                    dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
                 }
-                pb[u] = cat8(pp[0], pp[1], pp[2], pp[3]);
-                dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
             }
-#pragma unroll
-            for (int u = 0; u < PVS; ++u) {
+            // dV^T += dO^T P and dK^T += Q^T dS. The transposed operands of
+            // contraction step u+1 are read from LDS before the products of
+            // step u are issued, so the reads overlap the matrix work.
+            bf16x8 a_do[NDT], a_q[NDT];
+            auto read_ops = [&](int u, bf16x8* ado, bf16x8* aq) {
                 const bf16* gp = dOs + (u * 16 + tr_row) * QP + tr_col;
                 const bf16* qp = Qs + (u * 16 + tr_row) * QP + tr_col;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const bf16x8 a_do = join8(lds_read_tr4(gp + dt * 32), lds_read_tr4(gp + 8 * QP + dt * 32));
-                    dvacc[dt] = mfma32(a_do, pb[u], dvacc[dt]);
-                    const bf16x8 a_q = join8(lds_read_tr4(qp + dt * 32), lds_read_tr4(qp + 8 * QP + dt * 32));
-                    dkacc[dt] = mfma32(a_q, dsb[u], dkacc[dt]);
+                    ado[dt] = join8(lds_read_tr4(gp + dt * 32), lds_read_tr4(gp + 8 * QP + dt * 32));
+                    aq[dt] = join8(lds_read_tr4(qp + dt * 32), lds_read_tr4(qp + 8 * QP + dt * 32));
+                }
+            };
+            // (d = 256 has no registers to spare for the look-ahead copy.)
+            constexpr bool LOOKAHEAD = NDT <= 4;
+            read_ops(0, a_do, a_q);
+#pragma unroll
+            for (int u = 0; u < PVS; ++u) {
+                bf16x8 n_do[NDT], n_q[NDT];
+                if (LOOKAHEAD && u + 1 < PVS) read_ops(u + 1, n_do, n_q);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    mfma32_agpr(dvacc[dt], a_do[dt], pb[u]);
+                    mfma32_agpr(dkacc[dt], a_q[dt], dsb[u]);
+                }
+                if (!LOOKAHEAD && u + 1 < PVS) read_ops(u + 1, a_do, a_q);
+                if (LOOKAHEAD && u + 1 < PVS) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) { a_do[dt] = n_do[dt]; a_q[dt] = n_q[dt]; }
                 }
             }
         }
@@ -280,6 +311,11 @@ void bwd_dkdv_kernel(BwdParams p) {
         __syncthreads();
     }
 
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        agpr_acc_ready(dkacc[dt]);
+        agpr_acc_ready(dvacc[dt]);
+    }
     if (key < N) {
         bf16* dkrow = static_cast<bf16*>(p.dk) + kv_off + (size_t)key * D;
         bf16* dvrow = static_cast<bf16*>(p.dv) + kv_off + (size_t)key * D;
@@ -390,8 +426,8 @@ void bwd_dq_kernel(BwdParams p) {
         const int kv0 = kb * BC;
         const bf16* Ks = smem + bufi * BUF;
         const bf16* Vs = Ks + BC * KP;
-        const bool active = !CAUSAL || kv0 <= qw0 + 31;
-        if (active) {
+        // Branch-free step: blocks past a wave's last query are masked to zero.
+        {
             f32x16 s[NKT], dp[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
@@ -405,29 +441,34 @@ void bwd_dq_kernel(BwdParams p) {
                     dp[kt] = mfma32(lds_read8(vp + ks * 16), gf[ks], dp[kt]);
                 }
             }
-            const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
+            // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to bf16
+            // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
+            // is masked when it is >= N or (causal) > qrow: one compare with a
+            // constant per element, skipped when the block needs no mask.
             bf16x8 dsb[PVS];
+            {
+                const bool MASKED = CAUSAL || (kv0 + BC > N);
+                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
 #pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-                const int kt = u >> 1;
-                const int r0 = (u & 1) * 8;
-                bf16x2 dd[4];
+                for (int u = 0; u < PVS; ++u) {
+                    const int kt = u >> 1;
+                    const int r0 = (u & 1) * 8;
+                    bf16x2 dd[4];
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float dv[2];
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        float dv[2];
 #pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        const int r = r0 + 2 * e2 + w;
-                        float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
-                        if (need_mask) {
-                            const int kk = kv0 + kt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                            if (kk >= N || (CAUSAL && kk > qrow)) pe = 0.0f;
+                        for (int w = 0; w < 2; ++w) {
+                            const int r = r0 + 2 * e2 + w;
+                            const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
+                            float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
+                            if (MASKED && koff > lim) pe = 0.0f;
+                            dv[w] = pe * (dp[kt][r] - del);
                         }
-                        dv[w] = pe * (dp[kt][r] - del);
+                        dd[e2] = to_bf16x2(dv[0], dv[1]);
                     }
-                    dd[e2] = to_bf16x2(dv[0], dv[1]);
+                    dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
                 }
-                dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
             }
 #pragma unroll
             for (int u = 0; u < PVS; ++u) {
@@ -464,34 +505,43 @@ void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- launch
 
 template <int D, bool CAUSAL>
-static hipError_t launch_bwd_dc(const BwdParams& p, hipStream_t stream) {
-    const long long rows = (long long)p.B * p.Hq * p.N;
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                       static_cast<const bf16*>(p.o), static_cast<const bf16*>(p.dout), p.delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long nkb = (p.N + 127) / 128;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * p.B * p.Hkv)), dim3(256), 0,
-                       stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long nqb = (p.N + 127) / 128;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0,
-                       stream, p);
-    return hipGetLastError();
+static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stream) {
+    if (passes & kBwdPre) {
+        const long long rows = (long long)p.B * p.Hq * p.N;
+        hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                           stream, static_cast<const bf16*>(p.o), static_cast<const bf16*>(p.dout),
+                           p.delta, rows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (passes & kBwdDkDv) {
+        const long long nkb = (p.N + 127) / 128;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * p.B * p.Hkv)), dim3(256),
+                           0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (passes & kBwdDq) {
+        const long long nqb = (p.N + 127) / 128;
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0,
+                           stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t stream) {
-    return causal ? launch_bwd_dc<D, true>(p, stream) : launch_bwd_dc<D, false>(p, stream);
+static hipError_t launch_bwd_d(const BwdParams& p, bool causal, int passes, hipStream_t stream) {
+    return causal ? launch_bwd_dc<D, true>(p, passes, stream) : launch_bwd_dc<D, false>(p, passes, stream);
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, int passes, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_bwd_d<64>(p, causal, stream);
-        case 80: return launch_bwd_d<80>(p, causal, stream);
-        case 128: return launch_bwd_d<128>(p, causal, stream);
-        case 256: return launch_bwd_d<256>(p, causal, stream);
+        case 64: return launch_bwd_d<64>(p, causal, passes, stream);
+        case 80: return launch_bwd_d<80>(p, causal, passes, stream);
+        case 128: return launch_bwd_d<128>(p, causal, passes, stream);
+        case 256: return launch_bwd_d<256>(p, causal, passes, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -38,6 +38,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Accumulating MFMA with the accumulator pinned in AGPRs (acc += a * b).
+// Used for long-lived accumulators that only matrix instructions touch inside
+// a loop, so that they do not compete with the loop's working set for VGPRs.
+// Written as inline assembly, so the compiler's hazard tracking does not see
+// it; the hazards it can meet are handled here:
+//  * a VALU write of an A/B operand VGPR followed by the MFMA read needs two
+//    wait states: the s_nop 1 in front of the instruction;
+//  * back-to-back accumulation into the same registers (srcC == vdst) is
+//    interlocked by the hardware;
+//  * reading the result with VALU instructions needs the MFMA to have drained:
+//    call agpr_acc_ready() on the accumulator before any such read.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states after the last mfma32_agpr into `acc` before VALU reads of it
+// (more than the 8-pass XDL write -> VALU read requirement).
+__device__ __forceinline__ void agpr_acc_ready(f32x16& acc) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
 // Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
     f32x2 x = {a, b};

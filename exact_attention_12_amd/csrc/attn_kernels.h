@@ -76,6 +76,8 @@ bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan);
 // Launchers return the hipError_t of the launch.
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, long long workgroups,
                       hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+// Backward passes: bit 0 = row-term preprocess, bit 1 = dK/dV, bit 2 = dQ.
+enum BwdPass { kBwdPre = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7 };
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, int passes, hipStream_t stream);
 
 }  // namespace attn

@@ -112,6 +112,31 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      void* stream);
 
+/*
+ * The three passes attn_bwd runs, in order, for callers that schedule them
+ * separately (for example the dK/dV and dQ passes on two streams after the
+ * preprocess, or to time each pass). Arguments mean exactly what they mean
+ * for attn_bwd; each validates them the same way and enqueues one kernel.
+ *   attn_bwd_preprocess: workspace <- D_i = <dout_i, o_i> per query row.
+ *   attn_bwd_dkdv: dk, dv from q, k, v, lse, dout and the workspace.
+ *   attn_bwd_dq:   dq from q, k, v, lse, dout and the workspace.
+ * The dK/dV and dQ passes read the workspace the preprocess wrote, so they
+ * must run after it completes (same stream, or an event between streams).
+ */
+attn_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                                size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                                void* stream);
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                          const void* dout, void* dk, void* dv,
+                          const void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                          void* stream);
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dq,
+                        const void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                        void* stream);
+
 /* Static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);
 

@@ -121,3 +121,30 @@ def test_fwd_plan(L):
     with pytest.raises(ea.AttnError) as e:
         ea.fwd_plan(1, 8, 8, 400, 96)
     assert e.value.name == "ATTN_ERR_HEAD_DIM"
+
+
+def test_pass_entry_points_validate(L):
+    ws, wsb = P, 1 << 20
+    # preprocess: o, dout, workspace
+    assert L.attn_bwd_preprocess(None, P, ws, wsb, 1, 2, 1, 8, 64, None) == 1
+    assert L.attn_bwd_preprocess(P, None, ws, wsb, 1, 2, 1, 8, 64, None) == 1
+    assert L.attn_bwd_preprocess(P, P, None, wsb, 1, 2, 1, 8, 64, None) == 7
+    assert L.attn_bwd_preprocess(P, P + 2, ws, wsb, 1, 2, 1, 8, 64, None) == 6
+    assert L.attn_bwd_preprocess(P, P, ws, 4, 1, 2, 1, 8, 64, None) == 7
+    assert L.attn_bwd_preprocess(P, P, ws, wsb, 1, 2, 1, 8, 96, None) == 4
+    # dK/dV pass: q, k, v, lse, dout, dk, dv, workspace
+    for i in range(7):
+        a = [P] * 7
+        a[i] = None
+        assert L.attn_bwd_dkdv(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, None) == 1
+        a[i] = P + 8
+        assert L.attn_bwd_dkdv(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, None) == 6
+    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 2, 1, 8, 64, -1.0, 1, None) == 5
+    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 3, 2, 8, 64, 0.125, 1, None) == 3
+    # dQ pass: q, k, v, lse, dout, dq, workspace
+    for i in range(6):
+        a = [P] * 6
+        a[i] = None
+        assert L.attn_bwd_dq(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 0, None) == 1
+    assert L.attn_bwd_dq(*[P] * 6, None, wsb, 1, 2, 1, 8, 64, 0.125, 0, None) == 7
+    assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 0, 64, 0.125, 0, None) == 2

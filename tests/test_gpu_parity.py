@@ -113,3 +113,16 @@ def test_outputs_fully_overwritten():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, gn):
         assert torch.equal(a, b)
+
+
+def test_separate_passes_match_fused_call():
+    inp = parity.to_gpu(si.make_inputs(2, 6, 3, 333, 128, seed=21, with_do=True))
+    for causal in (False, True):
+        o, lse = ea.fwd(inp["q"], inp["k"], inp["v"], causal=causal)
+        ref = ea.bwd(inp["q"], inp["k"], inp["v"], o, lse, inp["do"], causal=causal)
+        outs = [torch.full_like(t, float("nan")) for t in ref]
+        ws = torch.empty(ea.bwd_workspace_bytes(2, 6, 3, 333, 128), dtype=torch.uint8, device="cuda")
+        ea.bwd_passes(inp["q"], inp["k"], inp["v"], o, lse, inp["do"], *outs, ws, causal=causal)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a, b)
