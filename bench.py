@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--calibration-copy-mib", type=int, default=256,
                     help="size of the plain copy kernel run once after timing (its HBM counters "
                          "calibrate the byte counters of the attention kernels); 0 disables")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "OUT_MD"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of this script and the JSON "
+                         "line of a bench run into a markdown summary and exit")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
                          "into a traffic summary file and exit")
@@ -68,11 +71,14 @@ def kernel_flop_credit(w):
     }
 
 
+# Files each kernel is built from (relative to the package); the build script
+# is included because its flags change the generated code.
+_COMMON = ["csrc/attn_device.h", "csrc/attn_kernels.h", "build.py"]
 KERNEL_SOURCES = {
-    "fwd_kernel": ["attn_fwd.hip", "attn_device.h", "attn_kernels.h"],
-    "bwd_dkdv_kernel": ["attn_bwd.hip", "attn_device.h", "attn_kernels.h"],
-    "bwd_dq_kernel": ["attn_bwd.hip", "attn_device.h", "attn_kernels.h"],
-    "bwd_pre_kernel": ["attn_bwd.hip", "attn_device.h", "attn_kernels.h"],
+    "fwd_kernel": ["csrc/attn_fwd.hip", *_COMMON],
+    "bwd_dkdv_kernel": ["csrc/attn_bwd.hip", "csrc/attn_bwd_common.h", *_COMMON],
+    "bwd_pre_kernel": ["csrc/attn_bwd.hip", "csrc/attn_bwd_common.h", *_COMMON],
+    "bwd_dq_kernel": ["csrc/attn_bwd_dq.hip", "csrc/attn_bwd_common.h", *_COMMON],
 }
 CALIBRATION_KERNEL = "neg_kernel"
 
@@ -83,7 +89,7 @@ def source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "exact_attention_12_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, "exact_attention_12_amd", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -256,8 +262,51 @@ def parity_sample(w, inputs, o, lse):
     return {"head": [int(b), int(h)], "rows": int(len(rows)), "o_max_abs_err": eo, "lse_max_abs_err": el}
 
 
+def summarize_trace(trace_dir, bench_json, out_md, workload):
+    """Markdown table of a kernel-trace stats CSV next to the bench's own
+    HIP-event timings of the same build."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    w = si.WORKLOADS[workload]
+    b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    out = [f"# Kernel trace: {workload} (B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, N={w.N}, d={w.d}, "
+           f"{'causal' if w.causal else 'no mask'}, {'fwd+bwd' if w.backward else 'fwd'})", "",
+           "Commands (repository root on the MI355X box):", "",
+           f"    cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d <trace_dir> -o trace -- "
+           f"python <repo>/bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+           f"    python bench.py --workload {workload} > <bench_json>",
+           f"    python bench.py --workload {workload} --summarize-trace <trace_dir> <bench_json> <this file>",
+           "", "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(files[0])):
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "")
+        if CALIBRATION_KERNEL in name:
+            short = "calibration copy (torch neg, float32)"
+        elif "attn::" not in name:
+            short = short[:60]
+        out.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    out += ["", "HIP-event timings of the same build (bench run):", "",
+            "| kernel | avg ms | credited TFLOP/s | % of 2.5 PFLOP/s |", "|---|---|---|---|"]
+    for name, v in b["kernels"].items():
+        out.append(f"| {name} | {v['ms']} | {v['tflops']} | {v['pct_of_bf16_peak']} |")
+    out += ["", f"Step: {b['ms_per_step']} ms = {b['value']} TFLOP/s algorithmic "
+                f"({b['pct_of_bf16_peak']}% of the bf16 peak); roofline kernel "
+                f"{b['roofline']['kernel']} at {b['roofline']['achieved']} {b['roofline']['unit']} "
+                f"(frac {b['roofline']['frac']})."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(out_md)
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.workload)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload, args.calibration_copy_mib)
         return

@@ -46,6 +46,7 @@ class AttnError(RuntimeError):
 
 class AttnPlan(ctypes.Structure):
     _fields_ = [
+        ("rows_per_wave", ctypes.c_int),
         ("block_q", ctypes.c_int),
         ("block_kv", ctypes.c_int),
         ("threads", ctypes.c_int),

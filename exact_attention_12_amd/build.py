@@ -21,7 +21,14 @@ LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+# Sources and their extra flags. The dK/dV pass runs one wave per SIMD, so it
+# is scheduled for instruction-level parallelism rather than for occupancy.
+SOURCES = {
+    "attn_api.cpp": [],
+    "attn_fwd.hip": [],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bwd_dq.hip": [],
+}
 
 # Packed fp32 VALU forms are turned off for all device code. MFMA results
 # and accumulators are kept in the VGPR form: otherwise, above 256 live
@@ -42,7 +49,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCES[src], "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)

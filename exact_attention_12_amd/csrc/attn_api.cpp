@@ -81,8 +81,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     p.nqb = (N + plan.block_q - 1) / plan.block_q;
     p.c = scale * kLog2eHost;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_fwd(p, d, causal != 0, plan.workgroups,
-                                       static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_fwd(p, d, causal != 0, plan, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
@@ -203,6 +202,7 @@ attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn
     if (st != ATTN_OK) return st;
     attn::FwdPlan fp;
     attn::fwd_plan(B, Hq, N, d, &fp);
+    plan->rows_per_wave = fp.rows_per_wave;
     plan->block_q = fp.block_q;
     plan->block_kv = fp.block_kv;
     plan->threads = fp.threads;

@@ -28,8 +28,7 @@
 //     read transposed from the K tile.
 #include <type_traits>
 
-#include "attn_device.h"
-#include "attn_kernels.h"
+#include "attn_bwd_common.h"
 
 namespace attn {
 
@@ -60,51 +59,6 @@ void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
     if (row < rows && j == 0) delta[row] = acc;
 }
 
-// Loads `rows` rows of a [N, D] bf16 head starting at row r0 into registers
-// (16-byte chunks, zero beyond N) and stores them to an LDS tile.
-template <int D, int ROWS, int T>
-struct TileIO {
-    static constexpr int CPR = D / 8;
-    static constexpr int CHUNKS = ROWS * CPR;
-    static constexpr int NCH = (CHUNKS + T - 1) / T;
-    uint4 r[NCH];
-
-    __device__ __forceinline__ void load(const bf16* head, int r0, int N, int tid) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * T;
-            if (CHUNKS % T == 0 || c < CHUNKS) {
-                const int row = c / CPR;
-                const int col = c - row * CPR;
-                r[i] = (r0 + row < N)
-                           ? *reinterpret_cast<const uint4*>(head + (size_t)(r0 + row) * D + col * 8)
-                           : zero4();
-            }
-        }
-    }
-    __device__ __forceinline__ void store(bf16* tile, int pitch, int tid) const {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * T;
-            if (CHUNKS % T == 0 || c < CHUNKS) {
-                const int row = c / CPR;
-                const int col = c - row * CPR;
-                *reinterpret_cast<uint4*>(tile + row * pitch + col * 8) = r[i];
-            }
-        }
-    }
-};
-
-// Zero the columns D .. round_up(D, 32) of `rows` rows of an LDS tile (read
-// by the transposing read of the last 32-wide tile, never written by loads).
-template <int D>
-__device__ __forceinline__ void zero_pad_cols(bf16* tile, int rows, int pitch, int tid, int T) {
-    constexpr int PADC = ((D + 31) / 32) * 32 - D;
-    if constexpr (PADC > 0) {
-        for (int i = tid; i < rows * PADC; i += T) tile[(i / PADC) * pitch + D + i % PADC] = (bf16)0.0f;
-    }
-}
-
 // ---------------------------------------------------------------- dK, dV
 
 template <int D, bool CAUSAL>
@@ -118,7 +72,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int PVS = BQ / 16;
     constexpr int KS = D / 16;
     constexpr int NDT = (D + 31) / 32;
-    constexpr int QP = v_pitch(D);     // Q, dO tiles: row reads and transposing reads
+    constexpr int QP = sw_pitch(D);    // Q, dO tiles: row reads and transposing reads
     constexpr int TILE = BQ * QP;
     constexpr int BUF = 2 * TILE * 2 + 2 * BQ * 4;  // bytes: Q, dO, lse2, D
 
@@ -151,8 +105,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     auto deltile = [&](int bufi) { return reinterpret_cast<float*>(smem_raw + bufi * BUF + 4 * TILE) + BQ; };
 
     for (int bufi = 0; bufi < 2; ++bufi) {
-        zero_pad_cols<D>(qtile(bufi), BQ, QP, tid, T);
-        zero_pad_cols<D>(dotile(bufi), BQ, QP, tid, T);
+        zero_pad_cols_sw<D>(qtile(bufi), BQ, QP, tid, T);
+        zero_pad_cols_sw<D>(dotile(bufi), BQ, QP, tid, T);
     }
 
     // K, V as B operands (lane = key, 8 dims per register group).
@@ -192,8 +146,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     };
     auto store_step = [&](int bufi) {
-        qio.store(qtile(bufi), QP, tid);
-        doio.store(dotile(bufi), QP, tid);
+        qio.store_sw(qtile(bufi), QP, tid);
+        doio.store_sw(dotile(bufi), QP, tid);
         if (tid < BQ) lsetile(bufi)[tid] = lse_r;
         else if (tid < 2 * BQ) deltile(bufi)[tid - BQ] = del_r;
     };
@@ -234,12 +188,11 @@ void bwd_dkdv_kernel(BwdParams p) {
             for (int qt = 0; qt < NQT; ++qt) {
                 s[qt] = f32x16{};
                 dp[qt] = f32x16{};
-                const bf16* qp = Qs + (qt * 32 + l32) * QP + h * 8;
-                const bf16* gp = dOs + (qt * 32 + l32) * QP + h * 8;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    s[qt] = mfma32(lds_read8(qp + ks * 16), kf[ks], s[qt]);
-                    dp[qt] = mfma32(lds_read8(gp + ks * 16), vf[ks], dp[qt]);
+                    const int off = sw_off(qt * 32 + l32, ks * 16 + h * 8, QP);
+                    s[qt] = mfma32(lds_read8(Qs + off), kf[ks], s[qt]);
+                    dp[qt] = mfma32(lds_read8(dOs + off), vf[ks], dp[qt]);
                 }
             }
             // P = exp2(c*S - LSE2) and dS = P (dP - D), packed to bf16 in the
@@ -280,12 +233,12 @@ void bwd_dkdv_kernel(BwdParams p) {
             // step u are issued, so the reads overlap the matrix work.
             bf16x8 a_do[NDT], a_q[NDT];
             auto read_ops = [&](int u, bf16x8* ado, bf16x8* aq) {
-                const bf16* gp = dOs + (u * 16 + tr_row) * QP + tr_col;
-                const bf16* qp = Qs + (u * 16 + tr_row) * QP + tr_col;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    ado[dt] = join8(lds_read_tr4(gp + dt * 32), lds_read_tr4(gp + 8 * QP + dt * 32));
-                    aq[dt] = join8(lds_read_tr4(qp + dt * 32), lds_read_tr4(qp + 8 * QP + dt * 32));
+                    // Rows u*16 + tr_row and +8 share (row & 7) = tr_row.
+                    const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, QP);
+                    ado[dt] = join8(lds_read_tr4(dOs + o0), lds_read_tr4(dOs + o0 + 8 * QP));
+                    aq[dt] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o0 + 8 * QP));
                 }
             };
             // (d = 256 has no registers to spare for the look-ahead copy.)
@@ -335,173 +288,6 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-// ---------------------------------------------------------------- dQ
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
-void bwd_dq_kernel(BwdParams p) {
-    constexpr int NW = 4;
-    constexpr int T = NW * 64;
-    constexpr int BQ = NW * 32;
-    constexpr int BC = (D <= 128) ? 64 : 32;
-    constexpr int KS = D / 16;
-    constexpr int NDT = (D + 31) / 32;
-    constexpr int NKT = BC / 32;
-    constexpr int PVS = BC / 16;
-    constexpr int KP = v_pitch(D);     // K tile: row reads and transposing reads
-    constexpr int VP = k_pitch(D);     // V tile: row reads only
-    constexpr int BUF = BC * (KP + VP);
-
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int h = lane >> 5;
-    const int N = p.N;
-
-    const int BH = p.B * p.Hq;
-    const int nqb = (N + BQ - 1) / BQ;
-    const int bid = blockIdx.x;
-    const int bh = bid % BH;
-    const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
-    const int hkv = hq / p.G;
-    const size_t q_off = (size_t)bh * N;
-    const size_t kv_off = ((size_t)b * p.Hkv + hkv) * N * D;
-    const bf16* Kh = static_cast<const bf16*>(p.k) + kv_off;
-    const bf16* Vh = static_cast<const bf16*>(p.v) + kv_off;
-
-    const int q0 = qb * BQ;
-    const int qw0 = q0 + wave * 32;
-    const int qrow = qw0 + l32;
-
-    for (int bufi = 0; bufi < 2; ++bufi) zero_pad_cols<D>(smem + bufi * BUF, BC, KP, tid, T);
-
-    bf16x8 qf[KS], gf[KS];
-    float lse2 = __builtin_huge_valf(), del = 0.0f;
-    if (qrow < N) {
-        const bf16* qp = static_cast<const bf16*>(p.q) + (q_off + qrow) * D + h * 8;
-        const bf16* gp = static_cast<const bf16*>(p.dout) + (q_off + qrow) * D + h * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-            gf[ks] = *reinterpret_cast<const bf16x8*>(gp + ks * 16);
-        }
-        lse2 = p.lse[q_off + qrow] * kLog2e;
-        del = p.delta[q_off + qrow];
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) { qf[ks] = bf16x8{}; gf[ks] = bf16x8{}; }
-    }
-
-    const int nkb = (N + BC - 1) / BC;
-    const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
-
-    TileIO<D, BC, T> kio, vio;
-    kio.load(Kh, 0, N, tid);
-    vio.load(Vh, 0, N, tid);
-    kio.store(smem, KP, tid);
-    vio.store(smem + BC * KP, VP, tid);
-    __syncthreads();
-
-    f32x16 dqacc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x16{};
-    const float c = p.c;
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
-    const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
-
-    for (int kb = 0; kb < kb_end; ++kb) {
-        const int bufi = kb & 1;
-        const bool has_next = kb + 1 < kb_end;
-        if (has_next) {
-            kio.load(Kh, (kb + 1) * BC, N, tid);
-            vio.load(Vh, (kb + 1) * BC, N, tid);
-        }
-        const int kv0 = kb * BC;
-        const bf16* Ks = smem + bufi * BUF;
-        const bf16* Vs = Ks + BC * KP;
-        // Branch-free step: blocks past a wave's last query are masked to zero.
-        {
-            f32x16 s[NKT], dp[NKT];
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                s[kt] = f32x16{};
-                dp[kt] = f32x16{};
-                const bf16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
-                const bf16* vp = Vs + (kt * 32 + l32) * VP + h * 8;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    s[kt] = mfma32(lds_read8(kp + ks * 16), qf[ks], s[kt]);
-                    dp[kt] = mfma32(lds_read8(vp + ks * 16), gf[ks], dp[kt]);
-                }
-            }
-            // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to bf16
-            // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
-            // is masked when it is >= N or (causal) > qrow: one compare with a
-            // constant per element, skipped when the block needs no mask.
-            bf16x8 dsb[PVS];
-            {
-                const bool MASKED = CAUSAL || (kv0 + BC > N);
-                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
-#pragma unroll
-                for (int u = 0; u < PVS; ++u) {
-                    const int kt = u >> 1;
-                    const int r0 = (u & 1) * 8;
-                    bf16x2 dd[4];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        float dv[2];
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            const int r = r0 + 2 * e2 + w;
-                            const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
-                            float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
-                            if (MASKED && koff > lim) pe = 0.0f;
-                            dv[w] = pe * (dp[kt][r] - del);
-                        }
-                        dd[e2] = to_bf16x2(dv[0], dv[1]);
-                    }
-                    dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-                const bf16* kp = Ks + (u * 16 + tr_row) * KP + tr_col;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const bf16x8 a = join8(lds_read_tr4(kp + dt * 32), lds_read_tr4(kp + 8 * KP + dt * 32));
-                    dqacc[dt] = mfma32(a, dsb[u], dqacc[dt]);
-                }
-            }
-        }
-        if (has_next) {
-            kio.store(smem + (bufi ^ 1) * BUF, KP, tid);
-            vio.store(smem + (bufi ^ 1) * BUF + BC * KP, VP, tid);
-        }
-        __syncthreads();
-    }
-
-    if (qrow < N) {
-        bf16* dqrow = static_cast<bf16*>(p.dq) + (q_off + qrow) * D;
-        const float sc = p.scale;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = dt * 32 + g4 * 8 + h * 4;
-                if (d < D)
-                    store_bf16x4(dqrow + d, dqacc[dt][g4 * 4 + 0] * sc, dqacc[dt][g4 * 4 + 1] * sc,
-                                 dqacc[dt][g4 * 4 + 2] * sc, dqacc[dt][g4 * 4 + 3] * sc);
-            }
-    }
-}
-
 // ---------------------------------------------------------------- launch
 
 template <int D, bool CAUSAL>
@@ -522,10 +308,7 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
         if (e != hipSuccess) return e;
     }
     if (passes & kBwdDq) {
-        const long long nqb = (p.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0,
-                           stream, p);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_bwd_dq(p, D, CAUSAL, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

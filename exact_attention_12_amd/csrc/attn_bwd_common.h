@@ -1,0 +1,67 @@
+// attn_bwd_common.h - tile helpers shared by the backward kernels.
+#pragma once
+
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+
+// Loads `rows` rows of a [N, D] bf16 head starting at row r0 into registers
+// (16-byte chunks, zero beyond N) and stores them to an LDS tile.
+template <int D, int ROWS, int T>
+struct TileIO {
+    static constexpr int CPR = D / 8;
+    static constexpr int CHUNKS = ROWS * CPR;
+    static constexpr int NCH = (CHUNKS + T - 1) / T;
+    uint4 r[NCH];
+
+    __device__ __forceinline__ void load(const bf16* head, int r0, int N, int tid) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * T;
+            if (CHUNKS % T == 0 || c < CHUNKS) {
+                const int row = c / CPR;
+                const int col = c - row * CPR;
+                r[i] = (r0 + row < N)
+                           ? *reinterpret_cast<const uint4*>(head + (size_t)(r0 + row) * D + col * 8)
+                           : zero4();
+            }
+        }
+    }
+    __device__ __forceinline__ void store(bf16* tile, int pitch, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * T;
+            if (CHUNKS % T == 0 || c < CHUNKS) {
+                const int row = c / CPR;
+                const int col = c - row * CPR;
+                *reinterpret_cast<uint4*>(tile + row * pitch + col * 8) = r[i];
+            }
+        }
+    }
+    // Same, into a chunk-swizzled tile (sw_off).
+    __device__ __forceinline__ void store_sw(bf16* tile, int pitch, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + i * T;
+            if (CHUNKS % T == 0 || c < CHUNKS) {
+                const int row = c / CPR;
+                const int col = c - row * CPR;
+                *reinterpret_cast<uint4*>(tile + sw_off(row, col * 8, pitch)) = r[i];
+            }
+        }
+    }
+};
+
+// Zero the columns D .. round_up(D, 32) of `rows` rows of a chunk-swizzled
+// LDS tile (read by the transposing read of the last 32-wide tile, never
+// written by the loads).
+template <int D>
+__device__ __forceinline__ void zero_pad_cols_sw(bf16* tile, int rows, int pitch, int tid, int T) {
+    constexpr int PADC = ((D + 31) / 32) * 32 - D;
+    if constexpr (PADC > 0) {
+        for (int i = tid; i < rows * PADC; i += T) tile[sw_off(i / PADC, D + i % PADC, pitch)] = (bf16)0.0f;
+    }
+}
+
+}  // namespace attn

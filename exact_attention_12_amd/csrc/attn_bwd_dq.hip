@@ -1,0 +1,199 @@
+// attn_bwd_dq.hip - dQ pass of the attention backward, for gfx950.
+//
+// One workgroup per (batch, query head, 128-row query block), in the
+// forward's orientation: S^T = K Q^T and dP^T = V dO^T put one query per
+// lane, so LSE_i and D_i are per-lane scalars; dQ^T += K^T dS^T with K^T read
+// from the (chunk-swizzled) K tile by the transposing LDS read. It is a
+// separate translation unit because it is scheduled for occupancy (two waves
+// per SIMD), while the dK/dV pass, one wave per SIMD, is scheduled for ILP.
+// The formulas are the chain rule written out in attn_bwd.hip.
+#include <type_traits>
+
+#include "attn_bwd_common.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------- dQ
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
+void bwd_dq_kernel(BwdParams p) {
+    constexpr int NW = 4;
+    constexpr int T = NW * 64;
+    constexpr int BQ = NW * 32;
+    constexpr int BC = 32;  // keys per step: keeps two waves per SIMD without spills
+    constexpr int KS = D / 16;
+    constexpr int NDT = (D + 31) / 32;
+    constexpr int NKT = BC / 32;
+    constexpr int PVS = BC / 16;
+    constexpr int KP = sw_pitch(D);    // K tile: row reads and transposing reads
+    constexpr int VP = k_pitch(D);     // V tile: row reads only
+    constexpr int BUF = BC * (KP + VP);
+
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int N = p.N;
+
+    const int BH = p.B * p.Hq;
+    const int nqb = (N + BQ - 1) / BQ;
+    const int bid = blockIdx.x;
+    const int bh = bid % BH;
+    const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hkv = hq / p.G;
+    const size_t q_off = (size_t)bh * N;
+    const size_t kv_off = ((size_t)b * p.Hkv + hkv) * N * D;
+    const bf16* Kh = static_cast<const bf16*>(p.k) + kv_off;
+    const bf16* Vh = static_cast<const bf16*>(p.v) + kv_off;
+
+    const int q0 = qb * BQ;
+    const int qw0 = q0 + wave * 32;
+    const int qrow = qw0 + l32;
+
+    for (int bufi = 0; bufi < 2; ++bufi) zero_pad_cols_sw<D>(smem + bufi * BUF, BC, KP, tid, T);
+
+    bf16x8 qf[KS], gf[KS];
+    float lse2 = __builtin_huge_valf(), del = 0.0f;
+    if (qrow < N) {
+        const bf16* qp = static_cast<const bf16*>(p.q) + (q_off + qrow) * D + h * 8;
+        const bf16* gp = static_cast<const bf16*>(p.dout) + (q_off + qrow) * D + h * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+            gf[ks] = *reinterpret_cast<const bf16x8*>(gp + ks * 16);
+        }
+        lse2 = p.lse[q_off + qrow] * kLog2e;
+        del = p.delta[q_off + qrow];
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) { qf[ks] = bf16x8{}; gf[ks] = bf16x8{}; }
+    }
+
+    const int nkb = (N + BC - 1) / BC;
+    const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
+
+    TileIO<D, BC, T> kio, vio;
+    kio.load(Kh, 0, N, tid);
+    vio.load(Vh, 0, N, tid);
+    kio.store_sw(smem, KP, tid);
+    vio.store(smem + BC * KP, VP, tid);
+    __syncthreads();
+
+    f32x16 dqacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x16{};
+    const float c = p.c;
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
+    const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
+
+    for (int kb = 0; kb < kb_end; ++kb) {
+        const int bufi = kb & 1;
+        const bool has_next = kb + 1 < kb_end;
+        if (has_next) {
+            kio.load(Kh, (kb + 1) * BC, N, tid);
+            vio.load(Vh, (kb + 1) * BC, N, tid);
+        }
+        const int kv0 = kb * BC;
+        const bf16* Ks = smem + bufi * BUF;
+        const bf16* Vs = Ks + BC * KP;
+        // Branch-free step: blocks past a wave's last query are masked to zero.
+        {
+            f32x16 s[NKT], dp[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                s[kt] = f32x16{};
+                dp[kt] = f32x16{};
+                const bf16* vp = Vs + (kt * 32 + l32) * VP + h * 8;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s[kt] = mfma32(lds_read8(Ks + sw_off(kt * 32 + l32, ks * 16 + h * 8, KP)), qf[ks], s[kt]);
+                    dp[kt] = mfma32(lds_read8(vp + ks * 16), gf[ks], dp[kt]);
+                }
+            }
+            // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to bf16
+            // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
+            // is masked when it is >= N or (causal) > qrow: one compare with a
+            // constant per element, skipped when the block needs no mask.
+            bf16x8 dsb[PVS];
+            {
+                const bool MASKED = CAUSAL || (kv0 + BC > N);
+                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
+#pragma unroll
+                for (int u = 0; u < PVS; ++u) {
+                    const int kt = u >> 1;
+                    const int r0 = (u & 1) * 8;
+                    bf16x2 dd[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        float dv[2];
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            const int r = r0 + 2 * e2 + w;
+                            const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
+                            float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
+                            if (MASKED && koff > lim) pe = 0.0f;
+                            dv[w] = pe * (dp[kt][r] - del);
+                        }
+                        dd[e2] = to_bf16x2(dv[0], dv[1]);
+                    }
+                    dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < PVS; ++u) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, KP);
+                    const bf16x8 a = join8(lds_read_tr4(Ks + o0), lds_read_tr4(Ks + o0 + 8 * KP));
+                    dqacc[dt] = mfma32(a, dsb[u], dqacc[dt]);
+                }
+            }
+        }
+        if (has_next) {
+            kio.store_sw(smem + (bufi ^ 1) * BUF, KP, tid);
+            vio.store(smem + (bufi ^ 1) * BUF + BC * KP, VP, tid);
+        }
+        __syncthreads();
+    }
+
+    if (qrow < N) {
+        bf16* dqrow = static_cast<bf16*>(p.dq) + (q_off + qrow) * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = dt * 32 + g4 * 8 + h * 4;
+                if (d < D)
+                    store_bf16x4(dqrow + d, dqacc[dt][g4 * 4 + 0] * sc, dqacc[dt][g4 * 4 + 1] * sc,
+                                 dqacc[dt][g4 * 4 + 2] * sc, dqacc[dt][g4 * 4 + 3] * sc);
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
+    const long long nqb = (p.N + 127) / 128;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+    switch (d) {
+        case 64: return causal ? launch_dq_dc<64, true>(p, stream) : launch_dq_dc<64, false>(p, stream);
+        case 80: return causal ? launch_dq_dc<80, true>(p, stream) : launch_dq_dc<80, false>(p, stream);
+        case 128: return causal ? launch_dq_dc<128, true>(p, stream) : launch_dq_dc<128, false>(p, stream);
+        case 256: return causal ? launch_dq_dc<256, true>(p, stream) : launch_dq_dc<256, false>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn

@@ -18,15 +18,31 @@ template <> struct FwdTile<80>  { static constexpr int WAVES = 4, BLOCK_KV = 64;
 template <> struct FwdTile<128> { static constexpr int WAVES = 4, BLOCK_KV = 64; };
 template <> struct FwdTile<256> { static constexpr int WAVES = 4, BLOCK_KV = 32; };
 
-// Row pitches (in bf16 elements) of the LDS tiles.
-//  K tile, read 16 bytes per lane along d: pad one 16-byte chunk per row so
-//  that consecutive rows start in different banks.
-//  V tile, read with the transposing read (4 rows x 32 bytes per 16 lanes):
-//  the row pitch is an odd multiple of 32 bytes modulo 128 so that the four
-//  rows of one read land in different banks; rows are at least the padded
-//  output width (a multiple of 32 columns), the columns beyond d being zero.
+// Row pitches (in bf16 elements) of the LDS tiles. gfx950's LDS serves
+// 64 banks x 4 bytes, i.e. 256 bytes per cycle; measured on the part:
+//  * 16-byte row reads (lane i reads row i, same column; the S = K Q^T and
+//    dP operands) reach their conflict floor when the pitch is an odd
+//    multiple of 16 bytes modulo 256: pitch d + 8 elements;
+//  * the transposing read (each 16-lane group reads 4 rows x 32 bytes, two
+//    groups per cycle) is conflict free when the pitch is 64 or 192 bytes
+//    modulo 256: v_pitch;
+//  * a tile read both ways uses the 64-mod-256 pitch with its 16-byte chunks
+//    XOR-swizzled by (row & 7), which keeps both patterns at their floor:
+//    sw_pitch and sw_off. The swizzle permutes chunks inside aligned groups
+//    of 8, so the pitch must hold round_up(chunks, 8) chunks.
 constexpr int k_pitch(int d) { return d + 8; }
-constexpr int v_pitch(int d) { return ((d + 31) / 32) * 32 + 16; }
+constexpr int pitch_64mod256(int row_bytes) {
+    return (row_bytes + (((64 - row_bytes) % 128) + 128) % 128) / 2;
+}
+constexpr int v_pitch(int d) { return pitch_64mod256(((d + 31) / 32) * 32 * 2); }
+constexpr int sw_pitch(int d) { return pitch_64mod256(((d / 8 + 7) / 8) * 8 * 16); }
+static_assert(v_pitch(64) == 96 && v_pitch(80) == 96 && v_pitch(128) == 160 && v_pitch(256) == 288, "");
+static_assert(sw_pitch(64) == 96 && sw_pitch(80) == 160 && sw_pitch(128) == 160 && sw_pitch(256) == 288, "");
+
+// Element offset of (row, col) in a swizzled tile (chunk = 8 elements).
+__host__ __device__ constexpr int sw_off(int row, int col, int pitch) {
+    return row * pitch + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
 
 struct FwdParams {
     const void* q;
@@ -64,6 +80,7 @@ struct BwdParams {
 };
 
 struct FwdPlan {
+    int rows_per_wave;  // 32 (fwd_kernel) or 64 (fwd_kernel_r64)
     int block_q;
     int block_kv;
     int threads;
@@ -74,10 +91,11 @@ struct FwdPlan {
 bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan);
 
 // Launchers return the hipError_t of the launch.
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, long long workgroups,
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, const FwdPlan& plan,
                       hipStream_t stream);
 // Backward passes: bit 0 = row-term preprocess, bit 1 = dK/dV, bit 2 = dQ.
 enum BwdPass { kBwdPre = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7 };
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, int passes, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
 }  // namespace attn

@@ -147,12 +147,13 @@ const char* attn_status_string(attn_status status);
 const char* attn_last_hip_error(void);
 
 /*
- * Tile plan of the forward kernel for a shape: rows of Q per workgroup,
- * keys per inner step, threads per workgroup, number of workgroups and
- * bytes of LDS per workgroup. Host-only arithmetic (no device call).
- * Returns ATTN_OK or the validation error for that shape.
+ * Tile plan of the forward kernel for a shape: query rows per wave (32 or
+ * 64), rows of Q per workgroup, keys per inner step, threads per workgroup,
+ * number of workgroups and bytes of LDS per workgroup. Host-only arithmetic
+ * (no device call). Returns ATTN_OK or the validation error for that shape.
  */
 typedef struct attn_plan {
+    int rows_per_wave;
     int block_q;
     int block_kv;
     int threads;
