@@ -22,8 +22,12 @@
 //  * O^T += V^T P^T: the probabilities, converted to bf16, are already laid
 //    out as the B operand (a lane holds 8 keys of its query); V^T is read as
 //    the A operand straight from the row-major V tile with the transposing
-//    LDS read. O^T keeps one query per lane, so the rescale by
+//    LDS read. O^T keeps one query per lane, so a rescale by
 //    exp(m_old - m_new) needs no data movement.
+//  * Rescaling is lazy: the reference maximum only moves when a block's row
+//    maximum exceeds it by more than 2^8 (probabilities stay <= 2^8; O and l
+//    share the reference, so O / l and the LSE are unchanged). On the
+//    synthetic workloads this skips the rescale after the first block.
 //  * The row sum l is accumulated in fp32 from the unrounded probabilities
 //    (only the matrix-product operand is rounded to bf16), so LSE carries no
 //    bf16 rounding bias even for rows with few keys.
@@ -41,10 +45,9 @@
 
 namespace attn {
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, (D <= 128 ? 2 : 1))
 void fwd_kernel(FwdParams p) {
-    constexpr int NW = FwdTile<D>::WAVES;
     constexpr int T = NW * 64;
     constexpr int BQ = NW * 32;
     constexpr int BC = FwdTile<D>::BLOCK_KV;
@@ -196,10 +199,20 @@ void fwd_kernel(FwdParams p) {
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = max_across_halves(mx);
-            const float m_new = fmaxf(m, mx * c);
-            const float alpha = fast_exp2(m - m_new);
-            m = m_new;
+            // Lazy rescaling (see fwd_kernel_r64): the reference maximum m only
+            // moves, and O, l are rescaled, when a row's block maximum exceeds
+            // it by more than 2^8; the first block just adopts its maximum.
+            const float mb = max_across_halves(mx) * c;
+            if (m == -__builtin_huge_valf()) m = mb;
+            if (__any(mb > m + 8.0f)) {
+                const float m_new = fmaxf(m, mb);
+                const float alpha = fast_exp2(m - m_new);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+            }
+            const float m_new = m;
 
             bf16x8 pb[PVS];
             float lsum = 0.0f;
@@ -217,9 +230,7 @@ void fwd_kernel(FwdParams p) {
                 }
                 pb[u] = cat8(pr[0], pr[1], pr[2], pr[3]);
             }
-            l = fmaf(l, alpha, lsum);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+            l += lsum;
 
 #pragma unroll
             for (int u = 0; u < PVS; ++u) {
@@ -505,6 +516,7 @@ void fwd_kernel_r64(FwdParams p) {
     }
 }
 
+
 template <int D>
 static hipError_t launch_fwd_d(const FwdParams& p, bool causal, const FwdPlan& plan, hipStream_t stream) {
     const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
@@ -516,17 +528,21 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, const FwdPlan& p
                 hipLaunchKernelGGL((fwd_kernel_r64<D, false>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
+        if (plan.waves == 8) {
+            if (causal)
+                hipLaunchKernelGGL((fwd_kernel<D, true, 8>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((fwd_kernel<D, false, 8>), grid, block, 0, stream, p);
+            return hipGetLastError();
+        }
     }
     if (causal)
-        hipLaunchKernelGGL((fwd_kernel<D, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, true, 4>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, false, 4>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-// Tile plan: the 64-rows-per-wave kernel when it still gives every CU at
-// least one workgroup (it halves LDS traffic per flop), else the 32-row one
-// (twice the workgroups, two per CU) for short sequences and d = 256.
 // The 64-row kernel is used when it yields at least this many workgroups.
 // Measured on MI355X it is still slower than the 32-row kernel at every
 // listed shape (one wave per SIMD exposes the LDS latency of the S^T phase),
@@ -535,16 +551,22 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, const FwdPlan& p
 #define ATTN_FWD_R64_MIN_WORKGROUPS 0x7fffffffffffLL
 #endif
 
+// Tile plan. 8 waves (256 rows) per workgroup share one K/V pipeline, which
+// halves global-load issue and LDS stores per row; used while that still
+// gives every CU a workgroup. Shorter sequences use 4 waves (twice the
+// workgroups); d = 256 always uses 4.
 template <int D>
 static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
-    const long long wg64 = (long long)((N + 255) / 256) * B * Hq;
-    const bool r64 = D <= 128 && wg64 >= ATTN_FWD_R64_MIN_WORKGROUPS;
-    const int BQ = r64 ? 256 : FwdTile<D>::WAVES * 32;
+    const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
+    const bool r64 = D <= 128 && wg256 >= ATTN_FWD_R64_MIN_WORKGROUPS;
+    const int waves = (r64 || (D <= 128 && wg256 >= 256)) ? (r64 ? 4 : 8) : 4;
+    const int BQ = r64 ? 256 : waves * 32;
     const int BC = r64 ? 64 : FwdTile<D>::BLOCK_KV;
     plan->rows_per_wave = r64 ? 64 : 32;
+    plan->waves = waves;
     plan->block_q = BQ;
     plan->block_kv = BC;
-    plan->threads = 256;
+    plan->threads = waves * 64;
     plan->workgroups = (long long)((N + BQ - 1) / BQ) * B * Hq;
     plan->lds_bytes = 2 * BC * (k_pitch(D) + v_pitch(D)) * 2;
 }

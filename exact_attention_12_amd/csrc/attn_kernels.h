@@ -8,15 +8,16 @@
 
 namespace attn {
 
-// Forward tile plan per head dimension: 4 waves, 32 query rows per wave,
-// BLOCK_KV keys per inner step. The keys-per-step choice keeps two
-// workgroups resident per CU (LDS double buffer + registers) for d <= 128;
-// d = 256 halves it to keep the accumulator and Q operand in registers.
+// Forward tile plan per head dimension: 32 query rows per wave, 4 or 8 waves
+// per workgroup (chosen per shape), BLOCK_KV keys per inner step. The
+// keys-per-step choice keeps two waves per SIMD (LDS double buffer +
+// registers) for d <= 128; d = 256 halves it to keep the accumulator and Q
+// operand in registers.
 template <int D> struct FwdTile;
-template <> struct FwdTile<64>  { static constexpr int WAVES = 4, BLOCK_KV = 64; };
-template <> struct FwdTile<80>  { static constexpr int WAVES = 4, BLOCK_KV = 64; };
-template <> struct FwdTile<128> { static constexpr int WAVES = 4, BLOCK_KV = 64; };
-template <> struct FwdTile<256> { static constexpr int WAVES = 4, BLOCK_KV = 32; };
+template <> struct FwdTile<64>  { static constexpr int BLOCK_KV = 64; };
+template <> struct FwdTile<80>  { static constexpr int BLOCK_KV = 64; };
+template <> struct FwdTile<128> { static constexpr int BLOCK_KV = 64; };
+template <> struct FwdTile<256> { static constexpr int BLOCK_KV = 32; };
 
 // Row pitches (in bf16 elements) of the LDS tiles. gfx950's LDS serves
 // 64 banks x 4 bytes, i.e. 256 bytes per cycle; measured on the part:
@@ -81,6 +82,7 @@ struct BwdParams {
 
 struct FwdPlan {
     int rows_per_wave;  // 32 (fwd_kernel) or 64 (fwd_kernel_r64)
+    int waves;          // waves per workgroup
     int block_q;
     int block_kv;
     int threads;
