@@ -12,7 +12,7 @@ comment both give for Q, K, V.
 
 Notation: per (b, hq), query rows i and key rows j in [0, N); G = Hq / Hkv;
 hkv = hq // G; s_ij = scale * <q_i, k_j>; the allowed key set A_i is all j < N
-(no mask) or j <= i (causal mask).
+(no mask), j <= i (causal mask) or i - W < j <= i (sliding window of W keys).
 """
 
 from __future__ import annotations
@@ -45,25 +45,33 @@ def kv_head_of(hq: int, Hq: int, Hkv: int) -> int:
     return hq // (Hq // Hkv)
 
 
-def allowed_mask(row0: int, nrows: int, N: int, causal: bool) -> np.ndarray:
+def allowed_mask(row0: int, nrows: int, N: int, causal: bool, window=None) -> np.ndarray:
     """Boolean [nrows, N]: True where key j may be attended by query row0+r.
 
     [CANN-FA], tuning section on mask modes: the causal mask looks only at
     positions before the current one (the current one included, since a
-    query always sees itself in self-attention); no mask looks at everything.
+    query always sees itself in self-attention); the sliding-window mask
+    looks only at the most recent `window` positions, i.e. keys
+    i - window + 1 <= j <= i (it implies the causal mask); no mask looks at
+    everything.
     """
-    if not causal:
+    if window is not None and window < 1:
+        raise ValueError("window must be >= 1")
+    if not causal and window is None:
         return np.ones((nrows, N), dtype=bool)
     i = np.arange(row0, row0 + nrows)[:, None]
     j = np.arange(N)[None, :]
-    return j <= i
+    ok = j <= i
+    if window is not None:
+        ok &= j > i - window
+    return ok
 
 
-def _scores(q, k, scale, row0, causal):
+def _scores(q, k, scale, row0, causal, window=None):
     # [CANN-FA] standard attention code, step 1: scores = Q @ K^T / sqrt(d_k);
     # the scale is an explicit argument so that any value can be checked.
     S = (q @ k.T) * scale
-    mask = allowed_mask(row0, q.shape[0], k.shape[0], causal)
+    mask = allowed_mask(row0, q.shape[0], k.shape[0], causal, window)
     return np.where(mask, S, -np.inf)
 
 
@@ -86,7 +94,7 @@ def _softmax_rows(S):
     return P, lse
 
 
-def ref_fwd_head(q, k, v, scale, causal=False, row0=0, return_sp=False):
+def ref_fwd_head(q, k, v, scale, causal=False, row0=0, return_sp=False, window=None):
     """Forward of one head for query rows row0 .. row0+len(q)-1.
 
     q: [R, d]; k, v: [N, d]. Returns O [R, d] and LSE [R] (float64), plus S and
@@ -96,7 +104,7 @@ def ref_fwd_head(q, k, v, scale, causal=False, row0=0, return_sp=False):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    S = _scores(q, k, scale, row0, causal)
+    S = _scores(q, k, scale, row0, causal, window)
     P, lse = _softmax_rows(S)
     O = P @ v
     if return_sp:
@@ -116,7 +124,7 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, N, d
 
 
-def ref_fwd(q, k, v, scale, causal=False, heads=None, chunk=DEFAULT_CHUNK):
+def ref_fwd(q, k, v, scale, causal=False, heads=None, chunk=DEFAULT_CHUNK, window=None):
     """Forward for [B, Hq, N, d] query and [B, Hkv, N, d] key/value arrays.
 
     Returns (O [B, Hq, N, d], LSE [B, Hq, N]) in float64. ``heads`` restricts
@@ -136,13 +144,13 @@ def ref_fwd(q, k, v, scale, causal=False, heads=None, chunk=DEFAULT_CHUNK):
         vv = np.asarray(v[b, hkv], dtype=np.float64)
         for r0 in range(0, N, chunk):
             r1 = min(N, r0 + chunk)
-            o, lse = ref_fwd_head(q[b, hq, r0:r1], kk, vv, scale, causal, row0=r0)
+            o, lse = ref_fwd_head(q[b, hq, r0:r1], kk, vv, scale, causal, row0=r0, window=window)
             O[b, hq, r0:r1] = o
             LSE[b, hq, r0:r1] = lse
     return O, LSE
 
 
-def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK):
+def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK, window=None):
     """Backward of one KV head and the G query heads that share it.
 
     q, do: [G, N, d] (the query heads hkv*G .. hkv*G+G-1); k, v: [N, d].
@@ -172,7 +180,7 @@ def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK):
             r1 = min(N, r0 + chunk)
             qc = q[g, r0:r1]
             doc = do[g, r0:r1]
-            _, _, _, P = ref_fwd_head(qc, k, v, scale, causal, row0=r0, return_sp=True)
+            _, _, _, P = ref_fwd_head(qc, k, v, scale, causal, row0=r0, return_sp=True, window=window)
             dP = doc @ v.T
             row_term = (P * dP).sum(axis=1)
             dS = P * (dP - row_term[:, None])
@@ -182,7 +190,7 @@ def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK):
     return dQ, dK, dV
 
 
-def ref_bwd(q, k, v, do, scale, causal=False, kv_heads=None, chunk=DEFAULT_CHUNK):
+def ref_bwd(q, k, v, do, scale, causal=False, kv_heads=None, chunk=DEFAULT_CHUNK, window=None):
     """Backward for full [B, H, N, d] arrays; see :func:`ref_bwd_group`.
 
     ``kv_heads`` restricts the work to a list of (b, hkv) pairs (each brings its
@@ -200,14 +208,14 @@ def ref_bwd(q, k, v, do, scale, causal=False, kv_heads=None, chunk=DEFAULT_CHUNK
     for b, hkv in kv_heads:
         sl = slice(hkv * G, hkv * G + G)
         dq, dk, dv = ref_bwd_group(q[b, sl], k[b, hkv], v[b, hkv], do[b, sl],
-                                   scale, causal, chunk)
+                                   scale, causal, chunk, window)
         dQ[b, sl] = dq
         dK[b, hkv] = dk
         dV[b, hkv] = dv
     return dQ, dK, dV
 
 
-def blockwise_online_fwd(q, k, v, scale, causal=False, block_r=64, block_c=64):
+def blockwise_online_fwd(q, k, v, scale, causal=False, block_r=64, block_c=64, window=None):
     """The blockwise online-softmax forward of one head, in fp64.
 
     Follows the [CANN-FA] online-softmax pseudocode (section on online
@@ -237,10 +245,13 @@ def blockwise_online_fwd(q, k, v, scale, causal=False, block_r=64, block_c=64):
         for j0 in range(0, N, block_c):
             j1 = min(N, j0 + block_c)
             scores = (q[i0:i1] @ k[j0:j1].T) * scale
-            if causal:
+            if causal or window is not None:
                 ii = np.arange(i0, i1)[:, None]
                 jj = np.arange(j0, j1)[None, :]
-                scores = np.where(jj <= ii, scores, -np.inf)
+                ok = jj <= ii
+                if window is not None:
+                    ok &= jj > ii - window
+                scores = np.where(ok, scores, -np.inf)
             m_old = m[i0:i1]
             m_new = np.maximum(m_old, scores.max(axis=1))
             # exp(-inf - (-inf)) is undefined; a row whose keys have all been

@@ -32,7 +32,7 @@ def rng_arrays(seed, B, Hq, Hkv, N, d, with_do=True, scale_v=1.0):
 
 # ---------------------------------------------------------------- brute force
 
-def brute_force_fwd(q, k, v, scale, causal):
+def brute_force_fwd(q, k, v, scale, causal, window=None):
     """Scalar loops straight from the definitions, no max subtraction.
 
     softmax(x)_j = e^{x_j} / sum_j' e^{x_j'} ([CANN-FA] softmax definition),
@@ -50,7 +50,10 @@ def brute_force_fwd(q, k, v, scale, causal):
             for i in range(N):
                 weights = []
                 for j in range(N):
-                    if causal and j > i:
+                    if (causal or window) and j > i:
+                        weights.append(0.0)
+                        continue
+                    if window and j <= i - window:
                         weights.append(0.0)
                         continue
                     s = 0.0
@@ -333,3 +336,73 @@ def all_backward_checks(fwd, bwd):
         check_finite_differences(fwd, bwd, causal)
     for G in (1, 2, 3):
         check_gqa_is_repeated_mha(fwd, bwd, G)
+
+
+# --------------------------------------------------------- sliding window
+
+def check_window_brute_force(fwd_w, seed, B, Hq, Hkv, N, d, window, scale=0.7):
+    """[CANN-FA] sliding-window mask mode: keys i - W < j <= i only."""
+    q, k, v, _ = rng_arrays(seed, B, Hq, Hkv, N, d, with_do=False)
+    O, L = fwd_w(q, k, v, scale, window)
+    Ob, Lb = brute_force_fwd(q, k, v, scale, True, window)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L, Lb, rtol=1e-12, atol=1e-13)
+
+
+def check_window_special_cases(fwd, fwd_w):
+    """W = 1: each row sees only itself (O_i = v_i, LSE_i = s_ii). W >= N: the
+    plain causal mask. Q = 0: O_i is the mean of the last min(i+1, W) values
+    and LSE_i = ln min(i+1, W)."""
+    q, k, v, _ = rng_arrays(20, 1, 2, 1, 12, 5, with_do=False)
+    O, L = fwd_w(q, k, v, 0.6, 1)
+    np.testing.assert_allclose(O, np.repeat(v, 2, axis=1), atol=1e-14)
+    np.testing.assert_allclose(L, 0.6 * np.einsum("bhnd,bhnd->bhn", q, np.repeat(k, 2, axis=1)), atol=1e-13)
+    for W in (12, 13, 100):
+        Ow, Lw = fwd_w(q, k, v, 0.6, W)
+        Oc, Lc = fwd(q, k, v, 0.6, True)
+        np.testing.assert_allclose(Ow, Oc, atol=1e-15)
+        np.testing.assert_allclose(Lw, Lc, atol=1e-15)
+    z = np.zeros_like(q)
+    O, L = fwd_w(z, k, v, 0.6, 4)
+    for i in range(12):
+        lo = max(0, i - 3)
+        np.testing.assert_allclose(O[0, 0, i], v[0, 0, lo:i + 1].mean(0), atol=1e-14)
+        np.testing.assert_allclose(L[0, 0, i], np.log(i + 1 - lo), atol=1e-14)
+
+
+def check_window_blockwise(blockwise, fwd_head):
+    q, k, v, _ = rng_arrays(21, 1, 1, 1, 70, 8, with_do=False)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    for W in (1, 5, 33):
+        O, L = fwd_head(q, k, v, 0.5, True, window=W)
+        for br, bc in ((1, 1), (7, 7), (16, 5), (64, 64)):
+            Ob, Lb = blockwise(q, k, v, 0.5, True, br, bc, window=W)
+            np.testing.assert_allclose(Ob, O, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(Lb, L, rtol=0, atol=1e-12)
+
+
+def check_window_gradients(fwd_w, bwd_w):
+    """Finite differences and the key-shift / value-sum identities under the
+    window mask (every row still has at least one key: itself)."""
+    scale, W = 0.9, 3
+    q, k, v, do = rng_arrays(22, 1, 2, 1, 6, 3)
+    dQ, dK, dV = bwd_w(q, k, v, do, scale, W)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        O, _ = fwd_w(qq, kk, vv, scale, W)
+        return float(np.sum(O * do))
+
+    for arr, grad, which in ((q, dQ, 0), (k, dK, 1), (v, dV, 2)):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            a_p = [q.copy(), k.copy(), v.copy()]
+            a_m = [q.copy(), k.copy(), v.copy()]
+            a_p[which][idx] += h
+            a_m[which][idx] -= h
+            num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        assert np.linalg.norm(num - grad) / np.linalg.norm(grad) < 1e-7
+    np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dV.sum(axis=2), do.sum(axis=(1, 2))[:, None], atol=1e-12)

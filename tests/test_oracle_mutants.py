@@ -20,8 +20,8 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 MUTANTS = {
     "scale_dropped": ("S = (q @ k.T) * scale", "S = (q @ k.T)"),
     "gqa_modulo_mapping": ("return hq // (Hq // Hkv)", "return hq % Hkv"),
-    "causal_excludes_diagonal": ("return j <= i", "return j < i"),
-    "causal_transposed": ("return j <= i", "return j >= i"),
+    "causal_excludes_diagonal": ("ok = j <= i", "ok = j < i"),
+    "causal_transposed": ("ok = j <= i", "ok = j >= i"),
     "lse_without_max": ("safe_m + np.log(den)", "np.log(den)"),
     "softmax_not_normalised": ("E / den[:, None]", "E"),
     "pv_transposed": ("O = P @ v", "O = P.T @ v[: P.shape[0]]"),
@@ -37,6 +37,8 @@ MUTANTS = {
     "online_uses_old_max": ("np.exp(scores - m_new[:, None])",
                             "np.exp(scores - np.where(np.isfinite(m_old), m_old, m_new)[:, None])"),
     "online_drops_lse_max": ("m + np.log(l)", "np.log(l)"),
+    "window_off_by_one": ("ok &= j > i - window", "ok &= j >= i - window"),
+    "window_ignored": ("ok &= j > i - window", "pass"),
 }
 
 
@@ -59,6 +61,11 @@ def run_all_pins(mod):
     for causal in (False, True):
         pins.check_rows_sum_to_one(mod.ref_fwd_head, causal)
         pins.check_blockwise_equals_plain(mod.blockwise_online_fwd, mod.ref_fwd_head, causal)
+    fwd_w = lambda q, k, v, s, w: mod.ref_fwd(q, k, v, s, True, chunk=4, window=w)
+    bwd_w = lambda q, k, v, do, s, w: mod.ref_bwd(q, k, v, do, s, True, chunk=4, window=w)
+    pins.check_window_brute_force(fwd_w, 301, 1, 2, 1, 6, 3, 2)
+    pins.check_window_special_cases(fwd, fwd_w)
+    pins.check_window_gradients(fwd_w, bwd_w)
 
 
 def test_unmutated_copy_passes():

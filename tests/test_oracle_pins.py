@@ -112,3 +112,33 @@ def test_rejects_bad_grouping():
         oracle.ref_fwd(q, k, v, 1.0)
     with pytest.raises(ValueError):
         oracle.kv_head_of(0, 3, 2)
+
+
+def fwd_w(q, k, v, scale, window):
+    return oracle.ref_fwd(q, k, v, scale, True, chunk=4, window=window)
+
+
+def bwd_w(q, k, v, do, scale, window):
+    return oracle.ref_bwd(q, k, v, do, scale, True, chunk=4, window=window)
+
+
+@pytest.mark.parametrize("shape,window", [((1, 2, 1, 6, 3), 1), ((2, 4, 2, 6, 4), 2), ((1, 3, 3, 7, 2), 4)])
+def test_window_brute_force(shape, window):
+    pins.check_window_brute_force(fwd_w, 300 + window, *shape, window)
+
+
+def test_window_special_cases():
+    pins.check_window_special_cases(fwd, fwd_w)
+
+
+def test_window_blockwise_online():
+    pins.check_window_blockwise(oracle.blockwise_online_fwd, oracle.ref_fwd_head)
+
+
+def test_window_gradients():
+    pins.check_window_gradients(fwd_w, bwd_w)
+
+
+def test_window_rejects_zero():
+    with pytest.raises(ValueError):
+        oracle.allowed_mask(0, 3, 3, True, 0)
