@@ -215,10 +215,10 @@ def cpu_baseline(w, inputs, budget_s):
             k = si.to_f64(inputs["k"][b:b + 1, hk:hk + 1])
             v = si.to_f64(inputs["v"][b:b + 1, hk:hk + 1])
             t0 = time.perf_counter()
-            oracle.ref_fwd(q, k, v, w.scale, w.causal)
+            oracle.ref_fwd(q, k, v, w.scale, w.causal, window=w.window)
             if w.backward:
                 do = si.to_f64(inputs["do"][b:b + 1, h:h + 1])
-                oracle.ref_bwd(q, k, v, do, w.scale, w.causal)
+                oracle.ref_bwd(q, k, v, do, w.scale, w.causal, window=w.window)
             secs += time.perf_counter() - t0
             heads += 1
             if secs * (heads + 1) / heads > budget_s:
@@ -234,7 +234,7 @@ def cpu_baseline(w, inputs, budget_s):
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"{heads} of {w.B * w.Hq} heads of the same workload (N={w.N}, d={w.d}, "
-                   f"{'causal' if w.causal else 'no mask'}, {'fwd+bwd' if w.backward else 'fwd'}), "
+                   f"{w.mask}, {'fwd+bwd' if w.backward else 'fwd'}), "
                    f"numpy float64 with S and P materialised, {secs:.1f} s; value credits the "
                    f"same algorithmic flops per head as the GPU line"),
         "seconds": round(secs, 2),
@@ -256,7 +256,7 @@ def parity_sample(w, inputs, o, lse):
     lg = lse[b, h].double().cpu().numpy()
     eo, el = 0.0, 0.0
     for r in rows:
-        O, L = oracle.ref_fwd_head(q[r:r + 1], k, v, w.scale, w.causal, row0=int(r))
+        O, L = oracle.ref_fwd_head(q[r:r + 1], k, v, w.scale, w.causal, row0=int(r), window=w.window)
         eo = max(eo, float(np.abs(og[r] - O[0]).max()))
         el = max(el, float(abs(lg[r] - L[0])))
     return {"head": [int(b), int(h)], "rows": int(len(rows)), "o_max_abs_err": eo, "lse_max_abs_err": el}
@@ -273,7 +273,7 @@ def summarize_trace(trace_dir, bench_json, out_md, workload):
     w = si.WORKLOADS[workload]
     b = json.loads(open(bench_json).read().strip().splitlines()[-1])
     out = [f"# Kernel trace: {workload} (B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, N={w.N}, d={w.d}, "
-           f"{'causal' if w.causal else 'no mask'}, {'fwd+bwd' if w.backward else 'fwd'})", "",
+           f"{w.mask}, {'fwd+bwd' if w.backward else 'fwd'})", "",
            "Commands (repository root on the MI355X box):", "",
            f"    cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d <trace_dir> -o trace -- "
            f"python <repo>/bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
@@ -339,11 +339,11 @@ def main():
                          device="cuda")
 
     def run_fwd():
-        ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, out=o, lse=lse)
+        ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse)
 
     def run_bwd():
         ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal,
-               workspace=ws, dq=dq, dk=dk, dv=dv)
+               window=w.window, workspace=ws, dq=dq, dk=dk, dv=dv)
 
     def step():
         run_fwd()
@@ -367,7 +367,8 @@ def main():
     if w.backward:
         def bwd_pass(name):
             return lambda: ea.bwd_passes(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, ws,
-                                         scale=w.scale, causal=w.causal, passes=(name,))
+                                         scale=w.scale, causal=w.causal, window=w.window,
+                                         passes=(name,))
         rows = w.B * w.Hq * w.N
         kernels["bwd_pre_kernel"] = {"ms": time_loop(bwd_pass("pre"), args.steps, stream), "flops": 0.0,
                                      "bytes": 2 * rows * w.d * 2 + 4 * rows}
@@ -438,7 +439,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "passes": "fwd+bwd" if w.backward else "fwd",
+                   "causal": w.causal, "window": w.window,
+                   "passes": "fwd+bwd" if w.backward else "fwd",
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "passes": passes,

@@ -8,6 +8,7 @@ If the library is missing or fails to load, every call raises.
 
     o, lse = fwd(q, k, v, causal=True)              # scale defaults to 1/sqrt(d)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    o, lse = fwd(q, k, v, window=256)               # sliding window i-256 < j <= i
 """
 
 from __future__ import annotations
@@ -34,6 +35,7 @@ STATUS = {
     6: "ATTN_ERR_ALIGN",
     7: "ATTN_ERR_WORKSPACE",
     8: "ATTN_ERR_HIP",
+    9: "ATTN_ERR_WINDOW",
 }
 
 
@@ -71,13 +73,17 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_fwd_window.restype = i
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_window.restype = i
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
     L.attn_bwd_preprocess.restype = i
-    L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     L.attn_bwd_dkdv.restype = i
-    L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     L.attn_bwd_dq.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
@@ -145,12 +151,23 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-def fwd(q, k, v, *, scale=None, causal=False, out=None, lse=None):
+def _window_arg(window):
+    if window is None:
+        return None
+    window = int(window)
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    return window
+
+
+def fwd(q, k, v, *, scale=None, causal=False, window=None, out=None, lse=None):
     """Forward pass. q [B,Hq,N,d], k, v [B,Hkv,N,d] bf16 contiguous on the GPU.
 
-    Returns (o [B,Hq,N,d] bf16, lse [B,Hq,N] float32). Enqueued on the current
-    stream; no synchronisation.
+    window=W (>= 1) selects the sliding-window mask i-W < j <= i, which
+    implies the causal mask. Returns (o [B,Hq,N,d] bf16, lse [B,Hq,N] float32).
+    Enqueued on the current stream; no synchronisation.
     """
+    window = _window_arg(window)
     import torch
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     if scale is None:
@@ -167,8 +184,13 @@ def fwd(q, k, v, *, scale=None, causal=False, out=None, lse=None):
         _require(lse, "lse", torch.float32, 3)
         if tuple(lse.shape) != (B, Hq, N):
             raise ValueError("lse must be [B, Hq, N]")
-    _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device)))
+    if window is None:
+        _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device)))
+    else:
+        _check(lib().attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, Hq, Hkv, N, d, float(scale), window,
+                                     _stream_ptr(q.device)))
     return out, lse
 
 
@@ -176,9 +198,12 @@ def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
 
 
-def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, workspace=None, dq=None, dk=None, dv=None):
-    """Backward pass; returns (dq, dk, dv) bf16 like q, k, v."""
+def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, window=None, workspace=None,
+        dq=None, dk=None, dv=None):
+    """Backward pass; returns (dq, dk, dv) bf16 like q, k, v. `causal` and
+    `window` must be those of the forward call."""
     import torch
+    window = _window_arg(window)
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     _require(o, "o", torch.bfloat16, 4)
     _require(do, "do", torch.bfloat16, 4)
@@ -197,18 +222,27 @@ def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, workspace=None, dq=Non
         _require(t, name, torch.bfloat16, 4)
         if t.shape != ref.shape:
             raise ValueError(f"{name} has the wrong shape")
-    _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                          do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device)))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            B, Hq, Hkv, N, d, float(scale))
+    if window is None:
+        _check(lib().attn_bwd(*args, int(bool(causal)), _stream_ptr(q.device)))
+    else:
+        _check(lib().attn_bwd_window(*args, window, _stream_ptr(q.device)))
     return dq, dk, dv
 
 
 def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal=False,
-               passes=("pre", "dkdv", "dq")):
+               window=None, passes=("pre", "dkdv", "dq")):
     """Run selected backward passes through their own entry points (same
-    arguments and checks as bwd(); outputs must be preallocated)."""
+    arguments and checks as bwd(); outputs must be preallocated). A window
+    implies the causal mask."""
     import torch
+    window = _window_arg(window)
+    if window is not None:
+        causal = True
+    win = 0 if window is None else window
     B, Hq, Hkv, N, d = _shapes(q, k, v)
     if scale is None:
         scale = default_scale(d)
@@ -226,11 +260,11 @@ def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal
         elif p == "dkdv":
             _check(L.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                                    dk.data_ptr(), dv.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, float(scale),
-                                   int(bool(causal)), st))
+                                   int(bool(causal)), win, st))
         elif p == "dq":
             _check(L.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                                  dq.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, float(scale),
-                                 int(bool(causal)), st))
+                                 int(bool(causal)), win, st))
         else:
             raise ValueError(f"unknown backward pass {p!r}")
     return dq, dk, dv

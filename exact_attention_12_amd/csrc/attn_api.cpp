@@ -50,13 +50,18 @@ attn_status hip_status(hipError_t e) {
     return ATTN_ERR_HIP;
 }
 
-}  // namespace
+// Window as the kernels take it: 0 = no band, else W with 1 <= W < N (a band
+// of N or more keys is the plain causal mask).
+int kernel_window(int window, int N) { return window >= N ? 0 : window; }
 
-extern "C" {
+int mask_kind(int causal, int kernel_window) {
+    if (causal == 0) return attn::kMaskNone;
+    return kernel_window > 0 ? attn::kMaskWindow : attn::kMaskCausal;
+}
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream) {
+attn_status fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                       int window, void* stream) {
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
     attn_status st = check_shape(B, Hq, Hkv, N, d);
     if (st != ATTN_OK) return st;
@@ -79,9 +84,28 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     p.G = Hq / Hkv;
     p.BH = B * Hq;
     p.nqb = (N + plan.block_q - 1) / plan.block_q;
+    p.window = kernel_window(window, N);
     p.c = scale * kLog2eHost;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_fwd(p, d, causal != 0, plan, static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_fwd(p, d, mask_kind(causal, p.window), plan,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     void* stream) {
+    return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 0, stream);
+}
+
+attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int N, int d, float scale, int window,
+                            void* stream) {
+    if (window < 1) return ATTN_ERR_WINDOW;
+    return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, 1, window, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
@@ -89,6 +113,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
     const size_t bytes = (size_t)B * Hq * N * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -99,7 +125,7 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
                        const void* workspace, size_t workspace_bytes,
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                       void* stream, int passes) {
+                       int window, void* stream, int passes) {
     const bool pre = passes & attn::kBwdPre, kv = passes & attn::kBwdDkDv, qq = passes & attn::kBwdDq;
     const bool main = kv || qq;
     const void* used[] = {pre ? o : dout, dout, main ? q : dout, main ? k : dout,
@@ -112,6 +138,7 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
     if (main) {
         st = check_scale(scale);
         if (st != ATTN_OK) return st;
+        if (window < 0 || (window > 0 && causal == 0)) return ATTN_ERR_WINDOW;
     }
     if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
         return ATTN_ERR_WORKSPACE;
@@ -135,13 +162,17 @@ attn_status bwd_common(const void* q, const void* k, const void* v, const void* 
     p.Hkv = Hkv;
     p.G = Hq / Hkv;
     p.B = B;
+    p.window = kernel_window(window, N);
     p.scale = scale;
     p.c = scale * kLog2eHost;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_bwd(p, d, causal != 0, passes, static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_bwd(p, d, mask_kind(causal, p.window), passes,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
+
+extern "C" {
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout,
@@ -150,32 +181,43 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      void* stream) {
     return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
-                      d, scale, causal, stream, attn::kBwdAll);
+                      d, scale, causal, 0, stream, attn::kBwdAll);
+}
+
+attn_status attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int N, int d, float scale, int window,
+                            void* stream) {
+    if (window < 1) return ATTN_ERR_WINDOW;
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
+                      d, scale, 1, window, stream, attn::kBwdAll);
 }
 
 attn_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                                 void* stream) {
     return bwd_common(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
-                      workspace, workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, stream, attn::kBwdPre);
+                      workspace, workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, 0, stream, attn::kBwdPre);
 }
 
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dk, void* dv,
                           const void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                          void* stream) {
+                          int window, void* stream) {
     return bwd_common(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B, Hq,
-                      Hkv, N, d, scale, causal, stream, attn::kBwdDkDv);
+                      Hkv, N, d, scale, causal, window, stream, attn::kBwdDkDv);
 }
 
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                         const void* dout, void* dq,
                         const void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                        void* stream) {
+                        int window, void* stream) {
     return bwd_common(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes, B,
-                      Hq, Hkv, N, d, scale, causal, stream, attn::kBwdDq);
+                      Hq, Hkv, N, d, scale, causal, window, stream, attn::kBwdDq);
 }
 
 const char* attn_status_string(attn_status status) {
@@ -189,6 +231,7 @@ const char* attn_status_string(attn_status status) {
         case ATTN_ERR_ALIGN: return "device pointers must be 16-byte aligned";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_HIP: return "the HIP runtime refused a launch (see attn_last_hip_error)";
+        case ATTN_ERR_WINDOW: return "window must be >= 1 and needs the causal mask";
     }
     return "unknown status";
 }

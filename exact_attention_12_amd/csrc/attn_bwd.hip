@@ -61,9 +61,11 @@ void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_kernel(BwdParams p) {
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
     constexpr int NW = 4;
     constexpr int T = NW * 64;
     constexpr int BK = NW * 32;        // keys per workgroup
@@ -124,7 +126,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     const int nqb = (N + BQ - 1) / BQ;
     const int qb_start = CAUSAL ? (k0 / BQ) : 0;
-    const int nq_iter = nqb - qb_start;
+    // Sliding window: only queries i <= (last key) + window - 1 see this block.
+    const int W = WINDOW ? p.window : 0;
+    const int qb_stop = WINDOW ? min(nqb, (k0 + BK - 1 + W - 1) / BQ + 1) : nqb;
+    const int nq_iter = qb_stop - qb_start;
     const int total = p.G * nq_iter;
 
     TileIO<D, BQ, T> qio, doio;
@@ -198,11 +203,13 @@ void bwd_dkdv_kernel(BwdParams p) {
             // P = exp2(c*S - LSE2) and dS = P (dP - D), packed to bf16 in the
             // B-operand order of the dV/dK products. Under the causal mask the
             // query of register r (local offset qoff(r) + 4h) is masked for
-            // this lane's key when key - q0 - 4h > qoff(r): one compare with a
-            // constant per element.
+            // this lane's key when key - q0 - 4h > qoff(r) (one compare with a
+            // constant per element), and under a sliding window also when
+            // qoff(r) > key - q0 - 4h + W - 1.
             bf16x8 pb[PVS], dsb[PVS];
             {
                 const int kq = key - q0 - 4 * h;
+                const int kq_w = kq + W - 1;
 #pragma unroll
                 for (int u = 0; u < PVS; ++u) {
                     const int qt = u >> 1;
@@ -218,6 +225,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                             const int ql = qoff + h * 4;
                             float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
                             if (CAUSAL && kq > qoff) pe = 0.0f;
+                            if (WINDOW && qoff > kq_w) pe = 0.0f;
                             pv[w] = pe;
                             dv[w] = pe * (dp[qt][r] - Ds[ql]);
                         }
@@ -290,7 +298,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- launch
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stream) {
     if (passes & kBwdPre) {
         const long long rows = (long long)p.B * p.Hq * p.N;
@@ -302,29 +310,34 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
     }
     if (passes & kBwdDkDv) {
         const long long nkb = (p.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * p.B * p.Hkv)), dim3(256),
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK>), dim3((unsigned)(nkb * p.B * p.Hkv)), dim3(256),
                            0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (passes & kBwdDq) {
-        const hipError_t e = launch_bwd_dq(p, D, CAUSAL, stream);
+        const hipError_t e = launch_bwd_dq(p, D, MASK, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdParams& p, bool causal, int passes, hipStream_t stream) {
-    return causal ? launch_bwd_dc<D, true>(p, passes, stream) : launch_bwd_dc<D, false>(p, passes, stream);
+static hipError_t launch_bwd_d(const BwdParams& p, int mask, int passes, hipStream_t stream) {
+    switch (mask) {
+        case kMaskNone: return launch_bwd_dc<D, kMaskNone>(p, passes, stream);
+        case kMaskCausal: return launch_bwd_dc<D, kMaskCausal>(p, passes, stream);
+        case kMaskWindow: return launch_bwd_dc<D, kMaskWindow>(p, passes, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, int passes, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int d, int mask, int passes, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_bwd_d<64>(p, causal, passes, stream);
-        case 80: return launch_bwd_d<80>(p, causal, passes, stream);
-        case 128: return launch_bwd_d<128>(p, causal, passes, stream);
-        case 256: return launch_bwd_d<256>(p, causal, passes, stream);
+        case 64: return launch_bwd_d<64>(p, mask, passes, stream);
+        case 80: return launch_bwd_d<80>(p, mask, passes, stream);
+        case 128: return launch_bwd_d<128>(p, mask, passes, stream);
+        case 256: return launch_bwd_d<256>(p, mask, passes, stream);
         default: return hipErrorInvalidValue;
     }
 }

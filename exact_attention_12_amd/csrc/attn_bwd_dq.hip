@@ -15,9 +15,11 @@ namespace attn {
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
 void bwd_dq_kernel(BwdParams p) {
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
     constexpr int NW = 4;
     constexpr int T = NW * 64;
     constexpr int BQ = NW * 32;
@@ -77,12 +79,15 @@ void bwd_dq_kernel(BwdParams p) {
 
     const int nkb = (N + BC - 1) / BC;
     const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
+    // Sliding window: keys before the first row's band are skipped.
+    const int W = WINDOW ? p.window : 0;
+    const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
 
     TileIO<D, BC, T> kio, vio;
-    kio.load(Kh, 0, N, tid);
-    vio.load(Vh, 0, N, tid);
-    kio.store_sw(smem, KP, tid);
-    vio.store(smem + BC * KP, VP, tid);
+    kio.load(Kh, kb_begin * BC, N, tid);
+    vio.load(Vh, kb_begin * BC, N, tid);
+    kio.store_sw(smem + (kb_begin & 1) * BUF, KP, tid);
+    vio.store(smem + (kb_begin & 1) * BUF + BC * KP, VP, tid);
     __syncthreads();
 
     f32x16 dqacc[NDT];
@@ -94,7 +99,7 @@ void bwd_dq_kernel(BwdParams p) {
     const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
 
-    for (int kb = 0; kb < kb_end; ++kb) {
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
         const int bufi = kb & 1;
         const bool has_next = kb + 1 < kb_end;
         if (has_next) {
@@ -120,12 +125,14 @@ void bwd_dq_kernel(BwdParams p) {
             }
             // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to bf16
             // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
-            // is masked when it is >= N or (causal) > qrow: one compare with a
-            // constant per element, skipped when the block needs no mask.
+            // is masked when it is >= N, (causal) > qrow or (sliding window)
+            // < qrow - W + 1: compares with a constant per element, skipped
+            // when the block needs no mask.
             bf16x8 dsb[PVS];
             {
                 const bool MASKED = CAUSAL || (kv0 + BC > N);
                 const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
+                const int lo = qrow - W + 1 - kv0 - 4 * h;
 #pragma unroll
                 for (int u = 0; u < PVS; ++u) {
                     const int kt = u >> 1;
@@ -140,6 +147,7 @@ void bwd_dq_kernel(BwdParams p) {
                             const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
                             float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
                             if (MASKED && koff > lim) pe = 0.0f;
+                            if (WINDOW && koff < lo) pe = 0.0f;
                             dv[w] = pe * (dp[kt][r] - del);
                         }
                         dd[e2] = to_bf16x2(dv[0], dv[1]);
@@ -179,19 +187,29 @@ void bwd_dq_kernel(BwdParams p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
     const long long nqb = (p.N + 127) / 128;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+template <int D>
+static hipError_t launch_dq_d(const BwdParams& p, int mask, hipStream_t stream) {
+    switch (mask) {
+        case kMaskNone: return launch_dq_dc<D, kMaskNone>(p, stream);
+        case kMaskCausal: return launch_dq_dc<D, kMaskCausal>(p, stream);
+        case kMaskWindow: return launch_dq_dc<D, kMaskWindow>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int d, int mask, hipStream_t stream) {
     switch (d) {
-        case 64: return causal ? launch_dq_dc<64, true>(p, stream) : launch_dq_dc<64, false>(p, stream);
-        case 80: return causal ? launch_dq_dc<80, true>(p, stream) : launch_dq_dc<80, false>(p, stream);
-        case 128: return causal ? launch_dq_dc<128, true>(p, stream) : launch_dq_dc<128, false>(p, stream);
-        case 256: return causal ? launch_dq_dc<256, true>(p, stream) : launch_dq_dc<256, false>(p, stream);
+        case 64: return launch_dq_d<64>(p, mask, stream);
+        case 80: return launch_dq_d<80>(p, mask, stream);
+        case 128: return launch_dq_d<128>(p, mask, stream);
+        case 256: return launch_dq_d<256>(p, mask, stream);
         default: return hipErrorInvalidValue;
     }
 }

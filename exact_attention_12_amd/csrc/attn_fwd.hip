@@ -45,11 +45,13 @@
 
 namespace attn {
 
-template <int D, bool CAUSAL, int NW>
+template <int D, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, (D <= 128 ? 2 : 1))
 void fwd_kernel(FwdParams p) {
     constexpr int T = NW * 64;
     constexpr int BQ = NW * 32;
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
     constexpr int BC = FwdTile<D>::BLOCK_KV;
     constexpr int KS = D / 16;            // contraction steps of S^T = K Q^T
     constexpr int NDT = (D + 31) / 32;    // 32-row tiles of O^T
@@ -113,6 +115,9 @@ void fwd_kernel(FwdParams p) {
 
     const int nkb = (N + BC - 1) / BC;
     const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
+    // Sliding window: keys before the workgroup's first row's band are skipped.
+    const int W = WINDOW ? p.window : 0;
+    const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
 
     uint4 kreg[NCH], vreg[NCH];
     auto load_tile = [&](int kv0) {
@@ -148,8 +153,8 @@ void fwd_kernel(FwdParams p) {
         }
     };
 
-    load_tile(0);
-    store_tile(0);
+    load_tile(kb_begin * BC);
+    store_tile(kb_begin & 1);
     __syncthreads();
 
     f32x16 oacc[NDT];
@@ -165,7 +170,7 @@ void fwd_kernel(FwdParams p) {
     const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
 
-    for (int kb = 0; kb < kb_end; ++kb) {
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
         const int bufi = kb & 1;
         const bool has_next = kb + 1 < kb_end;
         if (has_next) load_tile((kb + 1) * BC);
@@ -173,7 +178,7 @@ void fwd_kernel(FwdParams p) {
         const int kv0 = kb * BC;
         const bf16* Ks = smem + bufi * BUF;
         const bf16* Vs = Ks + BC * KP;
-        const bool active = !CAUSAL || kv0 <= qw0 + 31;
+        const bool active = !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
         if (active) {
             f32x16 s[NKT];
 #pragma unroll
@@ -183,15 +188,20 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32(lds_read8(kp + ks * 16), qf[ks], s[kt]);
             }
-            const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N);
+            // Keys outside [lo, hi] (relative to kv0 + 4h) are masked: the
+            // tail beyond N, keys after the row (causal) and keys before its
+            // band (sliding window).
+            const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N) ||
+                                   (WINDOW && kv0 < qw0 + 32 - W);
             if (need_mask) {
+                const int hi = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
+                const int lo = (WINDOW ? qrow - W + 1 : 0) - kv0 - 4 * h;
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + kt * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        const bool masked = (key >= N) || (CAUSAL && key > qrow);
-                        s[kt][r] = masked ? -__builtin_huge_valf() : s[kt][r];
+                        const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
+                        s[kt][r] = (koff > hi || koff < lo) ? -__builtin_huge_valf() : s[kt][r];
                     }
             }
             float mx = s[0][0];
@@ -199,20 +209,24 @@ void fwd_kernel(FwdParams p) {
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            // Lazy rescaling (see fwd_kernel_r64): the reference maximum m only
-            // moves, and O, l are rescaled, when a row's block maximum exceeds
-            // it by more than 2^8; the first block just adopts its maximum.
+            // Lazy rescaling: the reference maximum m only moves, and O, l are
+            // rescaled, when a row's block maximum exceeds it by more than 2^8;
+            // the first block with an allowed key just adopts its maximum.
             const float mb = max_across_halves(mx) * c;
             if (m == -__builtin_huge_valf()) m = mb;
             if (__any(mb > m + 8.0f)) {
                 const float m_new = fmaxf(m, mb);
-                const float alpha = fast_exp2(m - m_new);
+                // (a lane still without an allowed key keeps m = -inf, alpha 1)
+                const float alpha = (m_new == -__builtin_huge_valf()) ? 1.0f : fast_exp2(m - m_new);
                 m = m_new;
                 l *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
             }
-            const float m_new = m;
+            // A row that has not met an allowed key yet (possible only under a
+            // sliding window) still has m = -inf: use 0 so masked scores give
+            // exp2(-inf) = 0 rather than NaN.
+            const float m_new = (m == -__builtin_huge_valf()) ? 0.0f : m;
 
             bf16x8 pb[PVS];
             float lsum = 0.0f;
@@ -264,292 +278,28 @@ void fwd_kernel(FwdParams p) {
     }
 }
 
-// Long-sequence variant: 64 query rows per wave (two 32-row tiles), 4 waves
-// = 256 rows per workgroup, one workgroup per CU. Each K fragment read from
-// LDS feeds two S^T products and each V^T fragment two O^T products, which
-// halves the LDS bytes per matrix flop relative to fwd_kernel (on gfx950 the
-// LDS read rate, not the matrix core, is what bounds the 32-row kernel). The
-// O^T accumulators live in AGPRs (mfma32_agpr) so that Q, S and P fit in
-// VGPRs.
-//
-// Rescaling is lazy: each row keeps the maximum m it last rescaled to and
-// only raises it (and rescales O and l) when the block maximum exceeds it by
-// more than 2^8 in the exp2 domain. Probabilities are then at most 2^8, and
-// O and l share the same reference maximum, so the final O / l and
-// LSE = (m + log2 l) ln 2 are the same exact quantities the per-block
-// rescaling of the online-softmax pseudocode produces. The loop body has no
-// other data-dependent branch: masks are a compare and a select per element.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1)
-void fwd_kernel_r64(FwdParams p) {
-    constexpr int NW = 4;
-    constexpr int T = NW * 64;
-    constexpr int RW = 64;
-    constexpr int BQ = NW * RW;
-    constexpr int BC = 64;
-    constexpr int KS = D / 16;
-    constexpr int NDT = (D + 31) / 32;
-    constexpr int NKT = BC / 32;
-    constexpr int PVS = BC / 16;
-    constexpr int KP = k_pitch(D);
-    constexpr int VP = v_pitch(D);
-    constexpr int CPR = D / 8;
-    constexpr int CHUNKS = BC * CPR;
-    constexpr int NCH = (CHUNKS + T - 1) / T;
-    constexpr int BUF = BC * (KP + VP);
-    constexpr float kRescaleSlack = 8.0f;
-
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int h = lane >> 5;
-    const int N = p.N;
-
-    const int bid = blockIdx.x;
-    const int bh = bid % p.BH;
-    const int qb = CAUSAL ? (p.nqb - 1 - bid / p.BH) : (bid / p.BH);
-    const int b = bh / p.Hq;
-    const int hq = bh - b * p.Hq;
-    const int hkv = hq / p.G;
-
-    const bf16* Qh = static_cast<const bf16*>(p.q) + (size_t)bh * N * D;
-    const bf16* Kh = static_cast<const bf16*>(p.k) + (size_t)(b * p.Hkv + hkv) * N * D;
-    const bf16* Vh = static_cast<const bf16*>(p.v) + (size_t)(b * p.Hkv + hkv) * N * D;
-
-    const int q0 = qb * BQ;
-    const int qw0 = q0 + wave * RW;
-
-    if constexpr (NDT * 32 > D) {
-        constexpr int PADC = NDT * 32 - D;
-        for (int i = tid; i < 2 * BC * PADC; i += T) {
-            const int row = i / PADC;
-            const int bufi = row / BC;
-            smem[bufi * BUF + BC * KP + (row % BC) * VP + D + i % PADC] = (bf16)0.0f;
-        }
-    }
-
-    bf16x8 qf[2][KS];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int qrow = qw0 + qt * 32 + l32;
-        const bf16* qp = Qh + (size_t)qrow * D + h * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[qt][ks] = (qrow < N) ? *reinterpret_cast<const bf16x8*>(qp + ks * 16) : bf16x8{};
-    }
-
-    const int nkb = (N + BC - 1) / BC;
-    const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
-
-    uint4 kreg[NCH], vreg[NCH];
-    auto load_tile = [&](int kv0) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * T;
-            if (CHUNKS % T == 0 || c < CHUNKS) {
-                const int row = c / CPR;
-                const int col = c - row * CPR;
-                const int key = kv0 + row;
-                kreg[i] = key < N ? *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + col * 8) : zero4();
-                vreg[i] = key < N ? *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + col * 8) : zero4();
-            }
-        }
-    };
-    auto store_tile = [&](int bufi) {
-        bf16* Ks = smem + bufi * BUF;
-        bf16* Vs = Ks + BC * KP;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * T;
-            if (CHUNKS % T == 0 || c < CHUNKS) {
-                const int row = c / CPR;
-                const int col = c - row * CPR;
-                *reinterpret_cast<uint4*>(Ks + row * KP + col * 8) = kreg[i];
-                *reinterpret_cast<uint4*>(Vs + row * VP + col * 8) = vreg[i];
-            }
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    f32x16 oacc[2][NDT];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[qt][dt] = f32x16{};
-    float m[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};
-    float l[2] = {0.0f, 0.0f};
-    const float c = p.c;
-    const int g16 = lane >> 4;
-    const int j16 = lane & 15;
-    const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
-    const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
-
-    for (int kb = 0; kb < kb_end; ++kb) {
-        const int bufi = kb & 1;
-        const bool has_next = kb + 1 < kb_end;
-        if (has_next) load_tile((kb + 1) * BC);
-        const int kv0 = kb * BC;
-        const bf16* Ks = smem + bufi * BUF;
-        const bf16* Vs = Ks + BC * KP;
-
-        f32x16 s[2][NKT];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) s[qt][kt] = f32x16{};
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-            const bf16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = lds_read8(kp + ks * 16);
-                s[0][kt] = mfma32(a, qf[0][ks], s[0][kt]);
-                s[1][kt] = mfma32(a, qf[1][ks], s[1][kt]);
-            }
-        }
-
-        // Mask: key kv0 + koff(r) + 4h is out when it is >= N or (causal)
-        // after the row.
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int qrow = qw0 + qt * 32 + l32;
-            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
-                    s[qt][kt][r] = (koff > lim) ? -__builtin_huge_valf() : s[qt][kt][r];
-                }
-        }
-
-        float mb[2];
-        bool grow = false;
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            float mx = s[qt][0][0];
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][kt][r]);
-            mb[qt] = max_across_halves(mx) * c;
-            // First block: adopt its maximum (O and l are still zero).
-            if (m[qt] == -__builtin_huge_valf()) m[qt] = mb[qt];
-            grow |= mb[qt] > m[qt] + kRescaleSlack;
-        }
-        if (__any(grow)) {
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const float m_new = fmaxf(m[qt], mb[qt]);
-                const float alpha = fast_exp2(m[qt] - m_new);
-                m[qt] = m_new;
-                l[qt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    agpr_acc_ready(oacc[qt][dt]);
-                    oacc[qt][dt] *= alpha;
-                }
-            }
-        }
-
-        bf16x8 pb[2][PVS];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            float lsum = 0.0f;
-#pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-                const int kt = u >> 1;
-                const int r0 = (u & 1) * 8;
-                bf16x2 pr[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a0 = fast_exp2(fmaf(s[qt][kt][r0 + 2 * e], c, -m[qt]));
-                    const float a1 = fast_exp2(fmaf(s[qt][kt][r0 + 2 * e + 1], c, -m[qt]));
-                    pr[e] = to_bf16x2(a0, a1);
-                    lsum += a0 + a1;
-                }
-                pb[qt][u] = cat8(pr[0], pr[1], pr[2], pr[3]);
-            }
-            l[qt] += lsum;
-        }
-
-#pragma unroll
-        for (int u = 0; u < PVS; ++u) {
-            const bf16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x8 a = join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32));
-                mfma32_agpr(oacc[0][dt], a, pb[0][u]);
-                mfma32_agpr(oacc[1][dt], a, pb[1][u]);
-            }
-        }
-        if (has_next) store_tile(bufi ^ 1);
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) agpr_acc_ready(oacc[qt][dt]);
-        const int qrow = qw0 + qt * 32 + l32;
-        const float lt = sum_across_halves(l[qt]);
-        const float inv = 1.0f / lt;
-        if (qrow < N) {
-            bf16* orow = static_cast<bf16*>(p.o) + ((size_t)bh * N + qrow) * D;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int d = dt * 32 + g4 * 8 + h * 4;
-                    if (d < D)
-                        store_bf16x4(orow + d, oacc[qt][dt][g4 * 4 + 0] * inv, oacc[qt][dt][g4 * 4 + 1] * inv,
-                                     oacc[qt][dt][g4 * 4 + 2] * inv, oacc[qt][dt][g4 * 4 + 3] * inv);
-                }
-            if (h == 0) p.lse[(size_t)bh * N + qrow] = (m[qt] + log2f(lt)) * kLn2;
-        }
-    }
-}
-
-
-template <int D>
-static hipError_t launch_fwd_d(const FwdParams& p, bool causal, const FwdPlan& plan, hipStream_t stream) {
+template <int D, int MASK>
+static hipError_t launch_fwd_dm(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
     const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
     if constexpr (D <= 128) {
-        if (plan.rows_per_wave == 64) {
-            if (causal)
-                hipLaunchKernelGGL((fwd_kernel_r64<D, true>), grid, block, 0, stream, p);
-            else
-                hipLaunchKernelGGL((fwd_kernel_r64<D, false>), grid, block, 0, stream, p);
-            return hipGetLastError();
-        }
         if (plan.waves == 8) {
-            if (causal)
-                hipLaunchKernelGGL((fwd_kernel<D, true, 8>), grid, block, 0, stream, p);
-            else
-                hipLaunchKernelGGL((fwd_kernel<D, false, 8>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_kernel<D, MASK, 8>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
     }
-    if (causal)
-        hipLaunchKernelGGL((fwd_kernel<D, true, 4>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((fwd_kernel<D, false, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, MASK, 4>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-// The 64-row kernel is used when it yields at least this many workgroups.
-// Measured on MI355X it is still slower than the 32-row kernel at every
-// listed shape (one wave per SIMD exposes the LDS latency of the S^T phase),
-// so by default it is not selected.
-#ifndef ATTN_FWD_R64_MIN_WORKGROUPS
-#define ATTN_FWD_R64_MIN_WORKGROUPS 0x7fffffffffffLL
-#endif
+template <int D>
+static hipError_t launch_fwd_d(const FwdParams& p, int mask, const FwdPlan& plan, hipStream_t stream) {
+    switch (mask) {
+        case kMaskNone: return launch_fwd_dm<D, kMaskNone>(p, plan, stream);
+        case kMaskCausal: return launch_fwd_dm<D, kMaskCausal>(p, plan, stream);
+        case kMaskWindow: return launch_fwd_dm<D, kMaskWindow>(p, plan, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 // Tile plan. 8 waves (256 rows) per workgroup share one K/V pipeline, which
 // halves global-load issue and LDS stores per row; used while that still
@@ -558,11 +308,10 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, const FwdPlan& p
 template <int D>
 static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
     const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
-    const bool r64 = D <= 128 && wg256 >= ATTN_FWD_R64_MIN_WORKGROUPS;
-    const int waves = (r64 || (D <= 128 && wg256 >= 256)) ? (r64 ? 4 : 8) : 4;
-    const int BQ = r64 ? 256 : waves * 32;
-    const int BC = r64 ? 64 : FwdTile<D>::BLOCK_KV;
-    plan->rows_per_wave = r64 ? 64 : 32;
+    const int waves = (D <= 128 && wg256 >= 256) ? 8 : 4;
+    const int BQ = waves * 32;
+    const int BC = FwdTile<D>::BLOCK_KV;
+    plan->rows_per_wave = 32;
     plan->waves = waves;
     plan->block_q = BQ;
     plan->block_kv = BC;
@@ -581,12 +330,12 @@ bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan) {
     }
 }
 
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, const FwdPlan& plan, hipStream_t stream) {
+hipError_t launch_fwd(const FwdParams& p, int d, int mask, const FwdPlan& plan, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_fwd_d<64>(p, causal, plan, stream);
-        case 80: return launch_fwd_d<80>(p, causal, plan, stream);
-        case 128: return launch_fwd_d<128>(p, causal, plan, stream);
-        case 256: return launch_fwd_d<256>(p, causal, plan, stream);
+        case 64: return launch_fwd_d<64>(p, mask, plan, stream);
+        case 80: return launch_fwd_d<80>(p, mask, plan, stream);
+        case 128: return launch_fwd_d<128>(p, mask, plan, stream);
+        case 256: return launch_fwd_d<256>(p, mask, plan, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -45,6 +45,10 @@ __host__ __device__ constexpr int sw_off(int row, int col, int pitch) {
     return row * pitch + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
 }
 
+// Mask modes, one kernel instantiation each: none, causal (keys j <= i) and
+// the causal sliding window (keys i - window < j <= i).
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -57,6 +61,7 @@ struct FwdParams {
     int G;        // Hq / Hkv
     int BH;       // B * Hq
     int nqb;      // query blocks per head
+    int window;   // causal band width in keys (query i sees i-window < j <= i); 0 = none
     float c;      // scale * log2(e)
 };
 
@@ -76,12 +81,13 @@ struct BwdParams {
     int Hkv;
     int G;
     int B;
+    int window;    // causal band width in keys; 0 = none
     float scale;
     float c;       // scale * log2(e)
 };
 
 struct FwdPlan {
-    int rows_per_wave;  // 32 (fwd_kernel) or 64 (fwd_kernel_r64)
+    int rows_per_wave;  // query rows per wave (32)
     int waves;          // waves per workgroup
     int block_q;
     int block_kv;
@@ -93,11 +99,11 @@ struct FwdPlan {
 bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan);
 
 // Launchers return the hipError_t of the launch.
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, const FwdPlan& plan,
+hipError_t launch_fwd(const FwdParams& p, int d, int mask, const FwdPlan& plan,
                       hipStream_t stream);
 // Backward passes: bit 0 = row-term preprocess, bit 1 = dK/dV, bit 2 = dQ.
 enum BwdPass { kBwdPre = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7 };
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, int passes, hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, int mask, int passes, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, int mask, hipStream_t stream);
 
 }  // namespace attn

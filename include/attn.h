@@ -34,6 +34,11 @@
  *   GQA: Hq must be a multiple of Hkv; query head h uses KV head
  *     h / (Hq / Hkv) (consecutive groups). Hkv == Hq is MHA, Hkv == 1 is MQA.
  *   Causal (causal != 0): query i attends to keys j <= i; otherwise to all j.
+ *   Sliding window (window = W >= 1, the *_window entry points and the
+ *     window argument of the pass entry points): query i attends to the W
+ *     most recent keys i - W < j <= i, a band inside the causal mask ("FlashAttention in CANN
+ *     ops-transformer on the Ascend NPU", tuning section on mask modes).
+ *     W >= N allows every key j <= i and so equals the causal mask.
  *   Scale: the factor applied to Q K^T before the softmax, finite and > 0
  *     (callers usually pass 1/sqrt(d)).
  *   Memory: every pointer is a device pointer owned by the caller; the
@@ -66,7 +71,8 @@ typedef enum attn_status {
     ATTN_ERR_SCALE = 5,      /* scale is not finite or not > 0 */
     ATTN_ERR_ALIGN = 6,      /* a pointer is not 16-byte aligned */
     ATTN_ERR_WORKSPACE = 7,  /* workspace NULL or smaller than required */
-    ATTN_ERR_HIP = 8         /* the HIP runtime refused a launch */
+    ATTN_ERR_HIP = 8,        /* the HIP runtime refused a launch */
+    ATTN_ERR_WINDOW = 9      /* window < 0, or a window (>= 1) without the causal mask */
 } attn_status;
 
 /* Head dimensions with a specialised kernel. */
@@ -86,6 +92,15 @@ typedef enum attn_status {
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      void* stream);
+
+/*
+ * Forward pass under the sliding-window mask of W = window keys (query i
+ * attends to keys i - W < j <= i). Arguments otherwise as for attn_fwd; lse
+ * is the log-sum-exp over the row's band. window < 1 is ATTN_ERR_WINDOW.
+ */
+attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int N, int d, float scale, int window,
+                            void* stream);
 
 /*
  * Bytes of device workspace attn_bwd needs: one float32 per query row for the
@@ -113,10 +128,24 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* stream);
 
 /*
+ * Backward pass of attn_fwd_window: the gradients of the banded attention,
+ * for a forward call with the same arguments. Arguments otherwise as for
+ * attn_bwd (same workspace size). window < 1 is ATTN_ERR_WINDOW.
+ */
+attn_status attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int N, int d, float scale, int window,
+                            void* stream);
+
+/*
  * The three passes attn_bwd runs, in order, for callers that schedule them
  * separately (for example the dK/dV and dQ passes on two streams after the
  * preprocess, or to time each pass). Arguments mean exactly what they mean
  * for attn_bwd; each validates them the same way and enqueues one kernel.
+ * window: 0 for the mask `causal` selects, or W >= 1 (with causal != 0) for
+ * the sliding window of attn_bwd_window.
  *   attn_bwd_preprocess: workspace <- D_i = <dout_i, o_i> per query row.
  *   attn_bwd_dkdv: dk, dv from q, k, v, lse, dout and the workspace.
  *   attn_bwd_dq:   dq from q, k, v, lse, dout and the workspace.
@@ -130,12 +159,12 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const flo
                           const void* dout, void* dk, void* dv,
                           const void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                          void* stream);
+                          int window, void* stream);
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                         const void* dout, void* dq,
                         const void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                        void* stream);
+                        int window, void* stream);
 
 /* Static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);
@@ -147,8 +176,8 @@ const char* attn_status_string(attn_status status);
 const char* attn_last_hip_error(void);
 
 /*
- * Tile plan of the forward kernel for a shape: query rows per wave (32 or
- * 64), rows of Q per workgroup, keys per inner step, threads per workgroup,
+ * Tile plan of the forward kernel for a shape: query rows per wave, rows
+ * of Q per workgroup, keys per inner step, threads per workgroup,
  * number of workgroups and bytes of LDS per workgroup. Host-only arithmetic
  * (no device call). Returns ATTN_OK or the validation error for that shape.
  */

@@ -29,6 +29,7 @@ class Workload:
     backward: bool
     seed: int
     note: str = field(default="", compare=False)
+    window: int | None = None  # sliding window W (keys i-W < j <= i); implies causal
 
     @property
     def scale(self) -> float:
@@ -40,8 +41,18 @@ class Workload:
         return self.Hq // self.Hkv
 
     def pairs(self) -> int:
-        """(query, key) pairs per (b, hq): N^2, or N(N+1)/2 under the causal mask."""
+        """(query, key) pairs per (b, hq): N^2, N(N+1)/2 under the causal mask,
+        and sum_i min(i+1, W) under a sliding window of W keys."""
+        if self.window is not None and self.window < self.N:
+            W = self.window
+            return W * (W + 1) // 2 + (self.N - W) * W
         return self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+
+    @property
+    def mask(self) -> str:
+        if self.window is not None:
+            return f"sliding window W={self.window}"
+        return "causal" if self.causal else "no mask"
 
     def fwd_flops(self) -> float:
         """Algorithmic forward flops: two matmuls of 2*d flops per allowed pair."""
@@ -65,8 +76,8 @@ class Workload:
         return 3 * q + 2 * kv + rows + (q + 2 * kv) + 3 * rows
 
 
-def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note=""):
-    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note)
+def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note="", window=None):
+    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window)
 
 
 # The five workload families (index k gives seed 1000 + k; the sequence sweep
@@ -88,6 +99,10 @@ WORKLOADS = {
         _w("c4_mqa_70b", 1, 64, 1, 8192, 128, True, False, 1004, "MQA, G=64"),
         _w("c5_bwd_d128", 1, 16, 16, 16384, 128, True, True, 1005, "fwd+bwd"),
         _w("c5_bwd_d80", 1, 16, 16, 4096, 80, True, True, 1005, "fwd+bwd, d=80"),
+        # Long-text case for the sliding-window mask (CANN FlashAttention page,
+        # mask modes): 16K tokens, a 4096-key band, GQA G=4, fwd+bwd.
+        _w("c6_window_d128", 1, 32, 8, 16384, 128, True, True, 1006,
+           "fwd+bwd, sliding window 4096, GQA G=4", window=4096),
     ]
 }
 

@@ -33,9 +33,9 @@ def rel_l2(g, r):
     return float(np.linalg.norm(g - r)) / den
 
 
-def check_fwd(inputs_cpu, o_gpu, lse_gpu, scale, causal, heads, tag=""):
+def check_fwd(inputs_cpu, o_gpu, lse_gpu, scale, causal, heads, tag="", window=None):
     q, k, v = (si.to_f64(inputs_cpu[x]) for x in ("q", "k", "v"))
-    O, L = oracle.ref_fwd(q, k, v, scale, causal, heads=heads)
+    O, L = oracle.ref_fwd(q, k, v, scale, causal, heads=heads, window=window)
     og = si.to_f64(o_gpu)
     lg = lse_gpu.detach().cpu().double().numpy()
     worst_o, worst_l = 0.0, 0.0
@@ -55,9 +55,9 @@ def check_fwd(inputs_cpu, o_gpu, lse_gpu, scale, causal, heads, tag=""):
     return worst_o, worst_l
 
 
-def check_bwd(inputs_cpu, grads_gpu, scale, causal, kv_heads, Hq, Hkv, tag=""):
+def check_bwd(inputs_cpu, grads_gpu, scale, causal, kv_heads, Hq, Hkv, tag="", window=None):
     q, k, v, do = (si.to_f64(inputs_cpu[x]) for x in ("q", "k", "v", "do"))
-    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, scale, causal, kv_heads=kv_heads)
+    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, scale, causal, kv_heads=kv_heads, window=window)
     G = Hq // Hkv
     gq, gk, gv = (si.to_f64(t) for t in grads_gpu)
     errs = {}

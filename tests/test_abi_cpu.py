@@ -33,13 +33,14 @@ def bwd(L, ws=P, ws_bytes=1 << 20, ptrs=None, B=1, Hq=2, Hkv=1, N=8, d=64, scale
 def test_exports_every_declared_function(L):
     names = ea.header_functions()
     assert set(names) >= {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
-                          "attn_last_hip_error", "attn_fwd_plan"}
+                          "attn_last_hip_error", "attn_fwd_plan", "attn_fwd_window",
+                          "attn_bwd_window", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings(L):
-    for code in range(9):
+    for code in range(10):
         s = ea.status_string(code)
         assert s and s != "unknown status"
     assert ea.status_string(99) == "unknown status"
@@ -136,15 +137,37 @@ def test_pass_entry_points_validate(L):
     for i in range(7):
         a = [P] * 7
         a[i] = None
-        assert L.attn_bwd_dkdv(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, None) == 1
+        assert L.attn_bwd_dkdv(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, 0, None) == 1
         a[i] = P + 8
-        assert L.attn_bwd_dkdv(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, None) == 6
-    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 2, 1, 8, 64, -1.0, 1, None) == 5
-    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 3, 2, 8, 64, 0.125, 1, None) == 3
+        assert L.attn_bwd_dkdv(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, 0, None) == 6
+    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 2, 1, 8, 64, -1.0, 1, 0, None) == 5
+    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 3, 2, 8, 64, 0.125, 1, 0, None) == 3
     # dQ pass: q, k, v, lse, dout, dq, workspace
     for i in range(6):
         a = [P] * 6
         a[i] = None
-        assert L.attn_bwd_dq(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 0, None) == 1
-    assert L.attn_bwd_dq(*[P] * 6, None, wsb, 1, 2, 1, 8, 64, 0.125, 0, None) == 7
-    assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 0, 64, 0.125, 0, None) == 2
+        assert L.attn_bwd_dq(*a, ws, wsb, 1, 2, 1, 8, 64, 0.125, 0, 0, None) == 1
+    assert L.attn_bwd_dq(*[P] * 6, None, wsb, 1, 2, 1, 8, 64, 0.125, 0, 0, None) == 7
+    assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 0, 64, 0.125, 0, 0, None) == 2
+
+
+def test_window_validation(L):
+    """The sliding-window mask needs W >= 1 and implies the causal mask (CANN
+    FlashAttention page, tuning section on mask modes)."""
+    for w in (0, -1, -(1 << 30)):
+        assert L.attn_fwd_window(*[P] * 5, 1, 2, 1, 8, 64, 0.125, w, None) == 9
+        assert L.attn_bwd_window(*[P] * 10, 1 << 20, 1, 2, 1, 8, 64, 0.125, w, None) == 9
+    # the window is checked before anything else in the window entry points
+    assert L.attn_fwd_window(None, *[P] * 4, 1, 2, 1, 8, 64, 0.125, 0, None) == 9
+    # valid windows still get the ordinary checks
+    assert L.attn_fwd_window(None, *[P] * 4, 1, 2, 1, 8, 64, 0.125, 3, None) == 1
+    assert L.attn_fwd_window(*[P] * 5, 1, 2, 1, 8, 96, 0.125, 3, None) == 4
+    assert L.attn_fwd_window(*[P] * 4, P + 2, 1, 2, 1, 8, 64, 0.125, 1 << 30, None) == 6
+    assert L.attn_bwd_window(*[P] * 10, 16, 1, 2, 1, 8, 64, 0.125, 4, None) == 7
+    assert L.attn_bwd_window(*[P] * 10, 1 << 20, 1, 2, 1, 8, 64, float("inf"), 4, None) == 5
+    # pass entry points: window >= 1 needs causal, negative windows are refused
+    ws, wsb = P, 1 << 20
+    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 2, 1, 8, 64, 0.125, 0, 4, None) == 9
+    assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, -1, None) == 9
+    assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 8, 64, 0.125, 0, 2, None) == 9
+    assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, -3, None) == 9

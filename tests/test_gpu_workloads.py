@@ -21,10 +21,12 @@ FWD_HEADS = {
     "c4_mqa_70b": [(0, 0), (0, 63)],
     "c5_bwd_d128": [(0, 0), (0, 15)],
     "c5_bwd_d80": [(0, 0), (0, 5), (0, 15)],
+    "c6_window_d128": [(0, 0), (0, 31)],
 }
 BWD_KV_HEADS = {
     "c5_bwd_d128": [(0, 3)],
     "c5_bwd_d80": [(0, 0), (0, 15)],
+    "c6_window_d128": [(0, 5)],
 }
 
 
@@ -38,17 +40,19 @@ def _gpu():
 @pytest.mark.parametrize("name", list(FWD_HEADS))
 def test_workload(name):
     w = si.WORKLOADS[name]
-    parity.log(f"workload {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} causal={w.causal}")
+    parity.log(f"workload {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.mask}")
     inp = si.workload_inputs(w)
     g = parity.to_gpu(inp)
-    o, lse = ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window)
     torch.cuda.synchronize()
     heads = FWD_HEADS[name] or [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    parity.check_fwd(inp, o, lse, w.scale, w.causal, heads, name)
+    parity.check_fwd(inp, o, lse, w.scale, w.causal, heads, name, window=w.window)
     if w.backward:
-        grads = ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal)
+        grads = ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal,
+                       window=w.window)
         torch.cuda.synchronize()
-        parity.check_bwd(inp, grads, w.scale, w.causal, BWD_KV_HEADS[name], w.Hq, w.Hkv, name)
+        parity.check_bwd(inp, grads, w.scale, w.causal, BWD_KV_HEADS[name], w.Hq, w.Hkv, name,
+                         window=w.window)
         # Identities that hold for every head: rows of P sum to one, so the
         # key-sum of dV equals the query-sum of dO over each group; shifting
         # all keys leaves O unchanged, so the key-sum of dK vanishes.

@@ -4,8 +4,10 @@ import json
 import math
 import os
 
+import pytest
 import torch
 
+import oracle
 import synthetic_inputs as si
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")))
@@ -51,3 +53,11 @@ def test_inputs_are_seeded_bf16_and_ordered():
     g = torch.Generator().manual_seed(7)
     q = torch.randn((1, 2, 5, 8), generator=g).to(torch.bfloat16)
     assert torch.equal(q, a["q"])
+
+
+@pytest.mark.parametrize("N,W", [(1, 1), (10, 1), (10, 3), (10, 10), (10, 25), (333, 64), (1000, 999)])
+def test_window_pair_count(N, W):
+    """The flop credit of a sliding-window workload counts exactly the pairs the
+    oracle's mask allows (keys i-W < j <= i)."""
+    w = si.Workload("t", 1, 1, 1, N, 64, True, False, 0, window=W)
+    assert w.pairs() == int(oracle.allowed_mask(0, N, N, True, W).sum())
