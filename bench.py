@@ -9,7 +9,10 @@ forward-only workloads. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is algorithmic TFLOP/s of a step (4*d flops per
 allowed (query, key) pair forward, 2.5x that backward; masked pairs and the
-backward's recomputed products are not credited).
+backward's recomputed products are not credited). The backward runs through
+its three pass entry points, with a HIP event between consecutive kernels, so
+the same timed steps give each kernel's average launch duration; the
+roofline object is computed for the kernel with the largest one.
 """
 
 from __future__ import annotations
@@ -329,7 +332,7 @@ def main():
 
     w = si.WORKLOADS[args.workload]
     inputs = si.workload_inputs(w)
-    g = {key: t.cuda() for key, t in inputs.items()}
+    g = {key: si.in_layout(t.cuda(), w.layout) for key, t in inputs.items()}
     stream = torch.cuda.current_stream()
     o = torch.empty_like(g["q"])
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
@@ -339,44 +342,58 @@ def main():
                          device="cuda")
 
     def run_fwd():
-        ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse)
+        ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
+               layout=w.layout, out=o, lse=lse)
 
     def run_bwd():
         ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal,
-               window=w.window, workspace=ws, dq=dq, dk=dk, dv=dv)
+               window=w.window, layout=w.layout, workspace=ws, dq=dq, dk=dk, dv=dv)
 
-    def step():
-        run_fwd()
-        if w.backward:
-            run_bwd()
+    def bwd_pass(name):
+        return lambda: ea.bwd_passes(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, ws,
+                                     scale=w.scale, causal=w.causal, window=w.window,
+                                     layout=w.layout, passes=(name,))
+
+    # One step = the forward, then the backward's three passes through their
+    # own entry points (the kernels attn_bwd launches, in its order). A HIP
+    # event on the launch stream sits between consecutive kernels, so the
+    # timed steps also give each kernel's average launch duration.
+    names, launches = ["fwd_kernel"], [run_fwd]
+    if w.backward:
+        names += ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+        launches += [bwd_pass("pre"), bwd_pass("dkdv"), bwd_pass("dq")]
 
     for _ in range(args.warmup):
-        step()
+        for f in launches:
+            f()
     torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+          for _ in range(args.steps)]
     t0 = time.perf_counter()
-    ms_step = time_loop(step, args.steps, stream)
+    for s_ev in ev:
+        s_ev[0].record(stream)
+        for i, f in enumerate(launches):
+            f()
+            s_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
     print(f"[bench] {args.steps} steps of {w.name}: {ms_step:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
-    # Per-kernel timings: each kernel launched alone through its own entry
-    # point, bracketed by HIP events on the stream it runs on.
     credit = kernel_flop_credit(w)
-    kernels = {"fwd_kernel": {"ms": time_loop(run_fwd, args.steps, stream), "flops": credit["fwd"],
-                              "bytes": w.fwd_bytes()}}
-    if w.backward:
-        def bwd_pass(name):
-            return lambda: ea.bwd_passes(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, ws,
-                                         scale=w.scale, causal=w.causal, window=w.window,
-                                         passes=(name,))
-        rows = w.B * w.Hq * w.N
-        kernels["bwd_pre_kernel"] = {"ms": time_loop(bwd_pass("pre"), args.steps, stream), "flops": 0.0,
-                                     "bytes": 2 * rows * w.d * 2 + 4 * rows}
-        kernels["bwd_dkdv_kernel"] = {"ms": time_loop(bwd_pass("dkdv"), args.steps, stream),
-                                      "flops": credit["bwd_dkdv"]}
-        kernels["bwd_dq_kernel"] = {"ms": time_loop(bwd_pass("dq"), args.steps, stream),
-                                    "flops": credit["bwd_dq"]}
-        ms_bwd = time_loop(run_bwd, args.steps, stream)
+    rows = w.B * w.Hq * w.N
+    work = {"fwd_kernel": (credit["fwd"], w.fwd_bytes()),
+            "bwd_pre_kernel": (0.0, 2 * rows * w.d * 2 + 4 * rows),
+            "bwd_dkdv_kernel": (credit["bwd_dkdv"], None),
+            "bwd_dq_kernel": (credit["bwd_dq"], None)}
+    kernels = {}
+    for i, name in enumerate(names):
+        ms = sum(s_ev[i].elapsed_time(s_ev[i + 1]) for s_ev in ev) / args.steps
+        flops, nbytes = work[name]
+        kernels[name] = {"ms": ms, "flops": flops}
+        if nbytes is not None:
+            kernels[name]["bytes"] = nbytes
     for k in kernels.values():
         k["tflops"] = round(k["flops"] / k["ms"] / 1e9, 2)
         k["pct_of_bf16_peak"] = round(100.0 * k["tflops"] / PEAK_BF16_TFLOPS, 2)
@@ -385,9 +402,12 @@ def main():
     passes = {"fwd": {"ms": kernels["fwd_kernel"]["ms"], "tflops": kernels["fwd_kernel"]["tflops"],
                       "pct_of_bf16_peak": kernels["fwd_kernel"]["pct_of_bf16_peak"]}}
     if w.backward:
+        ms_bwd = sum(kernels[n]["ms"] for n in names[1:])
         tf = w.bwd_flops() / ms_bwd / 1e9
         passes["bwd"] = {"ms": round(ms_bwd, 4), "tflops": round(tf, 2),
                          "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+        # The fused attn_bwd call (same kernels, no events between them).
+        passes["bwd"]["fused_call_ms"] = round(time_loop(run_bwd, args.steps, stream), 4)
 
     step_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     value = step_flops / (ms_step * 1e-3) / 1e12
@@ -417,7 +437,7 @@ def main():
 
     run_fwd()
     torch.cuda.synchronize()
-    par = parity_sample(w, inputs, o, lse)
+    par = parity_sample(w, inputs, o.transpose(1, 2) if w.layout == "bshd" else o, lse)
     print(f"[bench] parity sample: {par}", file=sys.stderr, flush=True)
 
     cpu = None
@@ -436,10 +456,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "window": w.window,
+                   "causal": w.causal, "window": w.window, "layout": w.layout,
                    "passes": "fwd+bwd" if w.backward else "fwd",
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

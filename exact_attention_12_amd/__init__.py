@@ -1,14 +1,21 @@
 """Python binding of libattn.so, the gfx950 exact-attention library.
 
-Argument marshalling only: tensors are checked (device, dtype, layout), their
-device pointers and the current HIP stream are passed to the C ABI declared in
-include/attn.h, and outputs are allocated with torch. Every step of the
-computation runs in the library's HIP kernels; there is no other code path.
+Argument marshalling only: tensors are checked (device, dtype, shape), their
+device pointers, strides and the current HIP stream are passed to the C ABI
+declared in include/attn.h, and outputs are allocated with torch. Every step of
+the computation runs in the library's HIP kernels; there is no other code path.
 If the library is missing or fails to load, every call raises.
 
     o, lse = fwd(q, k, v, causal=True)              # scale defaults to 1/sqrt(d)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
     o, lse = fwd(q, k, v, window=256)               # sliding window i-256 < j <= i
+    o, lse = fwd(q, k, v, layout="bshd")            # [B, N, H, d] tensors, read in place
+
+Tensors are bf16 or fp16 (all of one call alike), 4-D, innermost dim
+contiguous; `layout` says whether dims 1 and 2 are (H, N) ("bhsd", default) or
+(N, H) ("bshd"). Contiguous bf16 BHSD calls go through attn_fwd / attn_bwd (and
+their window and pass variants); anything else through attn_fwd_ex /
+attn_bwd_ex with explicit strides.
 """
 
 from __future__ import annotations
@@ -23,7 +30,7 @@ ROOT_DIR = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 HEADER_PATH = os.path.join(ROOT_DIR, "include", "attn.h")
 
-SUPPORTED_HEAD_DIMS = (64, 80, 128, 256)
+SUPPORTED_HEAD_DIMS = (32, 64, 80, 96, 128, 192, 256)
 
 STATUS = {
     0: "ATTN_OK",
@@ -36,7 +43,14 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE",
     8: "ATTN_ERR_HIP",
     9: "ATTN_ERR_WINDOW",
+    10: "ATTN_ERR_STRIDE",
+    11: "ATTN_ERR_DTYPE",
+    12: "ATTN_ERR_PASSES",
 }
+
+MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW = 0, 1, 2
+DTYPE_BF16, DTYPE_FP16 = 0, 1
+PASS_BITS = {"pre": 1, "dkdv": 2, "dq": 4}
 
 
 class AttnError(RuntimeError):
@@ -57,6 +71,29 @@ class AttnPlan(ctypes.Structure):
     ]
 
 
+class AttnTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_b", ctypes.c_longlong),
+        ("stride_h", ctypes.c_longlong),
+        ("stride_n", ctypes.c_longlong),
+    ]
+
+
+class AttnProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int),
+        ("Hq", ctypes.c_int),
+        ("Hkv", ctypes.c_int),
+        ("N", ctypes.c_int),
+        ("d", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("mask", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+    ]
+
+
 _lib = None
 
 
@@ -70,21 +107,20 @@ def lib() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build it with `python -m exact_attention_12_amd.build` "
             "or __graft_entry__.build(); there is no fallback implementation")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    vp, i, f, sz, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint
+    tp, pp = ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnProblem)
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
-    L.attn_fwd.restype = i
     L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
-    L.attn_fwd_window.restype = i
+    L.attn_fwd_ex.argtypes = [pp, tp, tp, tp, tp, vp, vp]
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
-    L.attn_bwd.restype = i
     L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
-    L.attn_bwd_window.restype = i
+    L.attn_bwd_ex.argtypes = [pp, tp, tp, tp, tp, vp, tp, tp, tp, tp, vp, sz, u, vp]
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
-    L.attn_bwd_preprocess.restype = i
     L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
-    L.attn_bwd_dkdv.restype = i
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
-    L.attn_bwd_dq.restype = i
+    for name in ("attn_fwd", "attn_fwd_window", "attn_fwd_ex", "attn_bwd", "attn_bwd_window",
+                 "attn_bwd_ex", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"):
+        getattr(L, name).restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_status_string.argtypes = [i]
@@ -120,30 +156,82 @@ def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require(t, name, dtype, ndim):
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float16:
+        return DTYPE_FP16
+    raise TypeError(f"tensors must be bfloat16 or float16 (got {t.dtype})")
+
+
+def _as_bhsd(t, name, layout):
+    """The [B, H, N, d] view of a 4-D operand given in `layout`."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims (got shape {tuple(t.shape)})")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous (stride 1)")
+    if layout == "bhsd":
+        return t
+    if layout == "bshd":
+        return t.transpose(1, 2)
+    raise ValueError(f"layout must be 'bhsd' or 'bshd' (got {layout!r})")
+
+
+def _new_like(ref_bhsd, layout):
+    """A fresh output with ref's [B, H, N, d] shape, contiguous in `layout`,
+    returned as its [B, H, N, d] view."""
+    import torch
+    B, H, N, d = ref_bhsd.shape
+    if layout == "bshd":
+        return torch.empty((B, N, H, d), dtype=ref_bhsd.dtype, device=ref_bhsd.device).transpose(1, 2)
+    return torch.empty((B, H, N, d), dtype=ref_bhsd.dtype, device=ref_bhsd.device)
+
+
+def _plain(ts):
+    """True when every tensor is contiguous bf16 [B, H, N, d]."""
+    import torch
+    return all(t is None or (t.dtype == torch.bfloat16 and t.is_contiguous()) for t in ts)
+
+
+def _tensor(t):
+    if t is None:
+        return None
+    return ctypes.byref(AttnTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)))
 
 
 def _shapes(q, k, v):
-    import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, torch.bfloat16, 4)
     B, Hq, N, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must have one dtype")
+    _dtype_code(q)
     return B, Hq, k.shape[1], N, d
+
+
+def _same(t, name, ref):
+    if tuple(t.shape) != tuple(ref.shape):
+        raise ValueError(f"{name} must have shape {tuple(ref.shape)} (got {tuple(t.shape)})")
+    if t.dtype != ref.dtype:
+        raise TypeError(f"{name} must be {ref.dtype} (got {t.dtype})")
+    if t.device != ref.device:
+        raise ValueError(f"{name} must be on {ref.device}")
+
+
+def _rows(t, name, B, Hq, N, device):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device != device or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 tensor on {device}")
+    if tuple(t.shape) != (B, Hq, N) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, Hq, N] = {(B, Hq, N)}")
 
 
 def default_scale(d: int) -> float:
@@ -160,114 +248,130 @@ def _window_arg(window):
     return window
 
 
-def fwd(q, k, v, *, scale=None, causal=False, window=None, out=None, lse=None):
-    """Forward pass. q [B,Hq,N,d], k, v [B,Hkv,N,d] bf16 contiguous on the GPU.
+def _problem(B, Hq, Hkv, N, d, scale, causal, window, dtype):
+    if window is not None:
+        mask, win = MASK_SLIDING_WINDOW, window
+    else:
+        mask, win = (MASK_CAUSAL if causal else MASK_NONE), 0
+    return AttnProblem(B, Hq, Hkv, N, d, float(scale), mask, win, dtype)
+
+
+def fwd(q, k, v, *, scale=None, causal=False, window=None, layout="bhsd", out=None, lse=None,
+        use_ex=False):
+    """Forward pass. q [B,Hq,N,d], k, v [B,Hkv,N,d] (dims 1, 2 swapped for
+    layout="bshd"), bf16 or fp16, on the GPU.
 
     window=W (>= 1) selects the sliding-window mask i-W < j <= i, which
-    implies the causal mask. Returns (o [B,Hq,N,d] bf16, lse [B,Hq,N] float32).
-    Enqueued on the current stream; no synchronisation.
+    implies the causal mask. Returns (o like q, lse [B,Hq,N] float32).
+    Enqueued on the current stream; no synchronisation. use_ex forces the
+    strided entry point even for plain tensors.
     """
-    window = _window_arg(window)
     import torch
-    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    window = _window_arg(window)
+    qv, kv_, vv = (_as_bhsd(t, n, layout) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    B, Hq, Hkv, N, d = _shapes(qv, kv_, vv)
     if scale is None:
         scale = default_scale(d)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", torch.bfloat16, 4)
-        if out.shape != q.shape:
-            raise ValueError("out must have the shape of q")
+    ov = _new_like(qv, layout) if out is None else _as_bhsd(out, "out", layout)
+    _same(ov, "out", qv)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _rows(lse, "lse", B, Hq, N, q.device)
+    st = _stream_ptr(q.device)
+    L = lib()
+    if not use_ex and _plain((qv, kv_, vv, ov)):
+        if window is None:
+            _check(L.attn_fwd(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
+                              B, Hq, Hkv, N, d, float(scale), int(bool(causal)), st))
+        else:
+            _check(L.attn_fwd_window(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(),
+                                     lse.data_ptr(), B, Hq, Hkv, N, d, float(scale), window, st))
     else:
-        _require(lse, "lse", torch.float32, 3)
-        if tuple(lse.shape) != (B, Hq, N):
-            raise ValueError("lse must be [B, Hq, N]")
-    if window is None:
-        _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                              B, Hq, Hkv, N, d, float(scale), int(bool(causal)), _stream_ptr(q.device)))
-    else:
-        _check(lib().attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                     lse.data_ptr(), B, Hq, Hkv, N, d, float(scale), window,
-                                     _stream_ptr(q.device)))
-    return out, lse
+        prob = _problem(B, Hq, Hkv, N, d, scale, causal, window, _dtype_code(qv))
+        _check(L.attn_fwd_ex(ctypes.byref(prob), _tensor(qv), _tensor(kv_), _tensor(vv), _tensor(ov),
+                             lse.data_ptr(), st))
+    return (ov.transpose(1, 2) if layout == "bshd" else ov), lse
 
 
 def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
 
 
-def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, window=None, workspace=None,
-        dq=None, dk=None, dv=None):
-    """Backward pass; returns (dq, dk, dv) bf16 like q, k, v. `causal` and
-    `window` must be those of the forward call."""
-    import torch
-    window = _window_arg(window)
-    B, Hq, Hkv, N, d = _shapes(q, k, v)
-    _require(o, "o", torch.bfloat16, 4)
-    _require(do, "do", torch.bfloat16, 4)
-    _require(lse, "lse", torch.float32, 3)
-    if o.shape != q.shape or do.shape != q.shape or tuple(lse.shape) != (B, Hq, N):
-        raise ValueError("o, do must have the shape of q and lse must be [B, Hq, N]")
-    if scale is None:
-        scale = default_scale(d)
-    need = bwd_workspace_bytes(B, Hq, Hkv, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _require(t, name, torch.bfloat16, 4)
-        if t.shape != ref.shape:
-            raise ValueError(f"{name} has the wrong shape")
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            B, Hq, Hkv, N, d, float(scale))
-    if window is None:
-        _check(lib().attn_bwd(*args, int(bool(causal)), _stream_ptr(q.device)))
-    else:
-        _check(lib().attn_bwd_window(*args, window, _stream_ptr(q.device)))
-    return dq, dk, dv
+def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, window=None, layout="bhsd",
+        workspace=None, dq=None, dk=None, dv=None, use_ex=False):
+    """Backward pass; returns (dq, dk, dv) like q, k, v. `causal`, `window`
+    and `layout` must be those of the forward call."""
+    return bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=scale, causal=causal,
+                      window=window, layout=layout, passes=("pre", "dkdv", "dq"), use_ex=use_ex,
+                      fused=True)
 
 
 def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal=False,
-               window=None, passes=("pre", "dkdv", "dq")):
-    """Run selected backward passes through their own entry points (same
-    arguments and checks as bwd(); outputs must be preallocated). A window
-    implies the causal mask."""
+               window=None, layout="bhsd", passes=("pre", "dkdv", "dq"), use_ex=False, fused=False):
+    """Run selected backward passes (same arguments and checks as bwd()). With
+    fused=False each pass goes through its own entry point; outputs may be
+    None and are then allocated. A window implies the causal mask."""
     import torch
     window = _window_arg(window)
     if window is not None:
         causal = True
-    win = 0 if window is None else window
-    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    bits = 0
+    for p in passes:
+        if p not in PASS_BITS:
+            raise ValueError(f"unknown backward pass {p!r}")
+        bits |= PASS_BITS[p]
+    qv, kv_, vv = (_as_bhsd(t, n, layout) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    B, Hq, Hkv, N, d = _shapes(qv, kv_, vv)
+    ov, dov = _as_bhsd(o, "o", layout), _as_bhsd(do, "do", layout)
+    _same(ov, "o", qv)
+    _same(dov, "do", qv)
+    _rows(lse, "lse", B, Hq, N, q.device)
     if scale is None:
         scale = default_scale(d)
-    for name, t in (("o", o), ("do", do), ("dq", dq)):
-        _require(t, name, torch.bfloat16, 4)
-    for name, t in (("dk", dk), ("dv", dv)):
-        _require(t, name, torch.bfloat16, 4)
-    _require(lse, "lse", torch.float32, 3)
-    L = lib()
+    outs = []
+    for name, t, ref in (("dq", dq, qv), ("dk", dk, kv_), ("dv", dv, vv)):
+        tv = _new_like(ref, layout) if t is None else _as_bhsd(t, name, layout)
+        _same(tv, name, ref)
+        outs.append(tv)
+    dqv, dkv, dvv = outs
+    need = bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     ws, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = _stream_ptr(q.device)
-    for p in passes:
-        if p == "pre":
-            _check(L.attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, st))
-        elif p == "dkdv":
-            _check(L.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                                   dk.data_ptr(), dv.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, float(scale),
-                                   int(bool(causal)), win, st))
-        elif p == "dq":
-            _check(L.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                                 dq.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, float(scale),
-                                 int(bool(causal)), win, st))
+    L = lib()
+    win = 0 if window is None else window
+    if not use_ex and _plain((qv, kv_, vv, ov, dov, dqv, dkv, dvv)):
+        args = (qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
+                dov.data_ptr(), dqv.data_ptr(), dkv.data_ptr(), dvv.data_ptr(), ws, wsb,
+                B, Hq, Hkv, N, d, float(scale))
+        if fused and bits == 7:
+            if window is None:
+                _check(L.attn_bwd(*args, int(bool(causal)), st))
+            else:
+                _check(L.attn_bwd_window(*args, window, st))
         else:
-            raise ValueError(f"unknown backward pass {p!r}")
-    return dq, dk, dv
+            for p in ("pre", "dkdv", "dq"):
+                if not bits & PASS_BITS[p]:
+                    continue
+                if p == "pre":
+                    _check(L.attn_bwd_preprocess(ov.data_ptr(), dov.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, st))
+                elif p == "dkdv":
+                    _check(L.attn_bwd_dkdv(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), lse.data_ptr(),
+                                           dov.data_ptr(), dkv.data_ptr(), dvv.data_ptr(), ws, wsb,
+                                           B, Hq, Hkv, N, d, float(scale), int(bool(causal)), win, st))
+                else:
+                    _check(L.attn_bwd_dq(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), lse.data_ptr(),
+                                         dov.data_ptr(), dqv.data_ptr(), ws, wsb,
+                                         B, Hq, Hkv, N, d, float(scale), int(bool(causal)), win, st))
+    else:
+        prob = _problem(B, Hq, Hkv, N, d, scale, causal, window, _dtype_code(qv))
+        _check(L.attn_bwd_ex(ctypes.byref(prob), _tensor(qv), _tensor(kv_), _tensor(vv), _tensor(ov),
+                             lse.data_ptr(), _tensor(dov), _tensor(dqv), _tensor(dkv), _tensor(dvv),
+                             ws, wsb, bits, st))
+    if layout == "bshd":
+        return tuple(t.transpose(1, 2) for t in outs)
+    return dqv, dkv, dvv
 
 
 def fwd_plan(B, Hq, Hkv, N, d, causal=False) -> dict:

@@ -18,7 +18,15 @@ thread_local char g_last_hip_error[256] = "";
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
-bool head_dim_ok(int d) { return d == 64 || d == 80 || d == 128 || d == 256; }
+bool head_dim_ok(int d) {
+    switch (d) {
+#define ATTN_HEAD_DIM_OK(D_) case D_:
+        ATTN_FOR_EACH_HEAD_DIM(ATTN_HEAD_DIM_OK)
+#undef ATTN_HEAD_DIM_OK
+        return true;
+        default: return false;
+    }
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -44,51 +52,222 @@ attn_status check_scale(float scale) {
     return ATTN_OK;
 }
 
+// Mask kind and window of a problem; the window is returned in the form the
+// kernels take: 0 = no band, else W with 1 <= W < N (a band of N or more keys
+// is the plain causal mask).
+attn_status check_mask(const attn_problem& pr, int* kernel_mask, int* kernel_window) {
+    switch (pr.mask) {
+        case ATTN_MASK_NONE:
+        case ATTN_MASK_CAUSAL:
+            if (pr.window != 0) return ATTN_ERR_WINDOW;
+            *kernel_mask = pr.mask == ATTN_MASK_NONE ? attn::kMaskNone : attn::kMaskCausal;
+            *kernel_window = 0;
+            return ATTN_OK;
+        case ATTN_MASK_SLIDING_WINDOW:
+            if (pr.window < 1) return ATTN_ERR_WINDOW;
+            if (pr.window >= pr.N) {
+                *kernel_mask = attn::kMaskCausal;
+                *kernel_window = 0;
+            } else {
+                *kernel_mask = attn::kMaskWindow;
+                *kernel_window = pr.window;
+            }
+            return ATTN_OK;
+        default: return ATTN_ERR_WINDOW;
+    }
+}
+
 attn_status hip_status(hipError_t e) {
     if (e == hipSuccess) return ATTN_OK;
     std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s", hipGetErrorString(e));
     return ATTN_ERR_HIP;
 }
 
-// Window as the kernels take it: 0 = no band, else W with 1 <= W < N (a band
-// of N or more keys is the plain causal mask).
-int kernel_window(int window, int N) { return window >= N ? 0 : window; }
+attn::Strides strides_of(const attn_tensor& t) { return {t.stride_b, t.stride_h, t.stride_n}; }
 
-int mask_kind(int causal, int kernel_window) {
-    if (causal == 0) return attn::kMaskNone;
-    return kernel_window > 0 ? attn::kMaskWindow : attn::kMaskCausal;
+// Contiguous BHSD view of a plain pointer.
+attn_tensor bhsd(const void* p, int H, int N, int d) {
+    attn_tensor t;
+    t.data = const_cast<void*>(p);
+    t.stride_n = d;
+    t.stride_h = (long long)N * d;
+    t.stride_b = (long long)H * N * d;
+    return t;
 }
 
-attn_status fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                       int window, void* stream) {
-    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-    attn_status st = check_shape(B, Hq, Hkv, N, d);
+// Checks of the tensors an entry point uses: presence first (NULL), then
+// strides (STRIDE, ALIGN) and data alignment (ALIGN), so that the error
+// reported is the same whichever tensor carries it.
+attn_status check_null(const attn_tensor* const* ts, int n) {
+    for (int i = 0; i < n; ++i)
+        if (!ts[i] || !ts[i]->data) return ATTN_ERR_NULL;
+    return ATTN_OK;
+}
+attn_status check_layout(const attn_tensor* const* ts, int n) {
+    for (int i = 0; i < n; ++i)
+        if (ts[i]->stride_b < 0 || ts[i]->stride_h < 0 || ts[i]->stride_n < 0) return ATTN_ERR_STRIDE;
+    for (int i = 0; i < n; ++i) {
+        const attn_tensor& t = *ts[i];
+        if (!aligned16(t.data) || (t.stride_b | t.stride_h | t.stride_n) & 7) return ATTN_ERR_ALIGN;
+    }
+    return ATTN_OK;
+}
+
+attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_tensor* k,
+                     const attn_tensor* v, const attn_tensor* o, float* lse, void* stream) {
+    if (!pr) return ATTN_ERR_NULL;
+    const attn_tensor* ts[] = {q, k, v, o};
+    attn_status st = check_null(ts, 4);
     if (st != ATTN_OK) return st;
-    st = check_scale(scale);
+    if (!lse) return ATTN_ERR_NULL;
+    st = check_shape(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d);
     if (st != ATTN_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return ATTN_ERR_ALIGN;
+    st = check_scale(pr->scale);
+    if (st != ATTN_OK) return st;
+    int mask = 0, window = 0;
+    st = check_mask(*pr, &mask, &window);
+    if (st != ATTN_OK) return st;
+    if (pr->dtype != ATTN_DTYPE_BF16 && pr->dtype != ATTN_DTYPE_FP16) return ATTN_ERR_DTYPE;
+    st = check_layout(ts, 4);
+    if (st != ATTN_OK) return st;
+    if (!aligned16(lse)) return ATTN_ERR_ALIGN;
 
     attn::FwdPlan plan;
-    attn::fwd_plan(B, Hq, N, d, &plan);
+    attn::fwd_plan(pr->B, pr->Hq, pr->N, pr->d, &plan);
     attn::FwdParams p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
+    p.q = q->data;
+    p.k = k->data;
+    p.v = v->data;
+    p.o = o->data;
     p.lse = lse;
-    p.N = N;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.G = Hq / Hkv;
-    p.BH = B * Hq;
-    p.nqb = (N + plan.block_q - 1) / plan.block_q;
-    p.window = kernel_window(window, N);
-    p.c = scale * kLog2eHost;
+    p.sq = strides_of(*q);
+    p.sk = strides_of(*k);
+    p.sv = strides_of(*v);
+    p.so = strides_of(*o);
+    p.N = pr->N;
+    p.Hq = pr->Hq;
+    p.Hkv = pr->Hkv;
+    p.G = pr->Hq / pr->Hkv;
+    p.BH = pr->B * pr->Hq;
+    p.nqb = (pr->N + plan.block_q - 1) / plan.block_q;
+    p.window = window;
+    p.c = pr->scale * kLog2eHost;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_fwd(p, d, mask_kind(causal, p.window), plan,
+    return hip_status(attn::launch_fwd(p, pr->dtype, pr->d, mask, plan, static_cast<hipStream_t>(stream)));
+}
+
+size_t workspace_bytes_for(int B, int Hq, int Hkv, int N, int d) {
+    if (check_shape(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
+    const size_t bytes = (size_t)B * Hq * N * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+// Shared validation and dispatch of every backward entry point. Only the
+// tensors the selected passes read or write are checked; the others may be
+// NULL and are never dereferenced.
+attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_tensor* k,
+                     const attn_tensor* v, const attn_tensor* o, const float* lse,
+                     const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
+                     const attn_tensor* dv, const void* workspace, size_t workspace_bytes,
+                     unsigned passes, void* stream) {
+    if (!pr) return ATTN_ERR_NULL;
+    if (passes == 0 || (passes & ~(unsigned)attn::kBwdAll)) return ATTN_ERR_PASSES;
+    const bool pre = passes & attn::kBwdPre, kv = passes & attn::kBwdDkDv, qq = passes & attn::kBwdDq;
+    const bool main = kv || qq;
+    const attn_tensor* ts[8];
+    int n = 0;
+    ts[n++] = dout;
+    if (pre) ts[n++] = o;
+    if (main) { ts[n++] = q; ts[n++] = k; ts[n++] = v; }
+    if (qq) ts[n++] = dq;
+    if (kv) { ts[n++] = dk; ts[n++] = dv; }
+    attn_status st = check_null(ts, n);
+    if (st != ATTN_OK) return st;
+    if (main && !lse) return ATTN_ERR_NULL;
+    st = check_shape(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d);
+    if (st != ATTN_OK) return st;
+    int mask = 0, window = 0;
+    if (main) {
+        st = check_scale(pr->scale);
+        if (st != ATTN_OK) return st;
+        st = check_mask(*pr, &mask, &window);
+        if (st != ATTN_OK) return st;
+    }
+    if (pr->dtype != ATTN_DTYPE_BF16 && pr->dtype != ATTN_DTYPE_FP16) return ATTN_ERR_DTYPE;
+    if (!workspace || workspace_bytes < workspace_bytes_for(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d))
+        return ATTN_ERR_WORKSPACE;
+    st = check_layout(ts, n);
+    if (st != ATTN_OK) return st;
+    if ((main && !aligned16(lse)) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
+
+    const attn_tensor none = {nullptr, 0, 0, 0};
+    auto or_none = [&](const attn_tensor* t, bool used) -> const attn_tensor& {
+        return used ? *t : none;
+    };
+    attn::BwdParams p;
+    p.q = or_none(q, main).data;
+    p.k = or_none(k, main).data;
+    p.v = or_none(v, main).data;
+    p.o = or_none(o, pre).data;
+    p.lse = main ? lse : nullptr;
+    p.dout = dout->data;
+    p.dq = or_none(dq, qq).data;
+    p.dk = or_none(dk, kv).data;
+    p.dv = or_none(dv, kv).data;
+    p.delta = static_cast<float*>(const_cast<void*>(workspace));
+    p.sq = strides_of(or_none(q, main));
+    p.sk = strides_of(or_none(k, main));
+    p.sv = strides_of(or_none(v, main));
+    p.so = strides_of(or_none(o, pre));
+    p.sdo = strides_of(*dout);
+    p.sdq = strides_of(or_none(dq, qq));
+    p.sdk = strides_of(or_none(dk, kv));
+    p.sdv = strides_of(or_none(dv, kv));
+    p.N = pr->N;
+    p.Hq = pr->Hq;
+    p.Hkv = pr->Hkv;
+    p.G = pr->Hq / pr->Hkv;
+    p.B = pr->B;
+    p.window = window;
+    p.scale = pr->scale;
+    p.c = pr->scale * kLog2eHost;
+    g_last_hip_error[0] = '\0';
+    return hip_status(attn::launch_bwd(p, pr->dtype, pr->d, mask, (int)passes,
                                        static_cast<hipStream_t>(stream)));
+}
+
+attn_problem plain_problem(int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                           int window) {
+    attn_problem pr;
+    pr.B = B;
+    pr.Hq = Hq;
+    pr.Hkv = Hkv;
+    pr.N = N;
+    pr.d = d;
+    pr.scale = scale;
+    pr.mask = window > 0 ? ATTN_MASK_SLIDING_WINDOW : (causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE);
+    pr.window = window;
+    pr.dtype = ATTN_DTYPE_BF16;
+    return pr;
+}
+
+// The plain-pointer backward entry points: contiguous bf16 BHSD views of
+// whatever pointers a pass uses (NULL stays NULL).
+attn_status bwd_plain(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      const void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
+                      void* stream, unsigned passes) {
+    if (window < 0 || (window > 0 && causal == 0)) {
+        if (passes & (attn::kBwdDkDv | attn::kBwdDq)) return ATTN_ERR_WINDOW;
+        window = 0;
+    }
+    const attn_problem pr = plain_problem(B, Hq, Hkv, N, d, scale, causal, window);
+    const attn_tensor tq = bhsd(q, Hq, N, d), tk = bhsd(k, Hkv, N, d), tv = bhsd(v, Hkv, N, d),
+                      to = bhsd(o, Hq, N, d), tdo = bhsd(dout, Hq, N, d), tdq = bhsd(dq, Hq, N, d),
+                      tdk = bhsd(dk, Hkv, N, d), tdv = bhsd(dv, Hkv, N, d);
+    return bwd_impl(&pr, &tq, &tk, &tv, &to, lse, &tdo, &tdq, &tdk, &tdv, workspace, workspace_bytes,
+                    passes, stream);
 }
 
 }  // namespace
@@ -98,81 +277,30 @@ extern "C" {
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      void* stream) {
-    return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 0, stream);
+    const attn_problem pr = plain_problem(B, Hq, Hkv, N, d, scale, causal, 0);
+    const attn_tensor tq = bhsd(q, Hq, N, d), tk = bhsd(k, Hkv, N, d), tv = bhsd(v, Hkv, N, d),
+                      to = bhsd(o, Hq, N, d);
+    return fwd_impl(&pr, &tq, &tk, &tv, &to, lse, stream);
 }
 
 attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int N, int d, float scale, int window,
                             void* stream) {
     if (window < 1) return ATTN_ERR_WINDOW;
-    return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, 1, window, stream);
+    const attn_problem pr = plain_problem(B, Hq, Hkv, N, d, scale, 1, window);
+    const attn_tensor tq = bhsd(q, Hq, N, d), tk = bhsd(k, Hkv, N, d), tv = bhsd(v, Hkv, N, d),
+                      to = bhsd(o, Hq, N, d);
+    return fwd_impl(&pr, &tq, &tk, &tv, &to, lse, stream);
+}
+
+attn_status attn_fwd_ex(const attn_problem* problem, const attn_tensor* q, const attn_tensor* k,
+                        const attn_tensor* v, const attn_tensor* o, float* lse, void* stream) {
+    return fwd_impl(problem, q, k, v, o, lse, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
-    if (check_shape(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
-    const size_t bytes = (size_t)B * Hq * N * sizeof(float);
-    return (bytes + 255) & ~(size_t)255;
+    return workspace_bytes_for(B, Hq, Hkv, N, d);
 }
-
-}  // extern "C"
-
-namespace {
-
-// Shared validation and dispatch of attn_bwd and its three pass entry points.
-// Only the pointers the selected passes read or write are checked; the
-// others are NULL and never dereferenced.
-attn_status bwd_common(const void* q, const void* k, const void* v, const void* o,
-                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                       const void* workspace, size_t workspace_bytes,
-                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                       int window, void* stream, int passes) {
-    const bool pre = passes & attn::kBwdPre, kv = passes & attn::kBwdDkDv, qq = passes & attn::kBwdDq;
-    const bool main = kv || qq;
-    const void* used[] = {pre ? o : dout, dout, main ? q : dout, main ? k : dout,
-                          main ? v : dout, main ? static_cast<const void*>(lse) : dout,
-                          qq ? dq : dout, kv ? dk : dout, kv ? dv : dout};
-    for (const void* ptr : used)
-        if (!ptr) return ATTN_ERR_NULL;
-    attn_status st = check_shape(B, Hq, Hkv, N, d);
-    if (st != ATTN_OK) return st;
-    if (main) {
-        st = check_scale(scale);
-        if (st != ATTN_OK) return st;
-        if (window < 0 || (window > 0 && causal == 0)) return ATTN_ERR_WINDOW;
-    }
-    if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
-        return ATTN_ERR_WORKSPACE;
-    for (const void* ptr : used)
-        if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
-    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-
-    attn::BwdParams p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.lse = lse;
-    p.dout = dout;
-    p.dq = dq;
-    p.dk = dk;
-    p.dv = dv;
-    p.delta = static_cast<float*>(const_cast<void*>(workspace));
-    p.N = N;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.G = Hq / Hkv;
-    p.B = B;
-    p.window = kernel_window(window, N);
-    p.scale = scale;
-    p.c = scale * kLog2eHost;
-    g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_bwd(p, d, mask_kind(causal, p.window), passes,
-                                       static_cast<hipStream_t>(stream)));
-}
-
-}  // namespace
-
-extern "C" {
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout,
@@ -180,8 +308,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      void* stream) {
-    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
-                      d, scale, causal, 0, stream, attn::kBwdAll);
+    return bwd_plain(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
+                     scale, causal, 0, stream, attn::kBwdAll);
 }
 
 attn_status attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
@@ -191,15 +319,15 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
                             int B, int Hq, int Hkv, int N, int d, float scale, int window,
                             void* stream) {
     if (window < 1) return ATTN_ERR_WINDOW;
-    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
-                      d, scale, 1, window, stream, attn::kBwdAll);
+    return bwd_plain(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
+                     scale, 1, window, stream, attn::kBwdAll);
 }
 
 attn_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                                 void* stream) {
-    return bwd_common(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr,
-                      workspace, workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, 0, stream, attn::kBwdPre);
+    return bwd_plain(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr, workspace,
+                     workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, 0, stream, attn::kBwdPre);
 }
 
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
@@ -207,8 +335,8 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const flo
                           const void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                           int window, void* stream) {
-    return bwd_common(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B, Hq,
-                      Hkv, N, d, scale, causal, window, stream, attn::kBwdDkDv);
+    return bwd_plain(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B, Hq,
+                     Hkv, N, d, scale, causal, window, stream, attn::kBwdDkDv);
 }
 
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
@@ -216,8 +344,17 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float
                         const void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                         int window, void* stream) {
-    return bwd_common(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes, B,
-                      Hq, Hkv, N, d, scale, causal, window, stream, attn::kBwdDq);
+    return bwd_plain(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes, B,
+                     Hq, Hkv, N, d, scale, causal, window, stream, attn::kBwdDq);
+}
+
+attn_status attn_bwd_ex(const attn_problem* problem, const attn_tensor* q, const attn_tensor* k,
+                        const attn_tensor* v, const attn_tensor* o, const float* lse,
+                        const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
+                        const attn_tensor* dv, void* workspace, size_t workspace_bytes,
+                        unsigned passes, void* stream) {
+    return bwd_impl(problem, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, passes,
+                    stream);
 }
 
 const char* attn_status_string(attn_status status) {
@@ -226,12 +363,18 @@ const char* attn_status_string(attn_status status) {
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_SHAPE: return "B, Hq, Hkv and N must be >= 1 and the sizes must fit the grid";
         case ATTN_ERR_GQA: return "Hq must be a multiple of Hkv";
-        case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (supported: 64, 80, 128, 256)";
+        case ATTN_ERR_HEAD_DIM:
+            return "unsupported head dimension (supported: 32, 64, 80, 96, 128, 192, 256)";
         case ATTN_ERR_SCALE: return "scale must be finite and > 0";
-        case ATTN_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+        case ATTN_ERR_ALIGN:
+            return "device pointers must be 16-byte aligned and strides multiples of 8 elements";
         case ATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
         case ATTN_ERR_HIP: return "the HIP runtime refused a launch (see attn_last_hip_error)";
-        case ATTN_ERR_WINDOW: return "window must be >= 1 and needs the causal mask";
+        case ATTN_ERR_WINDOW:
+            return "unknown mask kind, or a window that is < 1 or comes without the causal mask";
+        case ATTN_ERR_STRIDE: return "strides must be >= 0";
+        case ATTN_ERR_DTYPE: return "unknown element type (supported: bf16, fp16)";
+        case ATTN_ERR_PASSES: return "passes must be a nonzero subset of ATTN_BWD_ALL";
     }
     return "unknown status";
 }

@@ -26,7 +26,6 @@
 //     forward's orientation: S^T = K Q^T and dP^T = V dO^T put one query per
 //     lane, so LSE_i and D_i are per-lane scalars; dQ^T += K^T dS^T with K^T
 //     read transposed from the K tile.
-#include <type_traits>
 
 #include "attn_bwd_common.h"
 
@@ -34,34 +33,39 @@ namespace attn {
 
 // ---------------------------------------------------------------- D_i
 
-template <int D>
+// One 16-lane group per query row; rows are numbered (b * Hq + h) * N + n,
+// the layout of the D_i workspace.
+template <int DT, int D>
 __global__ __launch_bounds__(256)
-void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                    float* __restrict__ delta, long long rows) {
+void bwd_pre_kernel(BwdParams p, long long rows) {
     constexpr int CPR = D / 8;
     const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int j = threadIdx.x & 15;
     float acc = 0.0f;
     if (row < rows) {
-        const bf16* op = o + row * D;
-        const bf16* dp = dout + row * D;
+        const long long bh = row / p.N;
+        const int n = (int)(row - bh * p.N);
+        const int b = (int)(bh / p.Hq);
+        const int hq = (int)(bh - (long long)b * p.Hq);
+        const e16* op = static_cast<const e16*>(p.o) + b * p.so.b + hq * p.so.h + n * p.so.n;
+        const e16* dp = static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h + n * p.sdo.n;
         for (int c = j; c < CPR; c += 16) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(op + c * 8);
-            const bf16x8 g = *reinterpret_cast<const bf16x8*>(dp + c * 8);
+            const e16x8 a = *reinterpret_cast<const e16x8*>(op + c * 8);
+            const e16x8 g = *reinterpret_cast<const e16x8*>(dp + c * 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)g[e], acc);
+            for (int e = 0; e < 8; ++e) acc = fmaf(widen<DT>(a[e]), widen<DT>(g[e]), acc);
         }
     }
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 4);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 1);
-    if (row < rows && j == 0) delta[row] = acc;
+    if (row < rows && j == 0) p.delta[row] = acc;
 }
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, int MASK>
+template <int DT, int D, int MASK>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_kernel(BwdParams p) {
     constexpr bool CAUSAL = MASK != kMaskNone;
@@ -97,12 +101,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int kw0 = k0 + wave * 32;
     const int key = kw0 + l32;
 
-    const size_t kv_off = (size_t)bhk * N * D;
-    const bf16* Kh = static_cast<const bf16*>(p.k) + kv_off;
-    const bf16* Vh = static_cast<const bf16*>(p.v) + kv_off;
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
 
-    auto qtile = [&](int bufi) { return reinterpret_cast<bf16*>(smem_raw + bufi * BUF); };
-    auto dotile = [&](int bufi) { return reinterpret_cast<bf16*>(smem_raw + bufi * BUF) + TILE; };
+    auto qtile = [&](int bufi) { return reinterpret_cast<e16*>(smem_raw + bufi * BUF); };
+    auto dotile = [&](int bufi) { return reinterpret_cast<e16*>(smem_raw + bufi * BUF) + TILE; };
     auto lsetile = [&](int bufi) { return reinterpret_cast<float*>(smem_raw + bufi * BUF + 4 * TILE); };
     auto deltile = [&](int bufi) { return reinterpret_cast<float*>(smem_raw + bufi * BUF + 4 * TILE) + BQ; };
 
@@ -112,16 +115,16 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 
     // K, V as B operands (lane = key, 8 dims per register group).
-    bf16x8 kf[KS], vf[KS];
+    e16x8 kf[KS], vf[KS];
     if (key < N) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + ks * 16 + h * 8);
-            vf[ks] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + ks * 16 + h * 8);
+            kf[ks] = *reinterpret_cast<const e16x8*>(Kh + key * p.sk.n + ks * 16 + h * 8);
+            vf[ks] = *reinterpret_cast<const e16x8*>(Vh + key * p.sv.n + ks * 16 + h * 8);
         }
     } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) { kf[ks] = bf16x8{}; vf[ks] = bf16x8{}; }
+        for (int ks = 0; ks < KS; ++ks) { kf[ks] = e16x8{}; vf[ks] = e16x8{}; }
     }
 
     const int nqb = (N + BQ - 1) / BQ;
@@ -138,16 +141,16 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int g = it / nq_iter;
         const int qb = qb_start + (it - g * nq_iter);
         const int hq = hkv * p.G + g;
-        const size_t q_off = ((size_t)b * p.Hq + hq) * N;
+        const size_t row_off = ((size_t)b * p.Hq + hq) * N;  // LSE, D_i: contiguous
         const int r0 = qb * BQ;
-        qio.load(static_cast<const bf16*>(p.q) + q_off * D, r0, N, tid);
-        doio.load(static_cast<const bf16*>(p.dout) + q_off * D, r0, N, tid);
+        qio.load(static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h, p.sq.n, r0, N, tid);
+        doio.load(static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h, p.sdo.n, r0, N, tid);
         if (tid < BQ) {
             const int r = r0 + tid;
-            lse_r = (r < N) ? p.lse[q_off + r] * kLog2e : __builtin_huge_valf();
+            lse_r = (r < N) ? p.lse[row_off + r] * kLog2e : __builtin_huge_valf();
         } else if (tid < 2 * BQ) {
             const int r = r0 + tid - BQ;
-            del_r = (r < N) ? p.delta[q_off + r] : 0.0f;
+            del_r = (r < N) ? p.delta[row_off + r] : 0.0f;
         }
     };
     auto store_step = [&](int bufi) {
@@ -184,8 +187,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         // loop body): a wave whose keys all lie after this query block just
         // contributes zeros through the mask.
         {
-            const bf16* Qs = qtile(bufi);
-            const bf16* dOs = dotile(bufi);
+            const e16* Qs = qtile(bufi);
+            const e16* dOs = dotile(bufi);
             const float* Ls = lsetile(bufi);
             const float* Ds = deltile(bufi);
             f32x16 s[NQT], dp[NQT];
@@ -196,17 +199,17 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int off = sw_off(qt * 32 + l32, ks * 16 + h * 8, QP);
-                    s[qt] = mfma32(lds_read8(Qs + off), kf[ks], s[qt]);
-                    dp[qt] = mfma32(lds_read8(dOs + off), vf[ks], dp[qt]);
+                    s[qt] = mfma32<DT>(lds_read8(Qs + off), kf[ks], s[qt]);
+                    dp[qt] = mfma32<DT>(lds_read8(dOs + off), vf[ks], dp[qt]);
                 }
             }
-            // P = exp2(c*S - LSE2) and dS = P (dP - D), packed to bf16 in the
+            // P = exp2(c*S - LSE2) and dS = P (dP - D), packed to 16 bits in the
             // B-operand order of the dV/dK products. Under the causal mask the
             // query of register r (local offset qoff(r) + 4h) is masked for
             // this lane's key when key - q0 - 4h > qoff(r) (one compare with a
             // constant per element), and under a sliding window also when
             // qoff(r) > key - q0 - 4h + W - 1.
-            bf16x8 pb[PVS], dsb[PVS];
+            e16x8 pb[PVS], dsb[PVS];
             {
                 const int kq = key - q0 - 4 * h;
                 const int kq_w = kq + W - 1;
@@ -214,7 +217,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                 for (int u = 0; u < PVS; ++u) {
                     const int qt = u >> 1;
                     const int r0 = (u & 1) * 8;
-                    bf16x2 pp[4], dd[4];
+                    e16x2 pp[4], dd[4];
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
                         float pv[2], dv[2];
@@ -229,8 +232,8 @@ void bwd_dkdv_kernel(BwdParams p) {
                             pv[w] = pe;
                             dv[w] = pe * (dp[qt][r] - Ds[ql]);
                         }
-                        pp[e2] = to_bf16x2(pv[0], pv[1]);
-                        dd[e2] = to_bf16x2(dv[0], dv[1]);
+                        pp[e2] = cvt2<DT>(pv[0], pv[1]);
+                        dd[e2] = cvt2<DT>(dv[0], dv[1]);
                     }
                     pb[u] = cat8(pp[0], pp[1], pp[2], pp[3]);
                     dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
@@ -239,8 +242,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             // dV^T += dO^T P and dK^T += Q^T dS. The transposed operands of
             // contraction step u+1 are read from LDS before the products of
             // step u are issued, so the reads overlap the matrix work.
-            bf16x8 a_do[NDT], a_q[NDT];
-            auto read_ops = [&](int u, bf16x8* ado, bf16x8* aq) {
+            e16x8 a_do[NDT], a_q[NDT];
+            auto read_ops = [&](int u, e16x8* ado, e16x8* aq) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     // Rows u*16 + tr_row and +8 share (row & 7) = tr_row.
@@ -254,12 +257,12 @@ void bwd_dkdv_kernel(BwdParams p) {
             read_ops(0, a_do, a_q);
 #pragma unroll
             for (int u = 0; u < PVS; ++u) {
-                bf16x8 n_do[NDT], n_q[NDT];
+                e16x8 n_do[NDT], n_q[NDT];
                 if (LOOKAHEAD && u + 1 < PVS) read_ops(u + 1, n_do, n_q);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    mfma32_agpr(dvacc[dt], a_do[dt], pb[u]);
-                    mfma32_agpr(dkacc[dt], a_q[dt], dsb[u]);
+                    mfma32_agpr<DT>(dvacc[dt], a_do[dt], pb[u]);
+                    mfma32_agpr<DT>(dkacc[dt], a_q[dt], dsb[u]);
                 }
                 if (!LOOKAHEAD && u + 1 < PVS) read_ops(u + 1, a_do, a_q);
                 if (LOOKAHEAD && u + 1 < PVS) {
@@ -278,8 +281,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         agpr_acc_ready(dvacc[dt]);
     }
     if (key < N) {
-        bf16* dkrow = static_cast<bf16*>(p.dk) + kv_off + (size_t)key * D;
-        bf16* dvrow = static_cast<bf16*>(p.dv) + kv_off + (size_t)key * D;
+        e16* dkrow = static_cast<e16*>(p.dk) + b * p.sdk.b + hkv * p.sdk.h + key * p.sdk.n;
+        e16* dvrow = static_cast<e16*>(p.dv) + b * p.sdv.b + hkv * p.sdv.h + key * p.sdv.n;
         const float sc = p.scale;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -287,9 +290,9 @@ void bwd_dkdv_kernel(BwdParams p) {
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d = dt * 32 + g4 * 8 + h * 4;
                 if (d < D) {
-                    store_bf16x4(dkrow + d, dkacc[dt][g4 * 4 + 0] * sc, dkacc[dt][g4 * 4 + 1] * sc,
+                    store4<DT>(dkrow + d, dkacc[dt][g4 * 4 + 0] * sc, dkacc[dt][g4 * 4 + 1] * sc,
                                  dkacc[dt][g4 * 4 + 2] * sc, dkacc[dt][g4 * 4 + 3] * sc);
-                    store_bf16x4(dvrow + d, dvacc[dt][g4 * 4 + 0], dvacc[dt][g4 * 4 + 1],
+                    store4<DT>(dvrow + d, dvacc[dt][g4 * 4 + 0], dvacc[dt][g4 * 4 + 1],
                                  dvacc[dt][g4 * 4 + 2], dvacc[dt][g4 * 4 + 3]);
                 }
             }
@@ -298,46 +301,55 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- launch
 
-template <int D, int MASK>
+template <int DT, int D, int MASK>
 static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stream) {
     if (passes & kBwdPre) {
         const long long rows = (long long)p.B * p.Hq * p.N;
-        hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                           stream, static_cast<const bf16*>(p.o), static_cast<const bf16*>(p.dout),
-                           p.delta, rows);
+        hipLaunchKernelGGL((bwd_pre_kernel<DT, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                           stream, p, rows);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (passes & kBwdDkDv) {
         const long long nkb = (p.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK>), dim3((unsigned)(nkb * p.B * p.Hkv)), dim3(256),
-                           0, stream, p);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK>), dim3((unsigned)(nkb * p.B * p.Hkv)),
+                           dim3(256), 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (passes & kBwdDq) {
-        const hipError_t e = launch_bwd_dq(p, D, MASK, stream);
+        const hipError_t e = launch_bwd_dq(p, DT, D, MASK, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-template <int D>
+template <int DT, int D>
 static hipError_t launch_bwd_d(const BwdParams& p, int mask, int passes, hipStream_t stream) {
     switch (mask) {
-        case kMaskNone: return launch_bwd_dc<D, kMaskNone>(p, passes, stream);
-        case kMaskCausal: return launch_bwd_dc<D, kMaskCausal>(p, passes, stream);
-        case kMaskWindow: return launch_bwd_dc<D, kMaskWindow>(p, passes, stream);
+        case kMaskNone: return launch_bwd_dc<DT, D, kMaskNone>(p, passes, stream);
+        case kMaskCausal: return launch_bwd_dc<DT, D, kMaskCausal>(p, passes, stream);
+        case kMaskWindow: return launch_bwd_dc<DT, D, kMaskWindow>(p, passes, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, int mask, int passes, hipStream_t stream) {
+template <int DT>
+static hipError_t launch_bwd_t(const BwdParams& p, int d, int mask, int passes, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_bwd_d<64>(p, mask, passes, stream);
-        case 80: return launch_bwd_d<80>(p, mask, passes, stream);
-        case 128: return launch_bwd_d<128>(p, mask, passes, stream);
-        case 256: return launch_bwd_d<256>(p, mask, passes, stream);
+#define ATTN_BWD_CASE(D_) \
+        case D_: return launch_bwd_d<DT, D_>(p, mask, passes, stream);
+        ATTN_FOR_EACH_HEAD_DIM(ATTN_BWD_CASE)
+#undef ATTN_BWD_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int mask, int passes,
+                      hipStream_t stream) {
+    switch (dtype) {
+        case kBF16: return launch_bwd_t<kBF16>(p, d, mask, passes, stream);
+        case kFP16: return launch_bwd_t<kFP16>(p, d, mask, passes, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -6,8 +6,9 @@
 
 namespace attn {
 
-// Loads `rows` rows of a [N, D] bf16 head starting at row r0 into registers
-// (16-byte chunks, zero beyond N) and stores them to an LDS tile.
+// Loads `rows` rows of one head's [N, D] 16-bit operand (row stride sn
+// elements) starting at row r0 into registers (16-byte chunks, zero beyond N)
+// and stores them to an LDS tile.
 template <int D, int ROWS, int T>
 struct TileIO {
     static constexpr int CPR = D / 8;
@@ -15,7 +16,7 @@ struct TileIO {
     static constexpr int NCH = (CHUNKS + T - 1) / T;
     uint4 r[NCH];
 
-    __device__ __forceinline__ void load(const bf16* head, int r0, int N, int tid) {
+    __device__ __forceinline__ void load(const e16* head, long long sn, int r0, int N, int tid) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * T;
@@ -23,12 +24,12 @@ struct TileIO {
                 const int row = c / CPR;
                 const int col = c - row * CPR;
                 r[i] = (r0 + row < N)
-                           ? *reinterpret_cast<const uint4*>(head + (size_t)(r0 + row) * D + col * 8)
+                           ? *reinterpret_cast<const uint4*>(head + (r0 + row) * sn + col * 8)
                            : zero4();
             }
         }
     }
-    __device__ __forceinline__ void store(bf16* tile, int pitch, int tid) const {
+    __device__ __forceinline__ void store(e16* tile, int pitch, int tid) const {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * T;
@@ -40,7 +41,7 @@ struct TileIO {
         }
     }
     // Same, into a chunk-swizzled tile (sw_off).
-    __device__ __forceinline__ void store_sw(bf16* tile, int pitch, int tid) const {
+    __device__ __forceinline__ void store_sw(e16* tile, int pitch, int tid) const {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * T;
@@ -57,10 +58,10 @@ struct TileIO {
 // LDS tile (read by the transposing read of the last 32-wide tile, never
 // written by the loads).
 template <int D>
-__device__ __forceinline__ void zero_pad_cols_sw(bf16* tile, int rows, int pitch, int tid, int T) {
+__device__ __forceinline__ void zero_pad_cols_sw(e16* tile, int rows, int pitch, int tid, int T) {
     constexpr int PADC = ((D + 31) / 32) * 32 - D;
     if constexpr (PADC > 0) {
-        for (int i = tid; i < rows * PADC; i += T) tile[sw_off(i / PADC, D + i % PADC, pitch)] = (bf16)0.0f;
+        for (int i = tid; i < rows * PADC; i += T) tile[sw_off(i / PADC, D + i % PADC, pitch)] = (e16)0;
     }
 }
 

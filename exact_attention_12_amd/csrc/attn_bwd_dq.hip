@@ -15,7 +15,7 @@ namespace attn {
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, int MASK>
+template <int DT, int D, int MASK>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
 void bwd_dq_kernel(BwdParams p) {
     constexpr bool CAUSAL = MASK != kMaskNone;
@@ -32,7 +32,7 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int VP = k_pitch(D);     // V tile: row reads only
     constexpr int BUF = BC * (KP + VP);
 
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -49,10 +49,9 @@ void bwd_dq_kernel(BwdParams p) {
     const int b = bh / p.Hq;
     const int hq = bh - b * p.Hq;
     const int hkv = hq / p.G;
-    const size_t q_off = (size_t)bh * N;
-    const size_t kv_off = ((size_t)b * p.Hkv + hkv) * N * D;
-    const bf16* Kh = static_cast<const bf16*>(p.k) + kv_off;
-    const bf16* Vh = static_cast<const bf16*>(p.v) + kv_off;
+    const size_t row_off = (size_t)bh * N;  // LSE, D_i: contiguous [B, Hq, N]
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
 
     const int q0 = qb * BQ;
     const int qw0 = q0 + wave * 32;
@@ -60,21 +59,22 @@ void bwd_dq_kernel(BwdParams p) {
 
     for (int bufi = 0; bufi < 2; ++bufi) zero_pad_cols_sw<D>(smem + bufi * BUF, BC, KP, tid, T);
 
-    bf16x8 qf[KS], gf[KS];
+    e16x8 qf[KS], gf[KS];
     float lse2 = __builtin_huge_valf(), del = 0.0f;
     if (qrow < N) {
-        const bf16* qp = static_cast<const bf16*>(p.q) + (q_off + qrow) * D + h * 8;
-        const bf16* gp = static_cast<const bf16*>(p.dout) + (q_off + qrow) * D + h * 8;
+        const e16* qp = static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h + qrow * p.sq.n + h * 8;
+        const e16* gp =
+            static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h + qrow * p.sdo.n + h * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-            gf[ks] = *reinterpret_cast<const bf16x8*>(gp + ks * 16);
+            qf[ks] = *reinterpret_cast<const e16x8*>(qp + ks * 16);
+            gf[ks] = *reinterpret_cast<const e16x8*>(gp + ks * 16);
         }
-        lse2 = p.lse[q_off + qrow] * kLog2e;
-        del = p.delta[q_off + qrow];
+        lse2 = p.lse[row_off + qrow] * kLog2e;
+        del = p.delta[row_off + qrow];
     } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) { qf[ks] = bf16x8{}; gf[ks] = bf16x8{}; }
+        for (int ks = 0; ks < KS; ++ks) { qf[ks] = e16x8{}; gf[ks] = e16x8{}; }
     }
 
     const int nkb = (N + BC - 1) / BC;
@@ -84,8 +84,8 @@ void bwd_dq_kernel(BwdParams p) {
     const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
 
     TileIO<D, BC, T> kio, vio;
-    kio.load(Kh, kb_begin * BC, N, tid);
-    vio.load(Vh, kb_begin * BC, N, tid);
+    kio.load(Kh, p.sk.n, kb_begin * BC, N, tid);
+    vio.load(Vh, p.sv.n, kb_begin * BC, N, tid);
     kio.store_sw(smem + (kb_begin & 1) * BUF, KP, tid);
     vio.store(smem + (kb_begin & 1) * BUF + BC * KP, VP, tid);
     __syncthreads();
@@ -103,12 +103,12 @@ void bwd_dq_kernel(BwdParams p) {
         const int bufi = kb & 1;
         const bool has_next = kb + 1 < kb_end;
         if (has_next) {
-            kio.load(Kh, (kb + 1) * BC, N, tid);
-            vio.load(Vh, (kb + 1) * BC, N, tid);
+            kio.load(Kh, p.sk.n, (kb + 1) * BC, N, tid);
+            vio.load(Vh, p.sv.n, (kb + 1) * BC, N, tid);
         }
         const int kv0 = kb * BC;
-        const bf16* Ks = smem + bufi * BUF;
-        const bf16* Vs = Ks + BC * KP;
+        const e16* Ks = smem + bufi * BUF;
+        const e16* Vs = Ks + BC * KP;
         // Branch-free step: blocks past a wave's last query are masked to zero.
         {
             f32x16 s[NKT], dp[NKT];
@@ -116,19 +116,19 @@ void bwd_dq_kernel(BwdParams p) {
             for (int kt = 0; kt < NKT; ++kt) {
                 s[kt] = f32x16{};
                 dp[kt] = f32x16{};
-                const bf16* vp = Vs + (kt * 32 + l32) * VP + h * 8;
+                const e16* vp = Vs + (kt * 32 + l32) * VP + h * 8;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    s[kt] = mfma32(lds_read8(Ks + sw_off(kt * 32 + l32, ks * 16 + h * 8, KP)), qf[ks], s[kt]);
-                    dp[kt] = mfma32(lds_read8(vp + ks * 16), gf[ks], dp[kt]);
+                    s[kt] = mfma32<DT>(lds_read8(Ks + sw_off(kt * 32 + l32, ks * 16 + h * 8, KP)), qf[ks], s[kt]);
+                    dp[kt] = mfma32<DT>(lds_read8(vp + ks * 16), gf[ks], dp[kt]);
                 }
             }
-            // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to bf16
+            // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to 16 bits
             // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
             // is masked when it is >= N, (causal) > qrow or (sliding window)
             // < qrow - W + 1: compares with a constant per element, skipped
             // when the block needs no mask.
-            bf16x8 dsb[PVS];
+            e16x8 dsb[PVS];
             {
                 const bool MASKED = CAUSAL || (kv0 + BC > N);
                 const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
@@ -137,7 +137,7 @@ void bwd_dq_kernel(BwdParams p) {
                 for (int u = 0; u < PVS; ++u) {
                     const int kt = u >> 1;
                     const int r0 = (u & 1) * 8;
-                    bf16x2 dd[4];
+                    e16x2 dd[4];
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
                         float dv[2];
@@ -150,7 +150,7 @@ void bwd_dq_kernel(BwdParams p) {
                             if (WINDOW && koff < lo) pe = 0.0f;
                             dv[w] = pe * (dp[kt][r] - del);
                         }
-                        dd[e2] = to_bf16x2(dv[0], dv[1]);
+                        dd[e2] = cvt2<DT>(dv[0], dv[1]);
                     }
                     dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
                 }
@@ -160,8 +160,8 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, KP);
-                    const bf16x8 a = join8(lds_read_tr4(Ks + o0), lds_read_tr4(Ks + o0 + 8 * KP));
-                    dqacc[dt] = mfma32(a, dsb[u], dqacc[dt]);
+                    const e16x8 a = join8(lds_read_tr4(Ks + o0), lds_read_tr4(Ks + o0 + 8 * KP));
+                    dqacc[dt] = mfma32<DT>(a, dsb[u], dqacc[dt]);
                 }
             }
         }
@@ -173,7 +173,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
 
     if (qrow < N) {
-        bf16* dqrow = static_cast<bf16*>(p.dq) + (q_off + qrow) * D;
+        e16* dqrow = static_cast<e16*>(p.dq) + b * p.sdq.b + hq * p.sdq.h + qrow * p.sdq.n;
         const float sc = p.scale;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -181,35 +181,45 @@ void bwd_dq_kernel(BwdParams p) {
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d = dt * 32 + g4 * 8 + h * 4;
                 if (d < D)
-                    store_bf16x4(dqrow + d, dqacc[dt][g4 * 4 + 0] * sc, dqacc[dt][g4 * 4 + 1] * sc,
+                    store4<DT>(dqrow + d, dqacc[dt][g4 * 4 + 0] * sc, dqacc[dt][g4 * 4 + 1] * sc,
                                  dqacc[dt][g4 * 4 + 2] * sc, dqacc[dt][g4 * 4 + 3] * sc);
             }
     }
 }
 
-template <int D, int MASK>
+template <int DT, int D, int MASK>
 static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
     const long long nqb = (p.N + 127) / 128;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int DT, int D>
 static hipError_t launch_dq_d(const BwdParams& p, int mask, hipStream_t stream) {
     switch (mask) {
-        case kMaskNone: return launch_dq_dc<D, kMaskNone>(p, stream);
-        case kMaskCausal: return launch_dq_dc<D, kMaskCausal>(p, stream);
-        case kMaskWindow: return launch_dq_dc<D, kMaskWindow>(p, stream);
+        case kMaskNone: return launch_dq_dc<DT, D, kMaskNone>(p, stream);
+        case kMaskCausal: return launch_dq_dc<DT, D, kMaskCausal>(p, stream);
+        case kMaskWindow: return launch_dq_dc<DT, D, kMaskWindow>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_bwd_dq(const BwdParams& p, int d, int mask, hipStream_t stream) {
+template <int DT>
+static hipError_t launch_dq_t(const BwdParams& p, int d, int mask, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_dq_d<64>(p, mask, stream);
-        case 80: return launch_dq_d<80>(p, mask, stream);
-        case 128: return launch_dq_d<128>(p, mask, stream);
-        case 256: return launch_dq_d<256>(p, mask, stream);
+#define ATTN_DQ_CASE(D_) \
+        case D_: return launch_dq_d<DT, D_>(p, mask, stream);
+        ATTN_FOR_EACH_HEAD_DIM(ATTN_DQ_CASE)
+#undef ATTN_DQ_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, int mask, hipStream_t stream) {
+    switch (dtype) {
+        case kBF16: return launch_dq_t<kBF16>(p, d, mask, stream);
+        case kFP16: return launch_dq_t<kFP16>(p, d, mask, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -1,9 +1,10 @@
 // attn_device.h - device building blocks for the gfx950 (CDNA4) attention kernels.
 //
-// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16 and its
+// fp16 twin, wave64):
 //   D[32x32] += A[32x16] * B[16x32]
-//   A operand: lane l holds A[l % 32][8*(l/32) .. 8*(l/32)+7]   (8 bf16)
-//   B operand: lane l holds B[8*(l/32) .. +7][l % 32]          (8 bf16)
+//   A operand: lane l holds A[l % 32][8*(l/32) .. 8*(l/32)+7]   (8 values)
+//   B operand: lane l holds B[8*(l/32) .. +7][l % 32]          (8 values)
 //   D / C:     lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l % 32]
 // so a lane owns one column of the result and 16 of its rows, in four runs
 // of four consecutive rows.
@@ -21,10 +22,19 @@
 
 namespace attn {
 
-typedef __bf16 bf16;
+// 16-bit operands are stored as raw bits (e16) and interpreted by the
+// element type DT (bf16 or fp16) only where it matters: the matrix
+// instruction, fp32 -> 16-bit rounding and 16-bit -> fp32 widening.
+enum DType { kBF16 = 0, kFP16 = 1 };
+
+typedef unsigned short e16;
+typedef e16 e16x2 __attribute__((ext_vector_type(2)));
+typedef e16 e16x4 __attribute__((ext_vector_type(4)));
+typedef e16 e16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -34,8 +44,15 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// D[32x32] += A[32x16] * B[16x32] (v_mfma_f32_32x32x16_bf16 / _f16).
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(e16x8 a, e16x8 b, f32x16 c) {
+    if constexpr (DT == kBF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 // Accumulating MFMA with the accumulator pinned in AGPRs (acc += a * b).
@@ -49,8 +66,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //    interlocked by the hardware;
 //  * reading the result with VALU instructions needs the MFMA to have drained:
 //    call agpr_acc_ready() on the accumulator before any such read.
-__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <int DT>
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, e16x8 a, e16x8 b) {
+    if constexpr (DT == kBF16)
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Wait states after the last mfma32_agpr into `acc` before VALU reads of it
@@ -59,26 +80,32 @@ __device__ __forceinline__ void agpr_acc_ready(f32x16& acc) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
 }
 
-// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
+// Two floats -> a packed 16-bit pair, rounded to nearest even.
+template <int DT>
+__device__ __forceinline__ e16x2 cvt2(float a, float b) {
     f32x2 x = {a, b};
-    return __builtin_convertvector(x, bf16x2);
+    if constexpr (DT == kBF16)
+        return __builtin_bit_cast(e16x2, __builtin_convertvector(x, bf16x2));
+    else
+        return __builtin_bit_cast(e16x2, __builtin_convertvector(x, f16x2));
 }
 
-__device__ __forceinline__ bf16x8 cat8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
-    bf16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-    bf16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+// One 16-bit value -> fp32 (exact).
+template <int DT>
+__device__ __forceinline__ float widen(e16 x) {
+    if constexpr (DT == kBF16)
+        return __uint_as_float((unsigned)x << 16);
+    else
+        return (float)__builtin_bit_cast(_Float16, x);
+}
+
+__device__ __forceinline__ e16x8 cat8(e16x2 a, e16x2 b, e16x2 c, e16x2 d) {
+    e16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    e16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Sum of a packed bf16 pair accumulated into c in fp32 (v_dot2c_f32_bf16).
-__device__ __forceinline__ float sum_pair(bf16x2 x, float c) {
-    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(x, one, c, false);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Lanes l and l^32 exchange a value (v_permlane32_swap); returns the pair
 // (own-half copy, other-half copy) combined by `op`.
@@ -92,27 +119,28 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 }
 
 // 16-byte LDS read (ds_read_b128).
-__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
+__device__ __forceinline__ e16x8 lds_read8(const e16* p) {
+    return *reinterpret_cast<const e16x8*>(p);
 }
 
 // Transposing LDS read of 4 b16 values (see the header comment).
-__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+__device__ __forceinline__ e16x4 lds_read_tr4(const e16* p) {
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-    return __builtin_bit_cast(bf16x4, v);
+    return __builtin_bit_cast(e16x4, v);
 }
 
-__device__ __forceinline__ bf16x8 join8(bf16x4 a, bf16x4 b) {
+__device__ __forceinline__ e16x8 join8(e16x4 a, e16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// Stores four fp32 values as four bf16 (8 bytes).
-__device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float c, float d) {
-    bf16x2 lo = to_bf16x2(a, b);
-    bf16x2 hi = to_bf16x2(c, d);
-    *reinterpret_cast<bf16x4*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+// Stores four fp32 values as four 16-bit values (8 bytes).
+template <int DT>
+__device__ __forceinline__ void store4(e16* dst, float a, float b, float c, float d) {
+    e16x2 lo = cvt2<DT>(a, b);
+    e16x2 hi = cvt2<DT>(c, d);
+    *reinterpret_cast<e16x4*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
 }
 
 }  // namespace attn

@@ -14,23 +14,26 @@
 //
 // Mapping onto the CDNA4 compute unit (4 waves per workgroup, 32 query rows
 // per wave, BLOCK_KV keys per step):
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand,
-//    the wave's 32 query rows (kept in registers for the whole loop) are the
-//    B operand. The result puts one query per lane (lane % 32) and 16 keys
-//    per lane in registers, so the row maximum is a register reduction plus a
-//    single permlane32 swap, and m, l live in one lane pair.
-//  * O^T += V^T P^T: the probabilities, converted to bf16, are already laid
-//    out as the B operand (a lane holds 8 keys of its query); V^T is read as
-//    the A operand straight from the row-major V tile with the transposing
-//    LDS read. O^T keeps one query per lane, so a rescale by
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (_f16 for fp16 inputs): K (from
+//    LDS) is the A operand, the wave's 32 query rows (kept in registers for
+//    the whole loop) are the B operand. The result puts one query per lane
+//    (lane % 32) and 16 keys per lane in registers, so the row maximum is a
+//    register reduction plus a single permlane32 swap, and m, l live in one
+//    lane pair.
+//  * O^T += V^T P^T: the probabilities, rounded to the input type, are
+//    already laid out as the B operand (a lane holds 8 keys of its query);
+//    V^T is read as the A operand straight from the row-major V tile with
+//    the transposing LDS read. O^T keeps one query per lane, so a rescale by
 //    exp(m_old - m_new) needs no data movement.
 //  * Rescaling is lazy: the reference maximum only moves when a block's row
 //    maximum exceeds it by more than 2^8 (probabilities stay <= 2^8; O and l
 //    share the reference, so O / l and the LSE are unchanged). On the
 //    synthetic workloads this skips the rescale after the first block.
 //  * The row sum l is accumulated in fp32 from the unrounded probabilities
-//    (only the matrix-product operand is rounded to bf16), so LSE carries no
-//    bf16 rounding bias even for rows with few keys.
+//    (only the matrix-product operand is rounded to 16 bits), so LSE carries
+//    no rounding bias even for rows with few keys.
+//  * Operands are [B, H, N, d] views with any element strides for b, h and n
+//    (d contiguous), so BHSD and BSHD tensors are read in place.
 //  * Scores are kept in the log2 domain: exp(scale*s - m) = exp2(c*s - m')
 //    with c = scale * log2(e).
 //  * K/V tiles are double buffered in LDS: the next tile's global loads are
@@ -45,7 +48,7 @@
 
 namespace attn {
 
-template <int D, int MASK, int NW>
+template <int DT, int D, int MASK, int NW>
 __global__ __launch_bounds__(NW * 64, (D <= 128 ? 2 : 1))
 void fwd_kernel(FwdParams p) {
     constexpr int T = NW * 64;
@@ -64,7 +67,7 @@ void fwd_kernel(FwdParams p) {
     constexpr int NCH = (CHUNKS + T - 1) / T;
     constexpr int BUF = BC * (KP + VP);
 
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -82,9 +85,10 @@ void fwd_kernel(FwdParams p) {
     const int hq = bh - b * p.Hq;
     const int hkv = hq / p.G;
 
-    const bf16* Qh = static_cast<const bf16*>(p.q) + (size_t)bh * N * D;
-    const bf16* Kh = static_cast<const bf16*>(p.k) + (size_t)(b * p.Hkv + hkv) * N * D;
-    const bf16* Vh = static_cast<const bf16*>(p.v) + (size_t)(b * p.Hkv + hkv) * N * D;
+    const e16* Qh = static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h;
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
+    const long long sqn = p.sq.n, skn = p.sk.n, svn = p.sv.n;
 
     const int q0 = qb * BQ;
     const int qw0 = q0 + wave * 32;
@@ -98,19 +102,19 @@ void fwd_kernel(FwdParams p) {
             const int row = i / PADC;
             const int col = D + i % PADC;
             const int bufi = row / BC;
-            smem[bufi * BUF + BC * KP + (row % BC) * VP + col] = (bf16)0.0f;
+            smem[bufi * BUF + BC * KP + (row % BC) * VP + col] = (e16)0;
         }
     }
 
     // Q operand (B of S^T = K Q^T): lane holds query qrow, dims 16*ks + 8*h .. +7.
-    bf16x8 qf[KS];
+    e16x8 qf[KS];
     if (qrow < N) {
-        const bf16* qp = Qh + (size_t)qrow * D + h * 8;
+        const e16* qp = Qh + qrow * sqn + h * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const e16x8*>(qp + ks * 16);
     } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8{};
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = e16x8{};
     }
 
     const int nkb = (N + BC - 1) / BC;
@@ -129,8 +133,8 @@ void fwd_kernel(FwdParams p) {
                 const int col = c - row * CPR;
                 const int key = kv0 + row;
                 if (key < N) {
-                    kreg[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)key * D + col * 8);
-                    vreg[i] = *reinterpret_cast<const uint4*>(Vh + (size_t)key * D + col * 8);
+                    kreg[i] = *reinterpret_cast<const uint4*>(Kh + key * skn + col * 8);
+                    vreg[i] = *reinterpret_cast<const uint4*>(Vh + key * svn + col * 8);
                 } else {
                     kreg[i] = zero4();
                     vreg[i] = zero4();
@@ -139,8 +143,8 @@ void fwd_kernel(FwdParams p) {
         }
     };
     auto store_tile = [&](int bufi) {
-        bf16* Ks = smem + bufi * BUF;
-        bf16* Vs = Ks + BC * KP;
+        e16* Ks = smem + bufi * BUF;
+        e16* Vs = Ks + BC * KP;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * T;
@@ -176,17 +180,17 @@ void fwd_kernel(FwdParams p) {
         if (has_next) load_tile((kb + 1) * BC);
 
         const int kv0 = kb * BC;
-        const bf16* Ks = smem + bufi * BUF;
-        const bf16* Vs = Ks + BC * KP;
+        const e16* Ks = smem + bufi * BUF;
+        const e16* Vs = Ks + BC * KP;
         const bool active = !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
         if (active) {
             f32x16 s[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 s[kt] = f32x16{};
-                const bf16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
+                const e16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32(lds_read8(kp + ks * 16), qf[ks], s[kt]);
+                for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32<DT>(lds_read8(kp + ks * 16), qf[ks], s[kt]);
             }
             // Keys outside [lo, hi] (relative to kv0 + 4h) are masked: the
             // tail beyond N, keys after the row (causal) and keys before its
@@ -228,18 +232,18 @@ void fwd_kernel(FwdParams p) {
             // exp2(-inf) = 0 rather than NaN.
             const float m_new = (m == -__builtin_huge_valf()) ? 0.0f : m;
 
-            bf16x8 pb[PVS];
+            e16x8 pb[PVS];
             float lsum = 0.0f;
 #pragma unroll
             for (int u = 0; u < PVS; ++u) {
                 const int kt = u >> 1;
                 const int r0 = (u & 1) * 8;
-                bf16x2 pr[4];
+                e16x2 pr[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float a0 = fast_exp2(fmaf(s[kt][r0 + 2 * e], c, -m_new));
                     const float a1 = fast_exp2(fmaf(s[kt][r0 + 2 * e + 1], c, -m_new));
-                    pr[e] = to_bf16x2(a0, a1);
+                    pr[e] = cvt2<DT>(a0, a1);
                     lsum += a0 + a1;
                 }
                 pb[u] = cat8(pr[0], pr[1], pr[2], pr[3]);
@@ -248,11 +252,11 @@ void fwd_kernel(FwdParams p) {
 
 #pragma unroll
             for (int u = 0; u < PVS; ++u) {
-                const bf16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
+                const e16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const bf16x8 a = join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32));
-                    oacc[dt] = mfma32(a, pb[u], oacc[dt]);
+                    const e16x8 a = join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32));
+                    oacc[dt] = mfma32<DT>(a, pb[u], oacc[dt]);
                 }
             }
         }
@@ -264,39 +268,51 @@ void fwd_kernel(FwdParams p) {
     const float lt = sum_across_halves(l);
     const float inv = 1.0f / lt;
     if (qrow < N) {
-        bf16* orow = static_cast<bf16*>(p.o) + ((size_t)bh * N + qrow) * D;
+        e16* orow = static_cast<e16*>(p.o) + b * p.so.b + hq * p.so.h + qrow * p.so.n;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d = dt * 32 + g4 * 8 + h * 4;
                 if (d < D)
-                    store_bf16x4(orow + d, oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv,
+                    store4<DT>(orow + d, oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv,
                                  oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv);
             }
         if (h == 0) p.lse[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
     }
 }
 
-template <int D, int MASK>
+template <int DT, int D, int MASK>
 static hipError_t launch_fwd_dm(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
     const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
     if constexpr (D <= 128) {
         if (plan.waves == 8) {
-            hipLaunchKernelGGL((fwd_kernel<D, MASK, 8>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((fwd_kernel<D, MASK, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 4>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int DT, int D>
 static hipError_t launch_fwd_d(const FwdParams& p, int mask, const FwdPlan& plan, hipStream_t stream) {
     switch (mask) {
-        case kMaskNone: return launch_fwd_dm<D, kMaskNone>(p, plan, stream);
-        case kMaskCausal: return launch_fwd_dm<D, kMaskCausal>(p, plan, stream);
-        case kMaskWindow: return launch_fwd_dm<D, kMaskWindow>(p, plan, stream);
+        case kMaskNone: return launch_fwd_dm<DT, D, kMaskNone>(p, plan, stream);
+        case kMaskCausal: return launch_fwd_dm<DT, D, kMaskCausal>(p, plan, stream);
+        case kMaskWindow: return launch_fwd_dm<DT, D, kMaskWindow>(p, plan, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT>
+static hipError_t launch_fwd_t(const FwdParams& p, int d, int mask, const FwdPlan& plan,
+                               hipStream_t stream) {
+    switch (d) {
+#define ATTN_FWD_CASE(D_) \
+        case D_: return launch_fwd_d<DT, D_>(p, mask, plan, stream);
+        ATTN_FOR_EACH_HEAD_DIM(ATTN_FWD_CASE)
+#undef ATTN_FWD_CASE
         default: return hipErrorInvalidValue;
     }
 }
@@ -304,7 +320,7 @@ static hipError_t launch_fwd_d(const FwdParams& p, int mask, const FwdPlan& plan
 // Tile plan. 8 waves (256 rows) per workgroup share one K/V pipeline, which
 // halves global-load issue and LDS stores per row; used while that still
 // gives every CU a workgroup. Shorter sequences use 4 waves (twice the
-// workgroups); d = 256 always uses 4.
+// workgroups); d > 128 always uses 4.
 template <int D>
 static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
     const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
@@ -322,20 +338,19 @@ static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
 
 bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan) {
     switch (d) {
-        case 64: plan_d<64>(B, Hq, N, plan); return true;
-        case 80: plan_d<80>(B, Hq, N, plan); return true;
-        case 128: plan_d<128>(B, Hq, N, plan); return true;
-        case 256: plan_d<256>(B, Hq, N, plan); return true;
+#define ATTN_PLAN_CASE(D_) \
+        case D_: plan_d<D_>(B, Hq, N, plan); return true;
+        ATTN_FOR_EACH_HEAD_DIM(ATTN_PLAN_CASE)
+#undef ATTN_PLAN_CASE
         default: return false;
     }
 }
 
-hipError_t launch_fwd(const FwdParams& p, int d, int mask, const FwdPlan& plan, hipStream_t stream) {
-    switch (d) {
-        case 64: return launch_fwd_d<64>(p, mask, plan, stream);
-        case 80: return launch_fwd_d<80>(p, mask, plan, stream);
-        case 128: return launch_fwd_d<128>(p, mask, plan, stream);
-        case 256: return launch_fwd_d<256>(p, mask, plan, stream);
+hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int mask, const FwdPlan& plan,
+                      hipStream_t stream) {
+    switch (dtype) {
+        case kBF16: return launch_fwd_t<kBF16>(p, d, mask, plan, stream);
+        case kFP16: return launch_fwd_t<kFP16>(p, d, mask, plan, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -8,18 +8,21 @@
 
 namespace attn {
 
+// Head dimensions with a kernel instantiation (multiples of 16: one MFMA
+// contraction step is 16 wide).
+#define ATTN_FOR_EACH_HEAD_DIM(X) X(32) X(64) X(80) X(96) X(128) X(192) X(256)
+
 // Forward tile plan per head dimension: 32 query rows per wave, 4 or 8 waves
 // per workgroup (chosen per shape), BLOCK_KV keys per inner step. The
 // keys-per-step choice keeps two waves per SIMD (LDS double buffer +
-// registers) for d <= 128; d = 256 halves it to keep the accumulator and Q
+// registers) for d <= 128; d > 128 halves it to keep the accumulator and Q
 // operand in registers.
-template <int D> struct FwdTile;
-template <> struct FwdTile<64>  { static constexpr int BLOCK_KV = 64; };
-template <> struct FwdTile<80>  { static constexpr int BLOCK_KV = 64; };
-template <> struct FwdTile<128> { static constexpr int BLOCK_KV = 64; };
-template <> struct FwdTile<256> { static constexpr int BLOCK_KV = 32; };
+template <int D> struct FwdTile {
+    static_assert(D % 16 == 0 && D >= 32 && D <= 256, "unsupported head dimension");
+    static constexpr int BLOCK_KV = D <= 128 ? 64 : 32;
+};
 
-// Row pitches (in bf16 elements) of the LDS tiles. gfx950's LDS serves
+// Row pitches (in 16-bit elements) of the LDS tiles. gfx950's LDS serves
 // 64 banks x 4 bytes, i.e. 256 bytes per cycle; measured on the part:
 //  * 16-byte row reads (lane i reads row i, same column; the S = K Q^T and
 //    dP operands) reach their conflict floor when the pitch is an odd
@@ -49,12 +52,19 @@ __host__ __device__ constexpr int sw_off(int row, int col, int pitch) {
 // the causal sliding window (keys i - window < j <= i).
 enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
 
+// Element strides of one [B, H, N, d] operand (d itself is contiguous):
+// element (b, h, n, e) sits at base + b*b_ + h*h_ + n*n_ + e.
+struct Strides {
+    long long b, h, n;
+};
+
 struct FwdParams {
     const void* q;
     const void* k;
     const void* v;
     void* o;
-    float* lse;
+    float* lse;    // [B, Hq, N], contiguous
+    Strides sq, sk, sv, so;
     int N;
     int Hq;
     int Hkv;
@@ -76,6 +86,7 @@ struct BwdParams {
     void* dk;
     void* dv;
     float* delta;  // [B, Hq, N] workspace: D_i = <dO_i, O_i>
+    Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     int N;
     int Hq;
     int Hkv;
@@ -99,11 +110,13 @@ struct FwdPlan {
 bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan);
 
 // Launchers return the hipError_t of the launch.
-hipError_t launch_fwd(const FwdParams& p, int d, int mask, const FwdPlan& plan,
+// dtype: 0 = bf16, 1 = fp16 (the kernels' DType).
+hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int mask, const FwdPlan& plan,
                       hipStream_t stream);
 // Backward passes: bit 0 = row-term preprocess, bit 1 = dK/dV, bit 2 = dQ.
 enum BwdPass { kBwdPre = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7 };
-hipError_t launch_bwd(const BwdParams& p, int d, int mask, int passes, hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdParams& p, int d, int mask, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, int mask, int passes,
+                      hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int d, int mask, hipStream_t stream);
 
 }  // namespace attn

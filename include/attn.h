@@ -28,9 +28,14 @@
  * Conventions shared by every entry point
  *   Layout: contiguous [B, H, N, d], d innermost ("BHSD"). q, o, dout, dq are
  *     [B, Hq, N, d]; k, v, dk, dv are [B, Hkv, N, d]; lse is [B, Hq, N].
- *     Self-attention: queries and keys have the same length N.
- *   Types: q, k, v, o, dout, dq, dk, dv are bfloat16 (passed as void*);
- *     lse is float32; all accumulation is float32.
+ *     Self-attention: queries and keys have the same length N. The *_ex
+ *     entry points take each operand as a strided view instead (attn_tensor),
+ *     which covers BSHD ([B, N, H, d], the layout flash_attn_func takes on the
+ *     yunthe.com GQA page) and sub-views of larger buffers.
+ *   Types: q, k, v, o, dout, dq, dk, dv are bfloat16 (passed as void*), or
+ *     float16 through the *_ex entry points ("FlashAttention in CANN
+ *     ops-transformer on the Ascend NPU", tuning section on data types); lse
+ *     is float32; all accumulation is float32.
  *   GQA: Hq must be a multiple of Hkv; query head h uses KV head
  *     h / (Hq / Hkv) (consecutive groups). Hkv == Hq is MHA, Hkv == 1 is MQA.
  *   Causal (causal != 0): query i attends to keys j <= i; otherwise to all j.
@@ -67,16 +72,21 @@ typedef enum attn_status {
     ATTN_ERR_NULL = 1,       /* a required pointer is NULL */
     ATTN_ERR_SHAPE = 2,      /* B, Hq, Hkv or N < 1, or a size overflows */
     ATTN_ERR_GQA = 3,        /* Hq is not a multiple of Hkv */
-    ATTN_ERR_HEAD_DIM = 4,   /* d is not one of 64, 80, 128, 256 */
+    ATTN_ERR_HEAD_DIM = 4,   /* d is not one of 32, 64, 80, 96, 128, 192, 256 */
     ATTN_ERR_SCALE = 5,      /* scale is not finite or not > 0 */
-    ATTN_ERR_ALIGN = 6,      /* a pointer is not 16-byte aligned */
+    ATTN_ERR_ALIGN = 6,      /* a pointer is not 16-byte aligned, or a stride is not a
+                                multiple of 8 elements */
     ATTN_ERR_WORKSPACE = 7,  /* workspace NULL or smaller than required */
     ATTN_ERR_HIP = 8,        /* the HIP runtime refused a launch */
-    ATTN_ERR_WINDOW = 9      /* window < 0, or a window (>= 1) without the causal mask */
+    ATTN_ERR_WINDOW = 9,     /* unknown mask kind, window < 0, or a window (>= 1)
+                                without the causal mask */
+    ATTN_ERR_STRIDE = 10,    /* a stride is negative */
+    ATTN_ERR_DTYPE = 11,     /* unknown element type */
+    ATTN_ERR_PASSES = 12     /* passes is 0 or has bits other than ATTN_BWD_ALL */
 } attn_status;
 
-/* Head dimensions with a specialised kernel. */
-#define ATTN_NUM_HEAD_DIMS 4
+/* Head dimensions with a specialised kernel: 32, 64, 80, 96, 128, 192, 256. */
+#define ATTN_NUM_HEAD_DIMS 7
 #define ATTN_MAX_SEQ_LEN (1 << 24)
 
 /*
@@ -165,6 +175,70 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float
                         const void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                         int window, void* stream);
+
+/*
+ * Strided, typed interface. The entry points above are the special case
+ * problem = {B, Hq, Hkv, N, d, scale, causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE,
+ * 0, ATTN_DTYPE_BF16} with contiguous BHSD tensors.
+ */
+typedef enum attn_dtype {
+    ATTN_DTYPE_BF16 = 0,
+    ATTN_DTYPE_FP16 = 1
+} attn_dtype;
+
+typedef enum attn_mask_kind {
+    ATTN_MASK_NONE = 0,           /* every key */
+    ATTN_MASK_CAUSAL = 1,         /* keys j <= i */
+    ATTN_MASK_SLIDING_WINDOW = 2  /* keys i - window < j <= i */
+} attn_mask_kind;
+
+/*
+ * One [B, H, N, d] operand in device memory: element (b, h, n, e) is at
+ * data + b*stride_b + h*stride_h + n*stride_n + e, strides counted in
+ * elements, the d elements of a row contiguous. Strides must be >= 0 and
+ * multiples of 8 (every row starts 16-byte aligned), data 16-byte aligned.
+ *   contiguous BHSD: stride_b = H*N*d, stride_h = N*d, stride_n = d
+ *   contiguous BSHD: stride_b = N*H*d, stride_h = d,   stride_n = H*d
+ * Output views must not overlap each other or the inputs.
+ */
+typedef struct attn_tensor {
+    void* data;
+    long long stride_b;
+    long long stride_h;
+    long long stride_n;
+} attn_tensor;
+
+typedef struct attn_problem {
+    int B, Hq, Hkv, N, d;
+    float scale;
+    int mask;    /* attn_mask_kind */
+    int window;  /* W >= 1 with ATTN_MASK_SLIDING_WINDOW, 0 otherwise */
+    int dtype;   /* attn_dtype of q, k, v, o, dout, dq, dk, dv */
+} attn_problem;
+
+/*
+ * Forward pass of `problem` (q, o: H = Hq; k, v: H = Hkv). lse is contiguous
+ * [B, Hq, N] float32. Returns ATTN_OK or an error code with nothing enqueued.
+ */
+attn_status attn_fwd_ex(const attn_problem* problem, const attn_tensor* q, const attn_tensor* k,
+                        const attn_tensor* v, const attn_tensor* o, float* lse, void* stream);
+
+/*
+ * Backward pass of `problem`: the passes selected by the bits of `passes`
+ * (ATTN_BWD_PREPROCESS, ATTN_BWD_DKDV, ATTN_BWD_DQ; ATTN_BWD_ALL for the
+ * whole backward), in that order. A tensor no selected pass touches may be
+ * passed as NULL; workspace as for attn_bwd (attn_bwd_workspace_bytes); the
+ * dK/dV and dQ passes read the D_i the preprocess wrote into it.
+ */
+#define ATTN_BWD_PREPROCESS 1u
+#define ATTN_BWD_DKDV 2u
+#define ATTN_BWD_DQ 4u
+#define ATTN_BWD_ALL 7u
+attn_status attn_bwd_ex(const attn_problem* problem, const attn_tensor* q, const attn_tensor* k,
+                        const attn_tensor* v, const attn_tensor* o, const float* lse,
+                        const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
+                        const attn_tensor* dv, void* workspace, size_t workspace_bytes,
+                        unsigned passes, void* stream);
 
 /* Static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);

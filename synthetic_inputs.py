@@ -6,7 +6,9 @@ tensors from here.
 
 Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws Q, K, V
 and then dO, in that order, as float32 standard normals, each rounded to
-bfloat16 (round to nearest even). Layout is contiguous [B, H, N, d].
+bfloat16 (or float16 for fp16 workloads; round to nearest even). Tensors are
+returned as contiguous [B, H, N, d]; a BSHD workload hands the same values to
+the kernels as contiguous [B, N, H, d].
 """
 
 from __future__ import annotations
@@ -30,6 +32,8 @@ class Workload:
     seed: int
     note: str = field(default="", compare=False)
     window: int | None = None  # sliding window W (keys i-W < j <= i); implies causal
+    dtype: str = "bf16"        # "bf16" or "fp16"
+    layout: str = "bhsd"       # "bhsd" or "bshd"
 
     @property
     def scale(self) -> float:
@@ -76,8 +80,9 @@ class Workload:
         return 3 * q + 2 * kv + rows + (q + 2 * kv) + 3 * rows
 
 
-def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note="", window=None):
-    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window)
+def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note="", window=None, dtype="bf16",
+       layout="bhsd"):
+    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window, dtype, layout)
 
 
 # The five workload families (index k gives seed 1000 + k; the sequence sweep
@@ -103,29 +108,45 @@ WORKLOADS = {
         # mask modes): 16K tokens, a 4096-key band, GQA G=4, fwd+bwd.
         _w("c6_window_d128", 1, 32, 8, 16384, 128, True, True, 1006,
            "fwd+bwd, sliding window 4096, GQA G=4", window=4096),
+        # fp16 operands in the [batch, seq, heads, dim] layout (CANN
+        # FlashAttention page, tuning section on data types; yunthe.com GQA
+        # page, flash_attn_func call): the C5 shape, so the two compare.
+        _w("c7_fp16_bshd_d128", 1, 16, 16, 16384, 128, True, True, 1007,
+           "fwd+bwd, fp16, BSHD", dtype="fp16", layout="bshd"),
     ]
 }
 
 
-def make_inputs(B, Hq, Hkv, N, d, seed, with_do=False):
-    """Draw bf16 Q [B,Hq,N,d], K, V [B,Hkv,N,d] (and dO like Q) on the CPU."""
+TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def make_inputs(B, Hq, Hkv, N, d, seed, with_do=False, dtype="bf16"):
+    """Draw Q [B,Hq,N,d], K, V [B,Hkv,N,d] (and dO like Q) on the CPU, in
+    bf16 or fp16."""
+    t = TORCH_DTYPES[dtype]
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(t)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32).to(t)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32).to(t)
     out = {"q": q, "k": k, "v": v}
     if with_do:
-        out["do"] = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+        out["do"] = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(t)
     return out
 
 
 def workload_inputs(w: Workload):
-    return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, with_do=w.backward)
+    return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, with_do=w.backward, dtype=w.dtype)
+
+
+def in_layout(t: torch.Tensor, layout: str) -> torch.Tensor:
+    """A contiguous copy of a [B, H, N, d] tensor in `layout` ("bhsd" returns
+    it unchanged, "bshd" gives [B, N, H, d])."""
+    return t if layout == "bhsd" else t.transpose(1, 2).contiguous()
 
 
 def to_f64(t: torch.Tensor):
-    """Exact float64 numpy copy of a (bf16) CPU or GPU tensor."""
+    """Exact float64 numpy copy of a (bf16 / fp16) CPU or GPU tensor."""
     return t.detach().to("cpu", torch.float64).numpy()
 
 

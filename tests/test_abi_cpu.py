@@ -5,6 +5,7 @@ import ctypes
 import math
 
 import pytest
+import torch
 
 import exact_attention_12_amd as ea
 from exact_attention_12_amd import build as ea_build
@@ -19,6 +20,11 @@ def L():
 
 
 P = 0x10000  # fake, aligned, never dereferenced: validation fails before any device call
+
+# Every call here must fail validation; should one pass by mistake it would
+# launch kernels on the fake pointers, so the module never runs next to a GPU.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only checks with fake device pointers")
 
 
 def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125, causal=0):
@@ -40,7 +46,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for code in range(10):
+    for code in range(13):
         s = ea.status_string(code)
         assert s and s != "unknown status"
     assert ea.status_string(99) == "unknown status"
@@ -65,7 +71,7 @@ def test_fwd_bad_grouping(L, Hq, Hkv):
     assert fwd(L, Hq=Hq, Hkv=Hkv) == 3
 
 
-@pytest.mark.parametrize("d", [0, 32, 63, 96, 112, 160, 192, 512])
+@pytest.mark.parametrize("d", [0, 16, 48, 63, 100, 112, 160, 224, 320, 512])
 def test_fwd_unsupported_head_dim(L, d):
     """Unsupported head dims are rejected with an error rather than served by a
     slower generic path (datacanvas head-dim article: the symptoms section)."""
@@ -96,7 +102,7 @@ def test_bwd_errors(L):
         ptrs[i] = P + 4
         assert bwd(L, ptrs=ptrs) == 6
     assert bwd(L, ws=P + 8) == 6
-    assert bwd(L, d=96) == 4
+    assert bwd(L, d=112) == 4
     assert bwd(L, Hq=3, Hkv=2) == 3
     assert bwd(L, scale=float("nan")) == 5
     assert bwd(L, N=0) == 2
@@ -107,7 +113,7 @@ def test_workspace_bytes(L):
     assert L.attn_bwd_workspace_bytes(1, 1, 1, 1, 64) == 256
     assert L.attn_bwd_workspace_bytes(2, 3, 1, 100, 80) == 2560  # 2400 rounded up to 256
     assert L.attn_bwd_workspace_bytes(1, 3, 2, 100, 80) == 0
-    assert L.attn_bwd_workspace_bytes(1, 2, 2, 100, 96) == 0
+    assert L.attn_bwd_workspace_bytes(1, 2, 2, 100, 112) == 0
 
 
 def test_fwd_plan(L):
@@ -120,7 +126,7 @@ def test_fwd_plan(L):
         assert q["workgroups"] == 2 * 32 * 4096 // q["block_q"]
         assert q["lds_bytes"] <= 160 * 1024 // (1 if d == 256 else 2)
     with pytest.raises(ea.AttnError) as e:
-        ea.fwd_plan(1, 8, 8, 400, 96)
+        ea.fwd_plan(1, 8, 8, 400, 112)
     assert e.value.name == "ATTN_ERR_HEAD_DIM"
 
 
@@ -132,7 +138,7 @@ def test_pass_entry_points_validate(L):
     assert L.attn_bwd_preprocess(P, P, None, wsb, 1, 2, 1, 8, 64, None) == 7
     assert L.attn_bwd_preprocess(P, P + 2, ws, wsb, 1, 2, 1, 8, 64, None) == 6
     assert L.attn_bwd_preprocess(P, P, ws, 4, 1, 2, 1, 8, 64, None) == 7
-    assert L.attn_bwd_preprocess(P, P, ws, wsb, 1, 2, 1, 8, 96, None) == 4
+    assert L.attn_bwd_preprocess(P, P, ws, wsb, 1, 2, 1, 8, 112, None) == 4
     # dK/dV pass: q, k, v, lse, dout, dk, dv, workspace
     for i in range(7):
         a = [P] * 7
@@ -161,7 +167,7 @@ def test_window_validation(L):
     assert L.attn_fwd_window(None, *[P] * 4, 1, 2, 1, 8, 64, 0.125, 0, None) == 9
     # valid windows still get the ordinary checks
     assert L.attn_fwd_window(None, *[P] * 4, 1, 2, 1, 8, 64, 0.125, 3, None) == 1
-    assert L.attn_fwd_window(*[P] * 5, 1, 2, 1, 8, 96, 0.125, 3, None) == 4
+    assert L.attn_fwd_window(*[P] * 5, 1, 2, 1, 8, 48, 0.125, 3, None) == 4
     assert L.attn_fwd_window(*[P] * 4, P + 2, 1, 2, 1, 8, 64, 0.125, 1 << 30, None) == 6
     assert L.attn_bwd_window(*[P] * 10, 16, 1, 2, 1, 8, 64, 0.125, 4, None) == 7
     assert L.attn_bwd_window(*[P] * 10, 1 << 20, 1, 2, 1, 8, 64, float("inf"), 4, None) == 5
@@ -171,3 +177,93 @@ def test_window_validation(L):
     assert L.attn_bwd_dkdv(*[P] * 7, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, -1, None) == 9
     assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 8, 64, 0.125, 0, 2, None) == 9
     assert L.attn_bwd_dq(*[P] * 6, ws, wsb, 1, 2, 1, 8, 64, 0.125, 1, -3, None) == 9
+
+
+# ------------------------------------------------------------ strided/typed ABI
+
+def T(data=P, sb=1 << 12, sh=1 << 10, sn=64):
+    return ea.AttnTensor(data, sb, sh, sn)
+
+
+def prob(**kw):
+    base = dict(B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125, mask=ea.MASK_CAUSAL, window=0,
+                dtype=ea.DTYPE_BF16)
+    base.update(kw)
+    return ea.AttnProblem(*[base[f] for f, _ in ea.AttnProblem._fields_])
+
+
+def fwd_ex(L, pr=None, ts=None, lse=P):
+    ts = ts or [T() for _ in range(4)]
+    return L.attn_fwd_ex(ctypes.byref(pr or prob()), *[ctypes.byref(t) if t is not None else None
+                                                       for t in ts], lse, None)
+
+
+def bwd_ex(L, pr=None, ts=None, lse=P, ws=P, wsb=1 << 20, passes=7):
+    ts = ts if ts is not None else [T() for _ in range(8)]
+    r = [ctypes.byref(t) if t is not None else None for t in ts]
+    return L.attn_bwd_ex(ctypes.byref(pr or prob()), *r[:4], lse, *r[4:], ws, wsb, passes, None)
+
+
+def test_ex_validation(L):
+    assert L.attn_fwd_ex(None, *[ctypes.byref(T())] * 4, P, None) == 1
+    for i in range(4):
+        ts = [T() for _ in range(4)]
+        ts[i] = None
+        assert fwd_ex(L, ts=ts) == 1
+        ts[i] = T(data=None)
+        assert fwd_ex(L, ts=ts) == 1
+        ts[i] = T(sn=-64)
+        assert fwd_ex(L, ts=ts) == 10
+        ts[i] = T(sn=60)
+        assert fwd_ex(L, ts=ts) == 6
+        ts[i] = T(sh=1 << 10 | 4)
+        assert fwd_ex(L, ts=ts) == 6
+        ts[i] = T(data=P + 8)
+        assert fwd_ex(L, ts=ts) == 6
+    assert fwd_ex(L, lse=None) == 1
+    assert fwd_ex(L, lse=P + 4) == 6
+    assert fwd_ex(L, pr=prob(dtype=2)) == 11
+    assert fwd_ex(L, pr=prob(dtype=-1)) == 11
+    assert fwd_ex(L, pr=prob(mask=3)) == 9
+    assert fwd_ex(L, pr=prob(mask=ea.MASK_CAUSAL, window=4)) == 9
+    assert fwd_ex(L, pr=prob(mask=ea.MASK_SLIDING_WINDOW, window=0)) == 9
+    assert fwd_ex(L, pr=prob(d=112)) == 4
+    assert fwd_ex(L, pr=prob(Hq=3, Hkv=2)) == 3
+    assert fwd_ex(L, pr=prob(scale=0.0)) == 5
+    assert fwd_ex(L, pr=prob(N=0)) == 2
+    # shape errors win over stride errors, which win over alignment
+    assert fwd_ex(L, pr=prob(N=0), ts=[T(sn=-8)] * 4) == 2
+    assert fwd_ex(L, ts=[T(sn=-8), T(data=P + 2), T(), T()]) == 10
+
+
+def test_bwd_ex_validation(L):
+    assert bwd_ex(L, passes=0) == 12
+    assert bwd_ex(L, passes=8) == 12
+    assert bwd_ex(L, passes=15) == 12
+    # order: dout, o (pre), q, k, v (main), dq, dk, dv; unused tensors may be NULL
+    names = ["q", "k", "v", "o", "dout", "dq", "dk", "dv"]
+    uses = {1: {"o", "dout"}, 2: {"q", "k", "v", "dout", "dk", "dv"}, 4: {"q", "k", "v", "dout", "dq"}}
+    for bits, used in uses.items():
+        for i, n in enumerate(names):
+            ts = [T() for _ in range(8)]
+            ts[i] = None
+            r = bwd_ex(L, ts=ts, passes=bits, ws=None)
+            assert r == (1 if n in used else 7), (bits, n, r)
+            if n in used:
+                ts[i] = T(sn=12)
+                assert bwd_ex(L, ts=ts, passes=bits) == 6, (bits, n)
+    assert bwd_ex(L, lse=None, passes=2) == 1
+    assert bwd_ex(L, lse=None, passes=1, ws=None) == 7   # preprocess needs no lse
+    assert bwd_ex(L, wsb=16) == 7
+    assert bwd_ex(L, ws=P + 8) == 6
+    assert bwd_ex(L, pr=prob(dtype=5)) == 11
+    assert bwd_ex(L, pr=prob(mask=ea.MASK_NONE, window=3)) == 9
+    assert bwd_ex(L, pr=prob(mask=ea.MASK_NONE, window=3), passes=1, ws=None) == 7  # no mask in pre
+    assert bwd_ex(L, pr=prob(d=100)) == 4
+
+
+def test_head_dims_have_plans(L):
+    for d in ea.SUPPORTED_HEAD_DIMS:
+        p = ea.fwd_plan(1, 4, 4, 1000, d)
+        assert p["lds_bytes"] <= 160 * 1024 // (2 if d <= 128 else 1)
+        assert p["block_kv"] == (64 if d <= 128 else 32)

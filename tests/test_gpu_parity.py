@@ -1,7 +1,8 @@
 """HIP path vs the fp64 oracle on seeded inputs (needs an MI355X).
 
-Small shapes run through every head dimension, both mask modes, ragged
-lengths (not multiples of the tiles) and GQA group sizes 1, 2, 8 and Hq.
+Small shapes run through every head dimension (32, 64, 80, 96, 128, 192,
+256), both mask modes, ragged lengths (not multiples of the tiles) and GQA
+group sizes 1, 2, 3, 4, 8 and Hq.
 Full workload shapes are checked on sampled heads (and, for the backward,
 sampled KV-head groups), which the oracle computes exactly."""
 
@@ -31,6 +32,12 @@ SMALL = [
     (1, 2, 1, 300, 64, True),
     (1, 2, 2, 333, 80, True),
     (1, 2, 2, 190, 128, False),
+    (1, 4, 2, 200, 32, True),
+    (2, 2, 1, 97, 32, False),
+    (1, 4, 1, 300, 96, True),
+    (1, 2, 2, 130, 96, False),
+    (1, 2, 1, 260, 192, True),
+    (1, 2, 2, 70, 192, False),
 ]
 
 
@@ -87,7 +94,7 @@ def test_deterministic():
 
 
 def test_errors_raise_through_binding():
-    q = torch.zeros((1, 2, 8, 96), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 2, 8, 112), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ea.AttnError) as e:
         ea.fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous())
     assert e.value.name == "ATTN_ERR_HEAD_DIM"

@@ -22,11 +22,13 @@ FWD_HEADS = {
     "c5_bwd_d128": [(0, 0), (0, 15)],
     "c5_bwd_d80": [(0, 0), (0, 5), (0, 15)],
     "c6_window_d128": [(0, 0), (0, 31)],
+    "c7_fp16_bshd_d128": [(0, 0), (0, 15)],
 }
 BWD_KV_HEADS = {
     "c5_bwd_d128": [(0, 3)],
     "c5_bwd_d80": [(0, 0), (0, 15)],
     "c6_window_d128": [(0, 5)],
+    "c7_fp16_bshd_d128": [(0, 7)],
 }
 
 
@@ -40,16 +42,21 @@ def _gpu():
 @pytest.mark.parametrize("name", list(FWD_HEADS))
 def test_workload(name):
     w = si.WORKLOADS[name]
-    parity.log(f"workload {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.mask}")
+    parity.log(f"workload {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} {w.mask} "
+               f"{w.dtype} {w.layout}")
     inp = si.workload_inputs(w)
-    g = parity.to_gpu(inp)
-    o, lse = ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window)
+    g = {key: si.in_layout(t.cuda(), w.layout) for key, t in inp.items()}
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
+                    layout=w.layout)
     torch.cuda.synchronize()
+    if w.layout == "bshd":  # back to [B, H, N, d] for the checks
+        o = o.transpose(1, 2)
+        g = {key: t.transpose(1, 2) for key, t in g.items()}
     heads = FWD_HEADS[name] or [(b, h) for b in range(w.B) for h in range(w.Hq)]
     parity.check_fwd(inp, o, lse, w.scale, w.causal, heads, name, window=w.window)
     if w.backward:
         grads = ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal,
-                       window=w.window)
+                       window=w.window)  # BHSD views of the same memory
         torch.cuda.synchronize()
         parity.check_bwd(inp, grads, w.scale, w.causal, BWD_KV_HEADS[name], w.Hq, w.Hkv, name,
                          window=w.window)
