@@ -16,7 +16,8 @@ Sources (pages are cited by title and section):
   FlashAttention-2 style kernel: section 2.2 (online softmax is exact),
   section 2.3 (backward recomputes S and P), section 3.2 (Q-block loop).
 * [FA-GQA] "Transformer高效注意力机制实现：Flash Attention与GQA原理对比与代码实践"
-  (yunthe.com): the MHA class and the GQA class (repeat_interleave of K, V).
+  (yunthe.com): the MHA class and the GQA class (repeat_interleave of K, V);
+  its KV-cache discussion motivates the decode reference (``ref_decode``).
 
 Every function here is pinned by CPU tests in ``tests/test_oracle_*.py``
 (brute force, hand-worked closed forms, invariants, finite differences).
@@ -30,4 +31,5 @@ from .attention import (  # noqa: F401
     blockwise_online_fwd,
     kv_head_of,
     allowed_mask,
+    ref_decode,
 )

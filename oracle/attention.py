@@ -27,6 +27,7 @@ __all__ = [
     "ref_bwd_group",
     "ref_bwd",
     "blockwise_online_fwd",
+    "ref_decode",
 ]
 
 DEFAULT_CHUNK = 1024
@@ -269,3 +270,45 @@ def blockwise_online_fwd(q, k, v, scale, causal=False, block_r=64, block_c=64, w
         O = np.where(l[:, None] > 0, O / l[:, None], 0.0)
         lse = np.where(l > 0, m + np.log(l), -np.inf)
     return O, lse
+
+
+def ref_decode(q, k, v, scale, causal=False, kv_lens=None, window=None):
+    """Attention of Nq new queries per sequence against a key/value cache.
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] caches whose first L_b rows are
+    valid, L_b = kv_lens[b] clamped to [0, Nk] (all Nk rows when kv_lens is
+    None). Returns (O [B, Hq, Nq, d], LSE [B, Hq, Nq]) in float64.
+
+    The pages describe decoding only through the KV cache that GQA shrinks
+    ([FA-GQA], sections on the KV cache of MHA and on GQA); they fix no
+    alignment between the new queries and the cached keys. The reading taken:
+    the cache already holds the keys of the new tokens, so query i sits at
+    position p_i = L_b - Nq + i, and its allowed keys are the A_i of a
+    sequence of length L_b at row p_i (all j < L_b; j <= p_i under the causal
+    mask; p_i - W < j <= p_i under a window of W). Decoding is then exactly
+    the last Nq rows of self-attention over the L_b cached positions. A query
+    with no allowed key (p_i < 0, i.e. L_b < Nq, under a causal mask; or an
+    empty cache) gets O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d]")
+    B, Hq, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    O = np.zeros((B, Hq, Nq, d))
+    LSE = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        L = Nk if kv_lens is None else int(min(max(int(kv_lens[b]), 0), Nk))
+        if L == 0:
+            continue
+        for hq in range(Hq):
+            hkv = kv_head_of(hq, Hq, Hkv)
+            o, lse = ref_fwd_head(q[b, hq], k[b, hkv, :L], v[b, hkv, :L], scale, causal,
+                                  row0=L - Nq, window=window)
+            O[b, hq] = o
+            LSE[b, hq] = lse
+    return O, LSE

@@ -102,6 +102,8 @@ WORKLOADS = {
         _w("c3_causal_7b", 2, 32, 32, 4096, 128, True, False, 1003, "7B-like"),
         _w("c4_gqa_70b", 1, 64, 8, 8192, 128, True, False, 1004, "70B-like GQA, G=8"),
         _w("c4_mqa_70b", 1, 64, 1, 8192, 128, True, False, 1004, "MQA, G=64"),
+        _w("c4_gqa_70b_bwd", 1, 64, 8, 8192, 128, True, True, 1004,
+           "70B-like GQA, G=8, fwd+bwd (dK/dV summed over the group)"),
         _w("c5_bwd_d128", 1, 16, 16, 16384, 128, True, True, 1005, "fwd+bwd"),
         _w("c5_bwd_d80", 1, 16, 16, 4096, 80, True, True, 1005, "fwd+bwd, d=80"),
         # Long-text case for the sliding-window mask (CANN FlashAttention page,

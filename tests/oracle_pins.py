@@ -406,3 +406,107 @@ def check_window_gradients(fwd_w, bwd_w):
         assert np.linalg.norm(num - grad) / np.linalg.norm(grad) < 1e-7
     np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-12)
     np.testing.assert_allclose(dV.sum(axis=2), do.sum(axis=(1, 2))[:, None], atol=1e-12)
+
+
+# ------------------------------------------------------------------- decoding
+
+def brute_force_decode(q, k, v, scale, causal, kv_lens, window=None):
+    """Scalar loops: query i of sequence b at position L_b - Nq + i, keys
+    j < L_b, the causal / window tests written out per pair, e^x / sum e^x
+    with no max subtraction; a query with no key gets O = 0, LSE = -inf."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, Nq, d))
+    L = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        Lb = min(max(int(kv_lens[b]), 0), Nk)
+        for h in range(Hq):
+            kv = h // G
+            for i in range(Nq):
+                pos = Lb - Nq + i
+                w = []
+                for j in range(Lb):
+                    ok = True
+                    if (causal or window) and j > pos:
+                        ok = False
+                    if window and j <= pos - window:
+                        ok = False
+                    if ok:
+                        s = sum(float(q[b, h, i, c]) * float(k[b, kv, j, c]) for c in range(d))
+                        w.append((j, math.exp(scale * s)))
+                if not w:
+                    continue
+                den = math.fsum(x for _, x in w)
+                L[b, h, i] = math.log(den)
+                for c in range(d):
+                    O[b, h, i, c] = math.fsum(x * float(v[b, kv, j, c]) for j, x in w) / den
+    return O, L
+
+
+def check_decode_brute_force(dec, seed, causal, window=None):
+    r = np.random.default_rng(seed)
+    B, Hq, Hkv, Nq, Nk, d = 3, 4, 2, 3, 9, 5
+    q = r.standard_normal((B, Hq, Nq, d))
+    k = r.standard_normal((B, Hkv, Nk, d))
+    v = r.standard_normal((B, Hkv, Nk, d))
+    lens = [9, 5, 2]  # full cache, partly filled, shorter than Nq
+    O, L = dec(q, k, v, 0.6, causal, lens, window)
+    Ob, Lb = brute_force_decode(q, k, v, 0.6, causal, lens, window)
+    np.testing.assert_allclose(O, Ob, rtol=RTOL_EXACT, atol=1e-13)
+    np.testing.assert_array_equal(np.isfinite(L), np.isfinite(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[fin], Lb[fin], rtol=RTOL_EXACT, atol=1e-13)
+
+
+def check_decode_is_last_rows(dec, fwd_full, causal, window=None):
+    """Decoding the last Nq tokens of a sequence gives the last Nq rows of
+    self-attention over it (the alignment rule), for every mask kind."""
+    r = np.random.default_rng(31)
+    B, Hq, Hkv, N, d, Nq = 2, 4, 2, 11, 6, 4
+    Q = r.standard_normal((B, Hq, N, d))
+    K = r.standard_normal((B, Hkv, N, d))
+    V = r.standard_normal((B, Hkv, N, d))
+    O, L = fwd_full(Q, K, V, 0.8, causal, window)
+    Od, Ld = dec(Q[:, :, N - Nq:], K, V, 0.8, causal, None, window)
+    np.testing.assert_allclose(Od, O[:, :, N - Nq:], rtol=RTOL_EXACT, atol=1e-13)
+    np.testing.assert_allclose(Ld, L[:, :, N - Nq:], rtol=RTOL_EXACT, atol=1e-13)
+    # per-sequence lengths: a cache padded with junk beyond L_b changes nothing
+    pad = r.standard_normal((B, Hkv, 5, d)) * 1e3
+    Kp = np.concatenate([K, pad], axis=2)
+    Vp = np.concatenate([V, pad], axis=2)
+    Od2, Ld2 = dec(Q[:, :, N - Nq:], Kp, Vp, 0.8, causal, [N, N], window)
+    np.testing.assert_allclose(Od2, Od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Ld2, Ld, rtol=0, atol=1e-13)
+
+
+def check_decode_special_cases(dec):
+    """One new token sees the whole cache under either mask; an empty cache or
+    a query before the first cached position sees nothing."""
+    r = np.random.default_rng(33)
+    q = r.standard_normal((2, 2, 1, 4))
+    k = r.standard_normal((2, 1, 6, 4))
+    v = r.standard_normal((2, 1, 6, 4))
+    a = dec(q, k, v, 0.5, False, [6, 3], None)
+    c = dec(q, k, v, 0.5, True, [6, 3], None)
+    np.testing.assert_allclose(a[0], c[0], atol=1e-15)
+    np.testing.assert_allclose(a[1], c[1], atol=1e-15)
+    # Q = 0: O is the mean of the visible values, LSE = ln(count)
+    z = np.zeros_like(q)
+    O, L = dec(z, k, v, 0.5, True, [6, 3], 4)
+    np.testing.assert_allclose(O[0, :, 0], np.repeat(v[0, :, 2:6].mean(axis=1), 2, axis=0), atol=1e-14)
+    np.testing.assert_allclose(L[0], np.log(4), atol=1e-14)
+    np.testing.assert_allclose(O[1, :, 0], np.repeat(v[1, :, 0:3].mean(axis=1), 2, axis=0), atol=1e-14)
+    np.testing.assert_allclose(L[1], np.log(3), atol=1e-14)
+    O, L = dec(q, k, v, 0.5, True, [0, 7], None)  # empty cache; length clamped to Nk
+    assert np.all(O[0] == 0) and np.all(np.isneginf(L[0]))
+    O6, L6 = dec(q, k, v, 0.5, True, [6, 6], None)
+    np.testing.assert_allclose(O[1], O6[1], atol=0)
+    q3 = r.standard_normal((1, 1, 3, 4))
+    O8, L8 = dec(q3, k[:1], v[:1], 0.5, True, [8], None)  # 8 > Nk = 6 is clamped to 6
+    O6, L6 = dec(q3, k[:1], v[:1], 0.5, True, [6], None)
+    np.testing.assert_allclose(O8, O6, atol=0)
+    np.testing.assert_allclose(L8, L6, atol=0)
+    O, L = dec(q3, k[:1], v[:1], 0.5, True, [2], None)  # L_b = 2 < Nq = 3
+    assert np.all(O[0, 0, 0] == 0) and np.isneginf(L[0, 0, 0])
+    assert np.all(np.isfinite(L[0, 0, 1:]))

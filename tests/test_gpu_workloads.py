@@ -19,12 +19,14 @@ FWD_HEADS = {
     "c3_causal_7b": [(0, 0), (1, 31)],
     "c4_gqa_70b": [(0, 0), (0, 9), (0, 63)],
     "c4_mqa_70b": [(0, 0), (0, 63)],
+    "c4_gqa_70b_bwd": [(0, 5), (0, 60)],
     "c5_bwd_d128": [(0, 0), (0, 15)],
     "c5_bwd_d80": [(0, 0), (0, 5), (0, 15)],
     "c6_window_d128": [(0, 0), (0, 31)],
     "c7_fp16_bshd_d128": [(0, 0), (0, 15)],
 }
 BWD_KV_HEADS = {
+    "c4_gqa_70b_bwd": [(0, 3)],
     "c5_bwd_d128": [(0, 3)],
     "c5_bwd_d80": [(0, 0), (0, 15)],
     "c6_window_d128": [(0, 5)],

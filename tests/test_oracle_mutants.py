@@ -39,6 +39,10 @@ MUTANTS = {
     "online_drops_lse_max": ("m + np.log(l)", "np.log(l)"),
     "window_off_by_one": ("ok &= j > i - window", "ok &= j >= i - window"),
     "window_ignored": ("ok &= j > i - window", "pass"),
+    "decode_top_left_alignment": ("row0=L - Nq, window=window)", "row0=0, window=window)"),
+    "decode_alignment_off_by_one": ("row0=L - Nq, window=window)", "row0=L - Nq + 1, window=window)"),
+    "decode_ignores_lengths": ("L = Nk if kv_lens is None else", "L = Nk if True else"),
+    "decode_length_not_clamped": ("int(min(max(int(kv_lens[b]), 0), Nk))", "int(kv_lens[b])"),
 }
 
 
@@ -66,6 +70,12 @@ def run_all_pins(mod):
     pins.check_window_brute_force(fwd_w, 301, 1, 2, 1, 6, 3, 2)
     pins.check_window_special_cases(fwd, fwd_w)
     pins.check_window_gradients(fwd_w, bwd_w)
+    dec = lambda q, k, v, s, c, lens, w: mod.ref_decode(q, k, v, s, c, kv_lens=lens, window=w)
+    full = lambda q, k, v, s, c, w: mod.ref_fwd(q, k, v, s, c, chunk=3, window=w)
+    for causal, window in ((False, None), (True, None), (True, 3)):
+        pins.check_decode_brute_force(dec, 41, causal, window)
+        pins.check_decode_is_last_rows(dec, full, causal, window)
+    pins.check_decode_special_cases(dec)
 
 
 def test_unmutated_copy_passes():

@@ -142,3 +142,27 @@ def test_window_gradients():
 def test_window_rejects_zero():
     with pytest.raises(ValueError):
         oracle.allowed_mask(0, 3, 3, True, 0)
+
+
+# ------------------------------------------------------------------- decoding
+
+def dec(q, k, v, scale, causal, kv_lens, window):
+    return oracle.ref_decode(q, k, v, scale, causal, kv_lens=kv_lens, window=window)
+
+
+def fwd_full(q, k, v, scale, causal, window):
+    return oracle.ref_fwd(q, k, v, scale, causal, chunk=3, window=window)
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 3), (True, 1)])
+def test_decode_brute_force(causal, window):
+    pins.check_decode_brute_force(dec, 40 + (window or 0), causal, window)
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 4), (True, 20)])
+def test_decode_is_last_rows_of_self_attention(causal, window):
+    pins.check_decode_is_last_rows(dec, fwd_full, causal, window)
+
+
+def test_decode_special_cases():
+    pins.check_decode_special_cases(dec)
