@@ -80,6 +80,21 @@ class AttnTensor(ctypes.Structure):
     ]
 
 
+class AttnDecodeProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int),
+        ("Hq", ctypes.c_int),
+        ("Hkv", ctypes.c_int),
+        ("Nq", ctypes.c_int),
+        ("Nk", ctypes.c_int),
+        ("d", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("mask", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+    ]
+
+
 class AttnProblem(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int),
@@ -118,7 +133,11 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
     L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
-    for name in ("attn_fwd", "attn_fwd_window", "attn_fwd_ex", "attn_bwd", "attn_bwd_window",
+    dp = ctypes.POINTER(AttnDecodeProblem)
+    L.attn_decode_workspace_bytes.argtypes = [dp]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode_fwd.argtypes = [dp, tp, tp, tp, vp, tp, vp, vp, sz, vp]
+    for name in ("attn_decode_fwd", "attn_fwd", "attn_fwd_window", "attn_fwd_ex", "attn_bwd", "attn_bwd_window",
                  "attn_bwd_ex", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"):
         getattr(L, name).restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -372,6 +391,63 @@ def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal
     if layout == "bshd":
         return tuple(t.transpose(1, 2) for t in outs)
     return dqv, dkv, dvv
+
+
+def _decode_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, dtype):
+    if window is not None:
+        mask, win = MASK_SLIDING_WINDOW, window
+    else:
+        mask, win = (MASK_CAUSAL if causal else MASK_NONE), 0
+    return AttnDecodeProblem(B, Hq, Hkv, Nq, Nk, d, float(scale), mask, win, dtype)
+
+
+def decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal=False, window=None, dtype=DTYPE_BF16) -> int:
+    prob = _decode_problem(B, Hq, Hkv, Nq, Nk, d, 1.0, causal, window, dtype)
+    return int(lib().attn_decode_workspace_bytes(ctypes.byref(prob)))
+
+
+def decode(q, k_cache, v_cache, *, kv_lens=None, scale=None, causal=False, window=None,
+           layout="bhsd", out=None, lse=None, workspace=None):
+    """Attention of Nq new queries per sequence against a KV cache.
+
+    q [B,Hq,Nq,d]; k_cache, v_cache [B,Hkv,Nk,d] (dims 1, 2 swapped for
+    layout="bshd"); kv_lens: None (every sequence fills the cache) or an
+    int32 GPU tensor [B] of valid cache rows. Query i of sequence b is the
+    token at position kv_lens[b] - Nq + i. Returns (o like q, lse [B,Hq,Nq]).
+    """
+    import torch
+    window = _window_arg(window)
+    qv = _as_bhsd(q, "q", layout)
+    kv_, vv = _as_bhsd(k_cache, "k_cache", layout), _as_bhsd(v_cache, "v_cache", layout)
+    B, Hq, Nq, d = qv.shape
+    if kv_.shape != vv.shape or kv_.shape[0] != B or kv_.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(qv.shape)}, caches {tuple(kv_.shape)}, {tuple(vv.shape)}")
+    if not (qv.dtype == kv_.dtype == vv.dtype):
+        raise TypeError("q and the caches must have one dtype")
+    Hkv, Nk = kv_.shape[1], kv_.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    ov = _new_like(qv, layout) if out is None else _as_bhsd(out, "out", layout)
+    _same(ov, "out", qv)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _rows(lse, "lse", B, Hq, Nq, q.device)
+    lens_ptr = None
+    if kv_lens is not None:
+        if (not isinstance(kv_lens, torch.Tensor) or kv_lens.dtype != torch.int32
+                or kv_lens.device != q.device or tuple(kv_lens.shape) != (B,) or not kv_lens.is_contiguous()):
+            raise TypeError("kv_lens must be a contiguous int32 tensor [B] on the GPU")
+        lens_ptr = kv_lens.data_ptr()
+    prob = _decode_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, _dtype_code(qv))
+    L = lib()
+    need = int(L.attn_decode_workspace_bytes(ctypes.byref(prob)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(L.attn_decode_fwd(ctypes.byref(prob), _tensor(qv), _tensor(kv_), _tensor(vv), lens_ptr,
+                             _tensor(ov), lse.data_ptr(), ws, wsb, _stream_ptr(q.device)))
+    return (ov.transpose(1, 2) if layout == "bshd" else ov), lse
 
 
 def fwd_plan(B, Hq, Hkv, N, d, causal=False) -> dict:

@@ -28,6 +28,7 @@ SOURCES = {
     "attn_fwd.hip": [],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "attn_bwd_dq.hip": [],
+    "attn_decode.hip": [],
 }
 
 # Packed fp32 VALU forms are turned off for all device code. MFMA results

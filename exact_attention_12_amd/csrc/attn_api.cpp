@@ -270,9 +270,101 @@ attn_status bwd_plain(const void* q, const void* k, const void* v, const void* o
                     passes, stream);
 }
 
+attn_status check_decode(const attn_decode_problem& pr, attn::DecPlan* plan, int* kernel_mask,
+                         int* kernel_window) {
+    if (pr.Nq < 1 || pr.Nk < 1 || pr.Nq > ATTN_MAX_SEQ_LEN || pr.Nk > ATTN_MAX_SEQ_LEN)
+        return ATTN_ERR_SHAPE;
+    attn_status st = check_shape(pr.B, pr.Hq, pr.Hkv, pr.Nq > pr.Nk ? pr.Nq : pr.Nk, pr.d);
+    if (st != ATTN_OK) return st;
+    st = check_scale(pr.scale);
+    if (st != ATTN_OK) return st;
+    switch (pr.mask) {
+        case ATTN_MASK_NONE:
+        case ATTN_MASK_CAUSAL:
+            if (pr.window != 0) return ATTN_ERR_WINDOW;
+            *kernel_mask = pr.mask == ATTN_MASK_NONE ? attn::kMaskNone : attn::kMaskCausal;
+            *kernel_window = 0;
+            break;
+        case ATTN_MASK_SLIDING_WINDOW:
+            if (pr.window < 1) return ATTN_ERR_WINDOW;
+            // A band of Nk or more keys reaches back past the start of the cache.
+            *kernel_mask = pr.window >= pr.Nk ? attn::kMaskCausal : attn::kMaskWindow;
+            *kernel_window = pr.window >= pr.Nk ? 0 : pr.window;
+            break;
+        default: return ATTN_ERR_WINDOW;
+    }
+    if (pr.dtype != ATTN_DTYPE_BF16 && pr.dtype != ATTN_DTYPE_FP16) return ATTN_ERR_DTYPE;
+    attn::decode_plan(pr.B, pr.Hkv, pr.Hq / pr.Hkv, pr.Nq, pr.Nk, pr.d, plan);
+    if (plan->workgroups > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t attn_decode_workspace_bytes(const attn_decode_problem* problem) {
+    if (!problem) return 0;
+    attn::DecPlan plan;
+    int mask = 0, window = 0;
+    if (check_decode(*problem, &plan, &mask, &window) != ATTN_OK) return 0;
+    return plan.workspace_bytes;
+}
+
+attn_status attn_decode_fwd(const attn_decode_problem* problem, const attn_tensor* q,
+                            const attn_tensor* k_cache, const attn_tensor* v_cache,
+                            const int* kv_lens, const attn_tensor* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (!problem) return ATTN_ERR_NULL;
+    const attn_tensor* ts[] = {q, k_cache, v_cache, o};
+    attn_status st = check_null(ts, 4);
+    if (st != ATTN_OK) return st;
+    if (!lse) return ATTN_ERR_NULL;
+    attn::DecPlan plan;
+    int mask = 0, window = 0;
+    st = check_decode(*problem, &plan, &mask, &window);
+    if (st != ATTN_OK) return st;
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+        return ATTN_ERR_WORKSPACE;
+    st = check_layout(ts, 4);
+    if (st != ATTN_OK) return st;
+    if (!aligned16(lse) || (plan.workspace_bytes > 0 && !aligned16(workspace)) ||
+        (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
+        return ATTN_ERR_ALIGN;
+
+    const attn_decode_problem& pr = *problem;
+    attn::DecParams p;
+    p.q = q->data;
+    p.k = k_cache->data;
+    p.v = v_cache->data;
+    p.o = o->data;
+    p.lse = lse;
+    p.kv_lens = kv_lens;
+    const size_t rows = (size_t)pr.B * pr.Hkv * plan.R;
+    p.part_o = plan.workspace_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+    p.part_lse = plan.workspace_bytes > 0
+                     ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                ((rows * plan.S * (size_t)pr.d * 4 + 255) & ~(size_t)255))
+                     : nullptr;
+    p.sq = strides_of(*q);
+    p.sk = strides_of(*k_cache);
+    p.sv = strides_of(*v_cache);
+    p.so = strides_of(*o);
+    p.B = pr.B;
+    p.Hq = pr.Hq;
+    p.Hkv = pr.Hkv;
+    p.G = pr.Hq / pr.Hkv;
+    p.Nq = pr.Nq;
+    p.Nk = pr.Nk;
+    p.R = plan.R;
+    p.RT = plan.RT;
+    p.S = plan.S;
+    p.LC = plan.LC;
+    p.window = window;
+    p.c = pr.scale * kLog2eHost;
+    g_last_hip_error[0] = '\0';
+    return hip_status(attn::launch_decode(p, pr.dtype, pr.d, mask, static_cast<hipStream_t>(stream)));
+}
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,

@@ -109,6 +109,41 @@ struct FwdPlan {
 
 bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan);
 
+// Decoding against a key/value cache: Nq new queries per sequence, at
+// positions L_b - Nq .. L_b - 1 of a cache holding L_b valid rows (of Nk).
+// The R = G * Nq query rows of one KV-head group are processed together in
+// 32-row tiles; the cache is cut into S splits of LC keys, each split's
+// partial (normalised O and log2-domain LSE) goes to the workspace, and a
+// second kernel merges the splits. With S == 1 the first kernel writes the
+// result directly.
+struct DecParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;          // [B, Hq, Nq], contiguous
+    const int* kv_lens;  // [B] valid cache rows per sequence, or NULL (= Nk)
+    float* part_o;       // [B * Hkv * R, S, d] fp32
+    float* part_lse;     // [B * Hkv * R, S] fp32, log2 domain
+    Strides sq, sk, sv, so;
+    int B, Hq, Hkv, G, Nq, Nk;
+    int R;       // G * Nq rows per KV-head group
+    int RT;      // 32-row tiles per group
+    int S;       // key splits
+    int LC;      // keys per split (multiple of 32)
+    int window;  // sliding window W, 0 = none
+    float c;     // scale * log2(e)
+};
+
+struct DecPlan {
+    int R, RT, S, LC;
+    long long workgroups;
+    size_t workspace_bytes;
+};
+
+bool decode_plan(int B, int Hkv, int G, int Nq, int Nk, int d, DecPlan* plan);
+hipError_t launch_decode(const DecParams& p, int dtype, int d, int mask, hipStream_t stream);
+
 // Launchers return the hipError_t of the launch.
 // dtype: 0 = bf16, 1 = fp16 (the kernels' DType).
 hipError_t launch_fwd(const FwdParams& p, int dtype, int d, int mask, const FwdPlan& plan,

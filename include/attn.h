@@ -240,6 +240,46 @@ attn_status attn_bwd_ex(const attn_problem* problem, const attn_tensor* q, const
                         const attn_tensor* dv, void* workspace, size_t workspace_bytes,
                         unsigned passes, void* stream);
 
+/*
+ * Decoding: Nq new queries per sequence against a key/value cache.
+ *   q [B, Hq, Nq, d] and o (same shape) as attn_tensor views; k_cache,
+ *   v_cache [B, Hkv, Nk, d] views of a cache with room for Nk rows, of which
+ *   the first L_b hold sequence b: L_b = kv_lens[b] clamped to [0, Nk]
+ *   (kv_lens: device int32 [B], or NULL for L_b = Nk).
+ *   Query i of sequence b is the token at position L_b - Nq + i (the cache
+ *   already holds its key and value), so the result equals the last Nq rows
+ *   of self-attention over the L_b cached positions under the same mask
+ *   (ATTN_MASK_NONE: all L_b keys; CAUSAL: keys j <= L_b - Nq + i;
+ *   SLIDING_WINDOW: the W keys ending there). A query that sees no key
+ *   (L_b < Nq under a causal mask, or L_b = 0) gets o = 0 and lse = -inf.
+ *   lse [B, Hq, Nq] float32 contiguous, natural log.
+ *   The KV cache and its GQA sharing are described on "Transformer高效注意力
+ *   机制实现：Flash Attention与GQA原理对比与代码实践" (yunthe.com), sections on
+ *   the MHA KV cache and on GQA.
+ * The cache is split along its length and the partial results are merged by
+ * a second kernel; the workspace (attn_decode_workspace_bytes, possibly 0)
+ * holds the partials. Returns ATTN_OK or an error code with nothing enqueued.
+ */
+typedef struct attn_decode_problem {
+    int B, Hq, Hkv;
+    int Nq;      /* new queries per sequence, >= 1 */
+    int Nk;      /* rows the cache views hold, >= 1 */
+    int d;
+    float scale;
+    int mask;    /* attn_mask_kind */
+    int window;  /* W >= 1 with ATTN_MASK_SLIDING_WINDOW, 0 otherwise */
+    int dtype;   /* attn_dtype of q, k_cache, v_cache, o */
+} attn_decode_problem;
+
+/* Workspace bytes attn_decode_fwd needs for `problem` (0 if the shape is
+ * invalid or no split is needed). */
+size_t attn_decode_workspace_bytes(const attn_decode_problem* problem);
+
+attn_status attn_decode_fwd(const attn_decode_problem* problem, const attn_tensor* q,
+                            const attn_tensor* k_cache, const attn_tensor* v_cache,
+                            const int* kv_lens, const attn_tensor* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);
 

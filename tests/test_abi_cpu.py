@@ -267,3 +267,65 @@ def test_head_dims_have_plans(L):
         p = ea.fwd_plan(1, 4, 4, 1000, d)
         assert p["lds_bytes"] <= 160 * 1024 // (2 if d <= 128 else 1)
         assert p["block_kv"] == (64 if d <= 128 else 32)
+
+
+# ------------------------------------------------------------------- decoding
+
+def dprob(**kw):
+    base = dict(B=2, Hq=8, Hkv=2, Nq=1, Nk=100, d=128, scale=0.1, mask=ea.MASK_CAUSAL, window=0,
+                dtype=ea.DTYPE_BF16)
+    base.update(kw)
+    return ea.AttnDecodeProblem(*[base[f] for f, _ in ea.AttnDecodeProblem._fields_])
+
+
+def dec(L, pr=None, ts=None, lens=None, lse=P, ws=P, wsb=1 << 24):
+    ts = ts if ts is not None else [T() for _ in range(4)]
+    r = [ctypes.byref(t) if t is not None else None for t in ts]
+    return L.attn_decode_fwd(ctypes.byref(pr or dprob()), r[0], r[1], r[2], lens, r[3], lse, ws, wsb,
+                             None)
+
+
+def test_decode_validation(L):
+    assert L.attn_decode_fwd(None, *[None] * 3, None, None, P, P, 1, None) == 1
+    for i in range(4):
+        ts = [T() for _ in range(4)]
+        ts[i] = None
+        assert dec(L, ts=ts) == 1
+        ts[i] = T(sb=-8)
+        assert dec(L, ts=ts) == 10
+        ts[i] = T(sn=4)
+        assert dec(L, ts=ts) == 6
+    assert dec(L, lse=None) == 1
+    assert dec(L, lse=P + 4) == 6
+    assert dec(L, lens=P + 2) == 6
+    assert dec(L, pr=dprob(Nq=0)) == 2
+    assert dec(L, pr=dprob(Nk=0)) == 2
+    assert dec(L, pr=dprob(Hq=6, Hkv=4)) == 3
+    assert dec(L, pr=dprob(d=100)) == 4
+    assert dec(L, pr=dprob(scale=-2.0)) == 5
+    assert dec(L, pr=dprob(mask=ea.MASK_SLIDING_WINDOW, window=0)) == 9
+    assert dec(L, pr=dprob(mask=ea.MASK_NONE, window=2)) == 9
+    assert dec(L, pr=dprob(mask=7)) == 9
+    assert dec(L, pr=dprob(dtype=3)) == 11
+    need = L.attn_decode_workspace_bytes(ctypes.byref(dprob()))
+    assert need > 0
+    assert dec(L, ws=None) == 7
+    assert dec(L, wsb=need - 1) == 7
+    assert dec(L, ws=P + 8, wsb=need) == 6
+    assert L.attn_decode_workspace_bytes(None) == 0
+    assert L.attn_decode_workspace_bytes(ctypes.byref(dprob(d=100))) == 0
+    # many sequences x KV heads fill the grid without splitting: no workspace
+    assert L.attn_decode_workspace_bytes(ctypes.byref(dprob(B=4096, Hkv=8, Hq=8, Nk=64))) == 0
+
+
+def test_decode_workspace_formula(L):
+    # rows x splits x (d floats + 1 float), each part rounded up to 256 bytes
+    pr = dprob(B=32, Hq=64, Hkv=8, Nq=1, Nk=4096, d=128)
+    groups = 32 * 8
+    S = -(-2048 // groups)
+    LC = -(-4096 // S)
+    LC = -(-LC // 32) * 32
+    S = -(-4096 // LC)
+    rows = 32 * 8 * 8
+    want = -(-(rows * S * 128 * 4) // 256) * 256 + -(-(rows * S * 4) // 256) * 256
+    assert L.attn_decode_workspace_bytes(ctypes.byref(pr)) == want
