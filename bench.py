@@ -82,7 +82,12 @@ KERNEL_SOURCES = {
     "bwd_dkdv_kernel": ["csrc/attn_bwd.hip", "csrc/attn_bwd_common.h", *_COMMON],
     "bwd_pre_kernel": ["csrc/attn_bwd.hip", "csrc/attn_bwd_common.h", *_COMMON],
     "bwd_dq_kernel": ["csrc/attn_bwd_dq.hip", "csrc/attn_bwd_common.h", *_COMMON],
+    "decode_split_kernel": ["csrc/attn_decode.hip", *_COMMON],
+    "decode_merge_kernel": ["csrc/attn_decode.hip", *_COMMON],
 }
+# The decode call launches the split kernel and then the merge kernel; it is
+# timed (and its traffic summed) as one unit.
+DECODE_UNIT = "decode_split_kernel+decode_merge_kernel"
 CALIBRATION_KERNEL = "neg_kernel"
 
 
@@ -104,6 +109,9 @@ def traffic_file(kernel, workload):
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, or None when
     it is missing or was measured on other source."""
+    if kernel == DECODE_UNIT:
+        parts = [read_traffic(k, workload) for k in kernel.split("+")]
+        return None if None in parts else sum(parts)
     path = traffic_file(kernel, workload)
     if not os.path.exists(path):
         return None
@@ -153,7 +161,8 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload, mib):
     sf, sw = known_kib / cal_f, known_kib / cal_w
     os.makedirs(out_dir, exist_ok=True)
     written = []
-    for kernel in ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel"):
+    for kernel in ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel",
+                   "decode_split_kernel", "decode_merge_kernel"):
         try:
             kf, kw = find(fetch, f"{kernel}<"), find(write, f"{kernel}<")
         except SystemExit:
@@ -218,7 +227,10 @@ def cpu_baseline(w, inputs, budget_s):
             k = si.to_f64(inputs["k"][b:b + 1, hk:hk + 1])
             v = si.to_f64(inputs["v"][b:b + 1, hk:hk + 1])
             t0 = time.perf_counter()
-            oracle.ref_fwd(q, k, v, w.scale, w.causal, window=w.window)
+            if w.Nq is not None:
+                oracle.ref_decode(q, k, v, w.scale, w.causal, window=w.window)
+            else:
+                oracle.ref_fwd(q, k, v, w.scale, w.causal, window=w.window)
             if w.backward:
                 do = si.to_f64(inputs["do"][b:b + 1, h:h + 1])
                 oracle.ref_bwd(q, k, v, do, w.scale, w.causal, window=w.window)
@@ -236,7 +248,8 @@ def cpu_baseline(w, inputs, budget_s):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{heads} of {w.B * w.Hq} heads of the same workload (N={w.N}, d={w.d}, "
+        "sample": (f"{heads} of {w.B * w.Hq} heads of the same workload "
+                   f"({'Nq=' + str(w.Nq) + ' against a cache of ' if w.Nq else ''}N={w.N}, d={w.d}, "
                    f"{w.mask}, {'fwd+bwd' if w.backward else 'fwd'}), "
                    f"numpy float64 with S and P materialised, {secs:.1f} s; value credits the "
                    f"same algorithmic flops per head as the GPU line"),
@@ -251,6 +264,12 @@ def parity_sample(w, inputs, o, lse):
     import oracle
     b, h = w.B - 1, w.Hq - 1
     hk = h // w.G
+    if w.Nq is not None:  # decoding: every query head of the last sequence
+        O, L = oracle.ref_decode(si.to_f64(inputs["q"][b:b + 1]), si.to_f64(inputs["k"][b:b + 1]),
+                                 si.to_f64(inputs["v"][b:b + 1]), w.scale, w.causal, window=w.window)
+        eo = float(np.abs(si.to_f64(o[b]) - O[0]).max())
+        el = float(np.abs(lse[b].double().cpu().numpy() - L[0]).max())
+        return {"sequence": int(b), "rows": int(w.Hq * w.Nq), "o_max_abs_err": eo, "lse_max_abs_err": el}
     rows = np.unique(np.linspace(0, w.N - 1, 48).astype(int))
     q = si.to_f64(inputs["q"][b, h])
     k = si.to_f64(inputs["k"][b, hk])
@@ -335,13 +354,22 @@ def main():
     g = {key: si.in_layout(t.cuda(), w.layout) for key, t in inputs.items()}
     stream = torch.cuda.current_stream()
     o = torch.empty_like(g["q"])
-    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    rows_per_head = w.Nq if w.Nq is not None else w.N
+    lse = torch.empty((w.B, w.Hq, rows_per_head), dtype=torch.float32, device="cuda")
+    if w.Nq is not None:
+        dws_bytes = ea.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.N, w.d, w.causal, w.window,
+                                              ea.DTYPE_FP16 if w.dtype == "fp16" else ea.DTYPE_BF16)
+        dws = torch.empty(max(dws_bytes, 256), dtype=torch.uint8, device="cuda")
     if w.backward:
         dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
         ws = torch.empty(ea.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8,
                          device="cuda")
 
     def run_fwd():
+        if w.Nq is not None:
+            ea.decode(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
+                      layout=w.layout, out=o, lse=lse, workspace=dws)
+            return
         ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
                layout=w.layout, out=o, lse=lse)
 
@@ -358,7 +386,7 @@ def main():
     # own entry points (the kernels attn_bwd launches, in its order). A HIP
     # event on the launch stream sits between consecutive kernels, so the
     # timed steps also give each kernel's average launch duration.
-    names, launches = ["fwd_kernel"], [run_fwd]
+    names, launches = [DECODE_UNIT if w.Nq is not None else "fwd_kernel"], [run_fwd]
     if w.backward:
         names += ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
         launches += [bwd_pass("pre"), bwd_pass("dkdv"), bwd_pass("dq")]
@@ -384,6 +412,7 @@ def main():
     credit = kernel_flop_credit(w)
     rows = w.B * w.Hq * w.N
     work = {"fwd_kernel": (credit["fwd"], w.fwd_bytes()),
+            DECODE_UNIT: (credit["fwd"], w.fwd_bytes()),
             "bwd_pre_kernel": (0.0, 2 * rows * w.d * 2 + 4 * rows),
             "bwd_dkdv_kernel": (credit["bwd_dkdv"], None),
             "bwd_dq_kernel": (credit["bwd_dq"], None)}
@@ -399,8 +428,8 @@ def main():
         k["pct_of_bf16_peak"] = round(100.0 * k["tflops"] / PEAK_BF16_TFLOPS, 2)
         k["ms"] = round(k["ms"], 4)
     print(f"[bench] kernels: {kernels}", file=sys.stderr, flush=True)
-    passes = {"fwd": {"ms": kernels["fwd_kernel"]["ms"], "tflops": kernels["fwd_kernel"]["tflops"],
-                      "pct_of_bf16_peak": kernels["fwd_kernel"]["pct_of_bf16_peak"]}}
+    passes = {"fwd": {"ms": kernels[names[0]]["ms"], "tflops": kernels[names[0]]["tflops"],
+                      "pct_of_bf16_peak": kernels[names[0]]["pct_of_bf16_peak"]}}
     if w.backward:
         ms_bwd = sum(kernels[n]["ms"] for n in names[1:])
         tf = w.bwd_flops() / ms_bwd / 1e9
@@ -416,7 +445,8 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     kd = kernels[dom]
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    hbm_bound = dom == "bwd_pre_kernel" or (dom == "fwd_kernel" and w.fwd_flops() / w.fwd_bytes() < ridge)
+    hbm_bound = dom == "bwd_pre_kernel" or (dom in ("fwd_kernel", DECODE_UNIT) and
+                                             w.fwd_flops() / w.fwd_bytes() < ridge)
     if hbm_bound:
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(kd["bytes"] / kd["ms"] / 1e6, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -459,7 +489,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "window": w.window, "layout": w.layout,
+                   "causal": w.causal, "window": w.window, "layout": w.layout, "Nq": w.Nq,
                    "passes": "fwd+bwd" if w.backward else "fwd",
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -5,8 +5,9 @@ attention arithmetic. Both the HIP path and the CPU oracle are fed the same
 tensors from here.
 
 Recipe: a CPU ``torch.Generator`` seeded with the workload's seed draws Q, K, V
-and then dO, in that order, as float32 standard normals, each rounded to
-bfloat16 (or float16 for fp16 workloads; round to nearest even). Tensors are
+and then dO, in that order (decoding: the K, V cache and then the new Q), as
+float32 standard normals, each rounded to bfloat16 (or float16 for fp16
+workloads; round to nearest even). Tensors are
 returned as contiguous [B, H, N, d]; a BSHD workload hands the same values to
 the kernels as contiguous [B, N, H, d].
 """
@@ -34,6 +35,7 @@ class Workload:
     window: int | None = None  # sliding window W (keys i-W < j <= i); implies causal
     dtype: str = "bf16"        # "bf16" or "fp16"
     layout: str = "bhsd"       # "bhsd" or "bshd"
+    Nq: int | None = None      # decoding: Nq new queries against a cache of N rows
 
     @property
     def scale(self) -> float:
@@ -46,7 +48,13 @@ class Workload:
 
     def pairs(self) -> int:
         """(query, key) pairs per (b, hq): N^2, N(N+1)/2 under the causal mask,
-        and sum_i min(i+1, W) under a sliding window of W keys."""
+        and sum_i min(i+1, W) under a sliding window of W keys. Decoding: the
+        last Nq rows of that count over a full cache of N rows."""
+        if self.Nq is not None:
+            rows = range(self.N - self.Nq, self.N)
+            if self.window is not None:
+                return sum(min(i + 1, self.window) for i in rows)
+            return sum(i + 1 for i in rows) if self.causal else self.Nq * self.N
         if self.window is not None and self.window < self.N:
             W = self.window
             return W * (W + 1) // 2 + (self.N - W) * W
@@ -67,7 +75,11 @@ class Workload:
         return 2.5 * self.fwd_flops()
 
     def fwd_bytes(self) -> float:
-        """Read Q, K, V once, write O (bf16) and LSE (fp32) once."""
+        """Read Q, K, V once, write O (16-bit) and LSE (fp32) once."""
+        if self.Nq is not None:
+            q = self.B * self.Hq * self.Nq * self.d * 2
+            kv = 2 * self.B * self.Hkv * self.N * self.d * 2
+            return q + kv + q + self.B * self.Hq * self.Nq * 4
         q = self.B * self.Hq * self.N * self.d * 2
         kv = 2 * self.B * self.Hkv * self.N * self.d * 2
         return q + kv + q + self.B * self.Hq * self.N * 4
@@ -81,8 +93,8 @@ class Workload:
 
 
 def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note="", window=None, dtype="bf16",
-       layout="bhsd"):
-    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window, dtype, layout)
+       layout="bhsd", Nq=None):
+    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window, dtype, layout, Nq)
 
 
 # The five workload families (index k gives seed 1000 + k; the sequence sweep
@@ -115,6 +127,11 @@ WORKLOADS = {
         # page, flash_attn_func call): the C5 shape, so the two compare.
         _w("c7_fp16_bshd_d128", 1, 16, 16, 16384, 128, True, True, 1007,
            "fwd+bwd, fp16, BSHD", dtype="fp16", layout="bshd"),
+        # One decoding step of the 70B-like GQA model against a full KV cache:
+        # batch 32, 4096 cached tokens (the KV-cache example of the yunthe.com
+        # GQA page), one new token per sequence.
+        _w("c8_decode_70b", 32, 64, 8, 4096, 128, True, False, 1008,
+           "decode, 1 new token, KV cache 4096, GQA G=8", Nq=1),
     ]
 }
 
@@ -138,7 +155,22 @@ def make_inputs(B, Hq, Hkv, N, d, seed, with_do=False, dtype="bf16"):
 
 
 def workload_inputs(w: Workload):
-    return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, with_do=w.backward, dtype=w.dtype)
+    """Q, K, V (and dO) of a workload; for decoding, K and V are the cache
+    [B, Hkv, N, d] and Q the Nq new queries, drawn after them."""
+    if w.Nq is None:
+        return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, with_do=w.backward, dtype=w.dtype)
+    return make_decode_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.N, w.d, w.seed, dtype=w.dtype)
+
+
+def make_decode_inputs(B, Hq, Hkv, Nq, Nk, d, seed, dtype="bf16"):
+    """Draw a K, V cache [B,Hkv,Nk,d] and then Nq new queries Q [B,Hq,Nq,d]."""
+    t = TORCH_DTYPES[dtype]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    k = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(t)
+    v = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(t)
+    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32).to(t)
+    return {"q": q, "k": k, "v": v}
 
 
 def in_layout(t: torch.Tensor, layout: str) -> torch.Tensor:

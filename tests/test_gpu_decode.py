@@ -137,3 +137,16 @@ def test_decode_errors():
                   torch.zeros((1, 2, 10, 64), dtype=torch.bfloat16, device="cuda"),
                   torch.zeros((1, 2, 10, 64), dtype=torch.bfloat16, device="cuda"))
     assert e.value.name == "ATTN_ERR_GQA"
+
+
+def test_decode_workload_full_shape():
+    """The timed decode workload (batch 32, 64 query heads on 8 KV heads,
+    4096 cached tokens, d 128), checked on every head of three sequences."""
+    w = si.WORKLOADS["c8_decode_70b"]
+    inp = si.workload_inputs(w)
+    g = parity.to_gpu(inp)
+    o, lse = ea.decode(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window)
+    torch.cuda.synchronize()
+    for b in (0, 17, w.B - 1):
+        sub = {x: inp[x][b:b + 1] for x in ("q", "k", "v")}
+        check(sub, None, o[b:b + 1], lse[b:b + 1], w.scale, w.causal, w.window, f"c8 seq {b}")
