@@ -19,6 +19,11 @@ Sources (pages are cited by title and section):
   (yunthe.com): the MHA class and the GQA class (repeat_interleave of K, V);
   its KV-cache discussion motivates the decode reference (``ref_decode``).
 
+* Philox-4xW-R: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+  easy as 1, 2, 3" (SC'11), the counter-based generator both the kernels and
+  ``philox.dropout_keep`` implement for the fused dropout that [CANN-FA]'s
+  tuning section recommends.
+
 Every function here is pinned by CPU tests in ``tests/test_oracle_*.py``
 (brute force, hand-worked closed forms, invariants, finite differences).
 """
@@ -33,3 +38,4 @@ from .attention import (  # noqa: F401
     allowed_mask,
     ref_decode,
 )
+from . import philox  # noqa: F401

@@ -19,6 +19,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .philox import dropout_keep
+
 __all__ = [
     "kv_head_of",
     "allowed_mask",
@@ -95,19 +97,40 @@ def _softmax_rows(S):
     return P, lse
 
 
-def ref_fwd_head(q, k, v, scale, causal=False, row0=0, return_sp=False, window=None):
+def _dropped(P, keep, p_drop):
+    """Attention weights after dropout: kept entries scaled by 1 / (1 - p),
+    dropped ones zero ([CANN-FA] tuning section: dropout applied inside the
+    fused kernel, on the attention weights, during training)."""
+    if keep is None:
+        return P
+    return np.where(keep, P / (1.0 - p_drop), 0.0)
+
+
+def _keep_rows(dropout, bh, r0, r1, N):
+    """Keep mask of rows r0..r1-1 of head bh under dropout = (p, seed, offset)."""
+    if dropout is None:
+        return None, 0.0
+    p, seed, offset = dropout
+    return dropout_keep(bh, np.arange(r0, r1), np.arange(N), p, seed, offset), float(p)
+
+
+def ref_fwd_head(q, k, v, scale, causal=False, row0=0, return_sp=False, window=None, keep=None,
+                 p_drop=0.0):
     """Forward of one head for query rows row0 .. row0+len(q)-1.
 
     q: [R, d]; k, v: [N, d]. Returns O [R, d] and LSE [R] (float64), plus S and
     P [R, N] when ``return_sp``. [CANN-FA] standard attention code:
-    scores -> softmax -> attn_weights @ V, with S and P materialised.
+    scores -> softmax -> attn_weights @ V, with S and P materialised. With a
+    boolean ``keep`` mask [R, N], the weights go through dropout of
+    probability ``p_drop`` before the product with V; LSE and the returned P
+    are those of the softmax itself.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     S = _scores(q, k, scale, row0, causal, window)
     P, lse = _softmax_rows(S)
-    O = P @ v
+    O = _dropped(P, keep, p_drop) @ v
     if return_sp:
         return O, lse, S, P
     return O, lse
@@ -125,14 +148,17 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, N, d
 
 
-def ref_fwd(q, k, v, scale, causal=False, heads=None, chunk=DEFAULT_CHUNK, window=None):
+def ref_fwd(q, k, v, scale, causal=False, heads=None, chunk=DEFAULT_CHUNK, window=None,
+            dropout=None):
     """Forward for [B, Hq, N, d] query and [B, Hkv, N, d] key/value arrays.
 
     Returns (O [B, Hq, N, d], LSE [B, Hq, N]) in float64. ``heads`` restricts
     the work to a list of (b, hq) pairs; other entries are left NaN. Rows are
     processed ``chunk`` at a time; each chunk still holds full rows of S, P
     ([YOLO11-FA2] section 3.2 loops over blocks of query rows the same way and
-    applies a full-row softmax to each block).
+    applies a full-row softmax to each block). ``dropout`` = (p, seed, offset)
+    applies dropout with the keep mask of ``philox.dropout_keep`` for head
+    bh = b * Hq + hq.
     """
     B, Hq, Hkv, N, d = _check_shapes(q, k, v)
     O = np.full((B, Hq, N, d), np.nan)
@@ -145,13 +171,15 @@ def ref_fwd(q, k, v, scale, causal=False, heads=None, chunk=DEFAULT_CHUNK, windo
         vv = np.asarray(v[b, hkv], dtype=np.float64)
         for r0 in range(0, N, chunk):
             r1 = min(N, r0 + chunk)
-            o, lse = ref_fwd_head(q[b, hq, r0:r1], kk, vv, scale, causal, row0=r0, window=window)
+            keep, p = _keep_rows(dropout, b * Hq + hq, r0, r1, N)
+            o, lse = ref_fwd_head(q[b, hq, r0:r1], kk, vv, scale, causal, row0=r0, window=window,
+                                  keep=keep, p_drop=p)
             O[b, hq, r0:r1] = o
             LSE[b, hq, r0:r1] = lse
     return O, LSE
 
 
-def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK, window=None):
+def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK, window=None, dropout=None):
     """Backward of one KV head and the G query heads that share it.
 
     q, do: [G, N, d] (the query heads hkv*G .. hkv*G+G-1); k, v: [N, d].
@@ -166,7 +194,10 @@ def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK, window=
       dQ_i  = scale * sum_j dS_ij k_j
       dK_j  = scale * sum_i dS_ij q_i
     and, because K and V are shared by the G heads ([FA-GQA]
-    repeat_interleave), dK and dV sum over those heads.
+    repeat_interleave), dK and dV sum over those heads. Under dropout
+    (``dropout`` = (p, seed, offset, bh0), head g being bh0 + g) the forward is
+    O = Pd V with Pd = P * M / (1 - p) for the fixed keep mask M, so dV uses
+    Pd and dP picks up the same factor M / (1 - p) before the softmax step.
     """
     q = np.asarray(q, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
@@ -182,16 +213,20 @@ def ref_bwd_group(q, k, v, do, scale, causal=False, chunk=DEFAULT_CHUNK, window=
             qc = q[g, r0:r1]
             doc = do[g, r0:r1]
             _, _, _, P = ref_fwd_head(qc, k, v, scale, causal, row0=r0, return_sp=True, window=window)
+            keep, p = _keep_rows(None if dropout is None else dropout[:3],
+                                 0 if dropout is None else dropout[3] + g, r0, r1, N)
             dP = doc @ v.T
+            dP = _dropped(dP, keep, p)
             row_term = (P * dP).sum(axis=1)
             dS = P * (dP - row_term[:, None])
             dQ[g, r0:r1] = scale * (dS @ k)
             dK += scale * (dS.T @ qc)
-            dV += P.T @ doc
+            dV += _dropped(P, keep, p).T @ doc
     return dQ, dK, dV
 
 
-def ref_bwd(q, k, v, do, scale, causal=False, kv_heads=None, chunk=DEFAULT_CHUNK, window=None):
+def ref_bwd(q, k, v, do, scale, causal=False, kv_heads=None, chunk=DEFAULT_CHUNK, window=None,
+            dropout=None):
     """Backward for full [B, H, N, d] arrays; see :func:`ref_bwd_group`.
 
     ``kv_heads`` restricts the work to a list of (b, hkv) pairs (each brings its
@@ -208,8 +243,9 @@ def ref_bwd(q, k, v, do, scale, causal=False, kv_heads=None, chunk=DEFAULT_CHUNK
         kv_heads = [(b, h) for b in range(B) for h in range(Hkv)]
     for b, hkv in kv_heads:
         sl = slice(hkv * G, hkv * G + G)
+        drop = None if dropout is None else (*dropout, b * Hq + hkv * G)
         dq, dk, dv = ref_bwd_group(q[b, sl], k[b, hkv], v[b, hkv], do[b, sl],
-                                   scale, causal, chunk, window)
+                                   scale, causal, chunk, window, drop)
         dQ[b, sl] = dq
         dK[b, hkv] = dk
         dV[b, hkv] = dv

@@ -510,3 +510,141 @@ def check_decode_special_cases(dec):
     O, L = dec(q3, k[:1], v[:1], 0.5, True, [2], None)  # L_b = 2 < Nq = 3
     assert np.all(O[0, 0, 0] == 0) and np.isneginf(L[0, 0, 0])
     assert np.all(np.isfinite(L[0, 0, 1:]))
+
+
+# ------------------------------------------------------------ Philox, dropout
+
+def check_philox_against_numpy(philox):
+    """The generic Philox-4xW-R at W = 64, R = 10 equals numpy's Philox bit
+    generator (a library implementation of the same published function);
+    numpy advances its 256-bit counter by one before producing each block."""
+    r = np.random.default_rng(7)
+    for _ in range(5):
+        key = [int(x) for x in r.integers(0, 2**63, size=2, dtype=np.uint64)]
+        ctr = [int(x) for x in r.integers(0, 2**63, size=4, dtype=np.uint64)]
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(ctr, dtype=np.uint64))
+        got = bg.random_raw(8)
+        for blk in range(2):
+            c = list(ctr)
+            c[0] += blk + 1  # no carry: ctr[0] < 2^63
+            want = philox(c, key, rounds=10, width=64)
+            assert [int(x) for x in want] == [int(x) for x in got[4 * blk:4 * blk + 4]]
+
+
+def check_philox32_stream(philox, philox4x32):
+    """The vectorised 32-bit path equals the generic one, and its words look
+    uniform: mean, per-bit frequencies and lag-1 correlation within 5 sigma."""
+    r = np.random.default_rng(8)
+    c = [r.integers(0, 2**32, size=2000, dtype=np.uint64) for _ in range(4)]
+    a = philox(c, (11, 22), rounds=10, width=32)
+    b = philox4x32(c, (11, 22), rounds=10)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    n = 1 << 18
+    j = np.arange(n)
+    w = np.concatenate(philox4x32((j, 0, 5, 9), (123, 456))).astype(np.float64)
+    u = w / 2.0**32
+    assert abs(u.mean() - 0.5) < 5 * np.sqrt(1 / 12 / u.size)
+    bits = ((w.astype(np.uint64)[:, None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)).mean(axis=0)
+    assert np.all(np.abs(bits - 0.5) < 5 * 0.5 / np.sqrt(w.size))
+    cc = np.corrcoef(u[:-1], u[1:])[0, 1]
+    assert abs(cc) < 5 / np.sqrt(u.size)
+    # rounds = 0 is the identity on the counter
+    z = philox4x32((1, 2, 3, 4), (5, 6), rounds=0)
+    assert [int(x) for x in z] == [1, 2, 3, 4]
+
+
+def check_keep_mask(dropout_keep, keep_threshold):
+    """Keep fraction 1 - p (5 sigma), p = 0 keeps everything, masks depend on
+    head, seed and offset, and are reproducible."""
+    assert keep_threshold(0.0) == 0 and keep_threshold(0.5) == 2**31
+    assert keep_threshold(np.float32(0.1)) == int(np.floor(np.float64(np.float32(0.1)) * 2**32))
+    for p in (0.1, 0.5, 0.9):
+        m = dropout_keep(3, np.arange(512), np.arange(512), p, 1234, 7)
+        sd = np.sqrt(p * (1 - p) / m.size)
+        assert abs(m.mean() - (1 - p)) < 5 * sd
+    assert dropout_keep(0, np.arange(8), np.arange(8), 0.0, 1, 2).all()
+    a = dropout_keep(3, np.arange(64), np.arange(64), 0.5, 1234, 7)
+    assert np.array_equal(a, dropout_keep(3, np.arange(64), np.arange(64), 0.5, 1234, 7))
+    for other in (dropout_keep(4, np.arange(64), np.arange(64), 0.5, 1234, 7),
+                  dropout_keep(3, np.arange(64), np.arange(64), 0.5, 1235, 7),
+                  dropout_keep(3, np.arange(64), np.arange(64), 0.5, 1234, 8),
+                  dropout_keep(3, np.arange(64), np.arange(64), 0.5, 1234 + (1 << 32), 7)):
+        assert 0.3 < (a != other).mean() < 0.7
+    # rows and columns are addressed absolutely (sub-blocks agree)
+    sub = dropout_keep(3, np.arange(10, 30), np.arange(5, 40), 0.5, 1234, 7)
+    assert np.array_equal(sub, a[10:30, 5:40])
+
+
+def brute_force_dropout_fwd(q, k, v, scale, causal, keep_of, p):
+    """Scalar loops: O_i = sum_j e^{s_ij} m_ij v_j / ((1 - p) sum_j e^{s_ij}),
+    LSE_i = ln sum_j e^{s_ij} (dropout does not touch the normaliser)."""
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    O = np.zeros((B, Hq, N, d))
+    L = np.zeros((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            m = keep_of(b * Hq + h, N)
+            for i in range(N):
+                e = [math.exp(scale * sum(float(q[b, h, i, c]) * float(k[b, kv, j, c]) for c in range(d)))
+                     if not (causal and j > i) else 0.0 for j in range(N)]
+                den = math.fsum(e)
+                L[b, h, i] = math.log(den)
+                for c in range(d):
+                    O[b, h, i, c] = math.fsum(e[j] * (1.0 if m[i, j] else 0.0) * float(v[b, kv, j, c])
+                                              for j in range(N)) / ((1.0 - p) * den)
+    return O, L
+
+
+def check_dropout_forward(fwd_d, fwd, dropout_keep):
+    p, seed, off = 0.3, 99, 5
+    q, k, v, _ = rng_arrays(60, 2, 4, 2, 7, 3, with_do=False)
+    for causal in (False, True):
+        O, L = fwd_d(q, k, v, 0.7, causal, (p, seed, off))
+        Ob, Lb = brute_force_dropout_fwd(q, k, v, 0.7, causal,
+                                         lambda bh, N: dropout_keep(bh, np.arange(N), np.arange(N), p, seed, off), p)
+        np.testing.assert_allclose(O, Ob, rtol=RTOL_EXACT, atol=1e-13)
+        np.testing.assert_allclose(L, Lb, rtol=RTOL_EXACT, atol=1e-13)
+        O0, L0 = fwd_d(q, k, v, 0.7, causal, (0.0, seed, off))
+        Oc, Lc = fwd(q, k, v, 0.7, causal)
+        np.testing.assert_allclose(O0, Oc, atol=1e-15)
+        np.testing.assert_allclose(L0, Lc, atol=1e-15)
+
+
+def check_dropout_expectation(fwd_d, fwd):
+    """E[M / (1 - p)] = 1: the mean of O over many seeds tends to the
+    no-dropout output (checked to 6 standard errors)."""
+    q, k, v, _ = rng_arrays(61, 1, 1, 1, 5, 2, with_do=False)
+    Oc, _ = fwd(q, k, v, 0.5, True)
+    outs = np.stack([fwd_d(q, k, v, 0.5, True, (0.4, s, 0))[0] for s in range(1500)])
+    se = outs.std(axis=0) / np.sqrt(outs.shape[0]) + 1e-12
+    assert np.all(np.abs(outs.mean(axis=0) - Oc) < 6 * se)
+
+
+def check_dropout_gradients(fwd_d, bwd_d):
+    """Finite differences of sum(O * dO) for a fixed mask (seed, offset) give
+    the backward under dropout, GQA with two heads per KV head."""
+    scale, drop = 0.8, (0.35, 4242, 3)
+    q, k, v, do = rng_arrays(62, 1, 2, 1, 6, 3)
+    for causal in (False, True):
+        dQ, dK, dV = bwd_d(q, k, v, do, scale, causal, drop)
+        h = 1e-6
+
+        def loss(qq, kk, vv):
+            O, _ = fwd_d(qq, kk, vv, scale, causal, drop)
+            return float(np.sum(O * do))
+
+        for arr, grad, which in ((q, dQ, 0), (k, dK, 1), (v, dV, 2)):
+            num = np.zeros_like(arr)
+            it = np.nditer(arr, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                a_p = [q.copy(), k.copy(), v.copy()]
+                a_m = [q.copy(), k.copy(), v.copy()]
+                a_p[which][idx] += h
+                a_m[which][idx] -= h
+                num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+            assert np.linalg.norm(num - grad) / np.linalg.norm(grad) < 1e-7
+        np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-12)

@@ -12,6 +12,7 @@ import types
 
 import pytest
 
+from oracle import philox
 from tests import oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
@@ -24,12 +25,13 @@ MUTANTS = {
     "causal_transposed": ("ok = j <= i", "ok = j >= i"),
     "lse_without_max": ("safe_m + np.log(den)", "np.log(den)"),
     "softmax_not_normalised": ("E / den[:, None]", "E"),
-    "pv_transposed": ("O = P @ v", "O = P.T @ v[: P.shape[0]]"),
+    "pv_transposed": ("O = _dropped(P, keep, p_drop) @ v", "O = P.T @ v[: P.shape[0]]"),
     "row_term_dropped": ("dS = P * (dP - row_term[:, None])", "dS = P * dP"),
     "row_term_sign": ("dS = P * (dP - row_term[:, None])", "dS = P * (dP + row_term[:, None])"),
     "dk_scale_dropped": ("dK += scale * (dS.T @ qc)", "dK += (dS.T @ qc)"),
     "dq_sign": ("dQ[g, r0:r1] = scale * (dS @ k)", "dQ[g, r0:r1] = -scale * (dS @ k)"),
-    "dv_uses_scores": ("dV += P.T @ doc", "dV += np.where(np.isfinite(_s), _s, 0).T @ doc"),
+    "dv_uses_scores": ("dV += _dropped(P, keep, p).T @ doc",
+                       "dV += np.where(np.isfinite(_s), _s, 0).T @ doc"),
     "dk_not_group_summed": ("dK += scale * (dS.T @ qc)", "dK = scale * (dS.T @ qc) if g == G - 1 else dK"),
     "dp_transposed_v": ("dP = doc @ v.T", "dP = doc @ v[::-1].T"),
     "online_l_not_rescaled": ("l[i0:i1] *= corr", "pass"),
@@ -43,6 +45,11 @@ MUTANTS = {
     "decode_alignment_off_by_one": ("row0=L - Nq, window=window)", "row0=L - Nq + 1, window=window)"),
     "decode_ignores_lengths": ("L = Nk if kv_lens is None else", "L = Nk if True else"),
     "decode_length_not_clamped": ("int(min(max(int(kv_lens[b]), 0), Nk))", "int(kv_lens[b])"),
+    "dropout_not_rescaled": ("np.where(keep, P / (1.0 - p_drop), 0.0)", "np.where(keep, P, 0.0)"),
+    "dropout_mask_not_on_dP": ("dP = _dropped(dP, keep, p)", "dP = dP"),
+    "dropout_dv_undropped": ("dV += _dropped(P, keep, p).T @ doc", "dV += P.T @ doc"),
+    "dropout_bwd_same_mask_for_group": ("dropout[3] + g, r0, r1, N)", "dropout[3], r0, r1, N)"),
+    "dropout_fwd_head_index_without_batch": ("_keep_rows(dropout, b * Hq + hq,", "_keep_rows(dropout, hq,"),
 }
 
 
@@ -53,6 +60,7 @@ def load_mutant(old, new):
     if "_s" in new:
         src = src.replace("_, _, _, P = ref_fwd_head(", "_, _, _s, P = ref_fwd_head(")
     mod = types.ModuleType("oracle_mutant")
+    mod.__package__ = "oracle"  # the copy imports the oracle's Philox module relatively
     exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
@@ -76,6 +84,10 @@ def run_all_pins(mod):
         pins.check_decode_brute_force(dec, 41, causal, window)
         pins.check_decode_is_last_rows(dec, full, causal, window)
     pins.check_decode_special_cases(dec)
+    fwd_d = lambda q, k, v, s, c, drop: mod.ref_fwd(q, k, v, s, c, chunk=4, dropout=drop)
+    bwd_d = lambda q, k, v, do, s, c, drop: mod.ref_bwd(q, k, v, do, s, c, chunk=4, dropout=drop)
+    pins.check_dropout_forward(fwd_d, fwd, philox.dropout_keep)
+    pins.check_dropout_gradients(fwd_d, bwd_d)
 
 
 def test_unmutated_copy_passes():

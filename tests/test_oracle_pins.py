@@ -166,3 +166,41 @@ def test_decode_is_last_rows_of_self_attention(causal, window):
 
 def test_decode_special_cases():
     pins.check_decode_special_cases(dec)
+
+
+# ------------------------------------------------------------ Philox, dropout
+
+from oracle import philox as ph  # noqa: E402
+
+
+def fwd_d(q, k, v, scale, causal, drop):
+    return oracle.ref_fwd(q, k, v, scale, causal, chunk=4, dropout=drop)
+
+
+def bwd_d(q, k, v, do, scale, causal, drop):
+    return oracle.ref_bwd(q, k, v, do, scale, causal, chunk=4, dropout=drop)
+
+
+def test_philox_matches_numpy_philox4x64():
+    pins.check_philox_against_numpy(ph.philox)
+
+
+def test_philox32_stream():
+    pins.check_philox32_stream(ph.philox, ph.philox4x32)
+
+
+def test_keep_mask():
+    pins.check_keep_mask(ph.dropout_keep, ph.keep_threshold)
+
+
+def test_dropout_forward():
+    pins.check_dropout_forward(fwd_d, lambda q, k, v, s, c: oracle.ref_fwd(q, k, v, s, c, chunk=4),
+                               ph.dropout_keep)
+
+
+def test_dropout_expectation():
+    pins.check_dropout_expectation(fwd_d, lambda q, k, v, s, c: oracle.ref_fwd(q, k, v, s, c, chunk=4))
+
+
+def test_dropout_gradients():
+    pins.check_dropout_gradients(fwd_d, bwd_d)
