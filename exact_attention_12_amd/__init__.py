@@ -46,6 +46,7 @@ STATUS = {
     10: "ATTN_ERR_STRIDE",
     11: "ATTN_ERR_DTYPE",
     12: "ATTN_ERR_PASSES",
+    13: "ATTN_ERR_DROPOUT",
 }
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW = 0, 1, 2
@@ -106,6 +107,9 @@ class AttnProblem(ctypes.Structure):
         ("mask", ctypes.c_int),
         ("window", ctypes.c_int),
         ("dtype", ctypes.c_int),
+        ("dropout_p", ctypes.c_float),
+        ("seed", ctypes.c_ulonglong),
+        ("offset", ctypes.c_uint),
     ]
 
 
@@ -267,26 +271,37 @@ def _window_arg(window):
     return window
 
 
-def _problem(B, Hq, Hkv, N, d, scale, causal, window, dtype):
+def _problem(B, Hq, Hkv, N, d, scale, causal, window, dtype, dropout=None):
     if window is not None:
         mask, win = MASK_SLIDING_WINDOW, window
     else:
         mask, win = (MASK_CAUSAL if causal else MASK_NONE), 0
-    return AttnProblem(B, Hq, Hkv, N, d, float(scale), mask, win, dtype)
+    p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
+    return AttnProblem(B, Hq, Hkv, N, d, float(scale), mask, win, dtype, float(p), int(seed), int(offset))
+
+
+def _dropout_arg(dropout_p, seed, offset):
+    if not dropout_p:
+        return None
+    if not (0.0 <= float(dropout_p) < 1.0):
+        raise ValueError("dropout_p must be in [0, 1)")
+    return float(dropout_p), int(seed) & ((1 << 64) - 1), int(offset) & 0xFFFFFFFF
 
 
 def fwd(q, k, v, *, scale=None, causal=False, window=None, layout="bhsd", out=None, lse=None,
-        use_ex=False):
+        use_ex=False, dropout_p=0.0, seed=0, offset=0):
     """Forward pass. q [B,Hq,N,d], k, v [B,Hkv,N,d] (dims 1, 2 swapped for
     layout="bshd"), bf16 or fp16, on the GPU.
 
     window=W (>= 1) selects the sliding-window mask i-W < j <= i, which
     implies the causal mask. Returns (o like q, lse [B,Hq,N] float32).
     Enqueued on the current stream; no synchronisation. use_ex forces the
-    strided entry point even for plain tensors.
+    strided entry point even for plain tensors. dropout_p > 0 drops attention
+    weights with the Philox stream keyed by (seed, offset) (see attn.h).
     """
     import torch
     window = _window_arg(window)
+    drop = _dropout_arg(dropout_p, seed, offset)
     qv, kv_, vv = (_as_bhsd(t, n, layout) for t, n in ((q, "q"), (k, "k"), (v, "v")))
     B, Hq, Hkv, N, d = _shapes(qv, kv_, vv)
     if scale is None:
@@ -298,7 +313,7 @@ def fwd(q, k, v, *, scale=None, causal=False, window=None, layout="bhsd", out=No
     _rows(lse, "lse", B, Hq, N, q.device)
     st = _stream_ptr(q.device)
     L = lib()
-    if not use_ex and _plain((qv, kv_, vv, ov)):
+    if not use_ex and drop is None and _plain((qv, kv_, vv, ov)):
         if window is None:
             _check(L.attn_fwd(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
                               B, Hq, Hkv, N, d, float(scale), int(bool(causal)), st))
@@ -306,7 +321,7 @@ def fwd(q, k, v, *, scale=None, causal=False, window=None, layout="bhsd", out=No
             _check(L.attn_fwd_window(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(),
                                      lse.data_ptr(), B, Hq, Hkv, N, d, float(scale), window, st))
     else:
-        prob = _problem(B, Hq, Hkv, N, d, scale, causal, window, _dtype_code(qv))
+        prob = _problem(B, Hq, Hkv, N, d, scale, causal, window, _dtype_code(qv), drop)
         _check(L.attn_fwd_ex(ctypes.byref(prob), _tensor(qv), _tensor(kv_), _tensor(vv), _tensor(ov),
                              lse.data_ptr(), st))
     return (ov.transpose(1, 2) if layout == "bshd" else ov), lse
@@ -317,21 +332,23 @@ def bwd_workspace_bytes(B, Hq, Hkv, N, d) -> int:
 
 
 def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, window=None, layout="bhsd",
-        workspace=None, dq=None, dk=None, dv=None, use_ex=False):
-    """Backward pass; returns (dq, dk, dv) like q, k, v. `causal`, `window`
-    and `layout` must be those of the forward call."""
+        workspace=None, dq=None, dk=None, dv=None, use_ex=False, dropout_p=0.0, seed=0, offset=0):
+    """Backward pass; returns (dq, dk, dv) like q, k, v. `causal`, `window`,
+    `layout` and the dropout arguments must be those of the forward call."""
     return bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=scale, causal=causal,
                       window=window, layout=layout, passes=("pre", "dkdv", "dq"), use_ex=use_ex,
-                      fused=True)
+                      fused=True, dropout_p=dropout_p, seed=seed, offset=offset)
 
 
 def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal=False,
-               window=None, layout="bhsd", passes=("pre", "dkdv", "dq"), use_ex=False, fused=False):
+               window=None, layout="bhsd", passes=("pre", "dkdv", "dq"), use_ex=False, fused=False,
+               dropout_p=0.0, seed=0, offset=0):
     """Run selected backward passes (same arguments and checks as bwd()). With
     fused=False each pass goes through its own entry point; outputs may be
     None and are then allocated. A window implies the causal mask."""
     import torch
     window = _window_arg(window)
+    drop = _dropout_arg(dropout_p, seed, offset)
     if window is not None:
         causal = True
     bits = 0
@@ -360,7 +377,7 @@ def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal
     st = _stream_ptr(q.device)
     L = lib()
     win = 0 if window is None else window
-    if not use_ex and _plain((qv, kv_, vv, ov, dov, dqv, dkv, dvv)):
+    if not use_ex and drop is None and _plain((qv, kv_, vv, ov, dov, dqv, dkv, dvv)):
         args = (qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse.data_ptr(),
                 dov.data_ptr(), dqv.data_ptr(), dkv.data_ptr(), dvv.data_ptr(), ws, wsb,
                 B, Hq, Hkv, N, d, float(scale))
@@ -384,7 +401,7 @@ def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal
                                          dov.data_ptr(), dqv.data_ptr(), ws, wsb,
                                          B, Hq, Hkv, N, d, float(scale), int(bool(causal)), win, st))
     else:
-        prob = _problem(B, Hq, Hkv, N, d, scale, causal, window, _dtype_code(qv))
+        prob = _problem(B, Hq, Hkv, N, d, scale, causal, window, _dtype_code(qv), drop)
         _check(L.attn_bwd_ex(ctypes.byref(prob), _tensor(qv), _tensor(kv_), _tensor(vv), _tensor(ov),
                              lse.data_ptr(), _tensor(dov), _tensor(dqv), _tensor(dkv), _tensor(dvv),
                              ws, wsb, bits, st))

@@ -85,6 +85,20 @@ attn_status hip_status(hipError_t e) {
 
 attn::Strides strides_of(const attn_tensor& t) { return {t.stride_b, t.stride_h, t.stride_n}; }
 
+// Dropout parameters of a problem: threshold floor(p * 2^32) on the 32-bit
+// Philox words, and the 1/(1-p) scale of the kept weights.
+attn_status make_drop(const attn_problem& pr, attn::DropParams* d) {
+    const float pd = pr.dropout_p;
+    if (!std::isfinite(pd) || pd < 0.0f || pd >= 1.0f) return ATTN_ERR_DROPOUT;
+    const double t = std::floor((double)pd * 4294967296.0);
+    d->thr = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+    d->scale = 1.0f / (1.0f - pd);
+    d->seed_lo = (uint32_t)(pr.seed & 0xffffffffull);
+    d->seed_hi = (uint32_t)(pr.seed >> 32);
+    d->offset = pr.offset;
+    return ATTN_OK;
+}
+
 // Contiguous BHSD view of a plain pointer.
 attn_tensor bhsd(const void* p, int H, int N, int d) {
     attn_tensor t;
@@ -128,6 +142,9 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     st = check_mask(*pr, &mask, &window);
     if (st != ATTN_OK) return st;
     if (pr->dtype != ATTN_DTYPE_BF16 && pr->dtype != ATTN_DTYPE_FP16) return ATTN_ERR_DTYPE;
+    attn::DropParams drop;
+    st = make_drop(*pr, &drop);
+    if (st != ATTN_OK) return st;
     st = check_layout(ts, 4);
     if (st != ATTN_OK) return st;
     if (!aligned16(lse)) return ATTN_ERR_ALIGN;
@@ -152,6 +169,7 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.nqb = (pr->N + plan.block_q - 1) / plan.block_q;
     p.window = window;
     p.c = pr->scale * kLog2eHost;
+    p.drop = drop;
     g_last_hip_error[0] = '\0';
     return hip_status(attn::launch_fwd(p, pr->dtype, pr->d, mask, plan, static_cast<hipStream_t>(stream)));
 }
@@ -187,6 +205,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     st = check_shape(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d);
     if (st != ATTN_OK) return st;
     int mask = 0, window = 0;
+    attn::DropParams drop = {0u, 1.0f, 0u, 0u, 0u};
     if (main) {
         st = check_scale(pr->scale);
         if (st != ATTN_OK) return st;
@@ -194,6 +213,10 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
         if (st != ATTN_OK) return st;
     }
     if (pr->dtype != ATTN_DTYPE_BF16 && pr->dtype != ATTN_DTYPE_FP16) return ATTN_ERR_DTYPE;
+    if (main) {
+        st = make_drop(*pr, &drop);
+        if (st != ATTN_OK) return st;
+    }
     if (!workspace || workspace_bytes < workspace_bytes_for(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d))
         return ATTN_ERR_WORKSPACE;
     st = check_layout(ts, n);
@@ -231,6 +254,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.window = window;
     p.scale = pr->scale;
     p.c = pr->scale * kLog2eHost;
+    p.drop = drop;
     g_last_hip_error[0] = '\0';
     return hip_status(attn::launch_bwd(p, pr->dtype, pr->d, mask, (int)passes,
                                        static_cast<hipStream_t>(stream)));
@@ -248,6 +272,9 @@ attn_problem plain_problem(int B, int Hq, int Hkv, int N, int d, float scale, in
     pr.mask = window > 0 ? ATTN_MASK_SLIDING_WINDOW : (causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE);
     pr.window = window;
     pr.dtype = ATTN_DTYPE_BF16;
+    pr.dropout_p = 0.0f;
+    pr.seed = 0;
+    pr.offset = 0;
     return pr;
 }
 
@@ -467,6 +494,7 @@ const char* attn_status_string(attn_status status) {
         case ATTN_ERR_STRIDE: return "strides must be >= 0";
         case ATTN_ERR_DTYPE: return "unknown element type (supported: bf16, fp16)";
         case ATTN_ERR_PASSES: return "passes must be a nonzero subset of ATTN_BWD_ALL";
+        case ATTN_ERR_DROPOUT: return "dropout_p must be in [0, 1)";
     }
     return "unknown status";
 }

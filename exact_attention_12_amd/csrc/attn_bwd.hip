@@ -65,7 +65,7 @@ void bwd_pre_kernel(BwdParams p, long long rows) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int DT, int D, int MASK>
+template <int DT, int D, int MASK, bool DROP>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_kernel(BwdParams p) {
     constexpr bool CAUSAL = MASK != kMaskNone;
@@ -213,6 +213,23 @@ void bwd_dkdv_kernel(BwdParams p) {
             {
                 const int kq = key - q0 - 4 * h;
                 const int kq_w = kq + W - 1;
+                // Dropout: the lane's key meets 4 consecutive queries per
+                // register group, exactly one Philox block each (bit r of
+                // keep[qt] for register r). dV takes P * M / (1-p); dP is
+                // scaled the same way before the softmax step.
+                uint32_t keep[NQT];
+                if constexpr (DROP) {
+                    const uint32_t bh = (uint32_t)(b * p.Hq + hkv * p.G + g);
+#pragma unroll
+                    for (int qt = 0; qt < NQT; ++qt) {
+                        keep[qt] = 0;
+#pragma unroll
+                        for (int gg = 0; gg < 4; ++gg)
+                            keep[qt] |= keep_nibble(p.drop, (uint32_t)key,
+                                                    (uint32_t)(q0 + qt * 32 + 8 * gg + 4 * h) >> 2, bh)
+                                        << (4 * gg);
+                    }
+                }
 #pragma unroll
                 for (int u = 0; u < PVS; ++u) {
                     const int qt = u >> 1;
@@ -229,8 +246,14 @@ void bwd_dkdv_kernel(BwdParams p) {
                             float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
                             if (CAUSAL && kq > qoff) pe = 0.0f;
                             if (WINDOW && qoff > kq_w) pe = 0.0f;
-                            pv[w] = pe;
-                            dv[w] = pe * (dp[qt][r] - Ds[ql]);
+                            if constexpr (DROP) {
+                                const bool kept = (keep[qt] >> r) & 1u;
+                                pv[w] = kept ? pe * p.drop.scale : 0.0f;
+                                dv[w] = pe * ((kept ? dp[qt][r] * p.drop.scale : 0.0f) - Ds[ql]);
+                            } else {
+                                pv[w] = pe;
+                                dv[w] = pe * (dp[qt][r] - Ds[ql]);
+                            }
                         }
                         pp[e2] = cvt2<DT>(pv[0], pv[1]);
                         dd[e2] = cvt2<DT>(dv[0], dv[1]);
@@ -312,8 +335,11 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
     }
     if (passes & kBwdDkDv) {
         const long long nkb = (p.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK>), dim3((unsigned)(nkb * p.B * p.Hkv)),
-                           dim3(256), 0, stream, p);
+        const dim3 grid((unsigned)(nkb * p.B * p.Hkv)), block(256);
+        if (p.drop.thr != 0)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, false>), grid, block, 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -15,7 +15,7 @@ namespace attn {
 
 // ---------------------------------------------------------------- dQ
 
-template <int DT, int D, int MASK>
+template <int DT, int D, int MASK, bool DROP>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
 void bwd_dq_kernel(BwdParams p) {
     constexpr bool CAUSAL = MASK != kMaskNone;
@@ -130,6 +130,19 @@ void bwd_dq_kernel(BwdParams p) {
             // when the block needs no mask.
             e16x8 dsb[PVS];
             {
+                // Dropout: dP of a dropped score is zero and a kept one is
+                // scaled by 1/(1-p); P itself (and the row term) are not.
+                uint32_t keep[NKT];
+                if constexpr (DROP) {
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        keep[kt] = 0;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            keep[kt] |= keep_bits_query_lane(p.drop, kv0 + kt * 32 + 8 * g + 4 * h, qrow,
+                                                             bh) << (4 * g);
+                    }
+                }
                 const bool MASKED = CAUSAL || (kv0 + BC > N);
                 const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
                 const int lo = qrow - W + 1 - kv0 - 4 * h;
@@ -148,7 +161,9 @@ void bwd_dq_kernel(BwdParams p) {
                             float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
                             if (MASKED && koff > lim) pe = 0.0f;
                             if (WINDOW && koff < lo) pe = 0.0f;
-                            dv[w] = pe * (dp[kt][r] - del);
+                            float dpe = dp[kt][r];
+                            if constexpr (DROP) dpe = ((keep[kt] >> r) & 1u) ? dpe * p.drop.scale : 0.0f;
+                            dv[w] = pe * (dpe - del);
                         }
                         dd[e2] = cvt2<DT>(dv[0], dv[1]);
                     }
@@ -190,8 +205,11 @@ void bwd_dq_kernel(BwdParams p) {
 template <int DT, int D, int MASK>
 static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
     const long long nqb = (p.N + 127) / 128;
-    hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK>), dim3((unsigned)(nqb * p.B * p.Hq)), dim3(256), 0,
-                       stream, p);
+    const dim3 grid((unsigned)(nqb * p.B * p.Hq)), block(256);
+    if (p.drop.thr != 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

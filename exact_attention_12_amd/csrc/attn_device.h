@@ -143,4 +143,69 @@ __device__ __forceinline__ void store4(e16* dst, float a, float b, float c, floa
     *reinterpret_cast<e16x4*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
 }
 
+// ------------------------------------------------------------------ dropout
+//
+// Counter-based random bits: Philox-4x32-10 (Salmon, Moraes, Dror, Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC'11). Each round
+// multiplies c0 and c2 by the published constants into 64-bit products and
+// mixes their halves with c1, c3 and the key; the key advances by the Weyl
+// constants between rounds. The key words are wave-uniform, so their updates
+// run on the scalar unit.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// Dropout stream: score (bh, i, j) is kept when word i % 4 of
+// philox4x32_10(j, i / 4, bh, offset; seed) is >= thr = floor(p * 2^32).
+struct DropParams {
+    uint32_t thr;     // 0 = no dropout
+    float scale;      // 1 / (1 - p)
+    uint32_t seed_lo, seed_hi, offset;
+};
+
+// Keep bits of the four queries 4*(i/4) .. +3 at key j (bit k: query 4*(i/4)+k).
+__device__ __forceinline__ uint32_t keep_nibble(const DropParams& dp, uint32_t j, uint32_t iq,
+                                                uint32_t bh) {
+    const uint4 w = philox4x32_10(j, iq, bh, dp.offset, dp.seed_lo, dp.seed_hi);
+    return (uint32_t)(w.x >= dp.thr) | ((uint32_t)(w.y >= dp.thr) << 1) |
+           ((uint32_t)(w.z >= dp.thr) << 2) | ((uint32_t)(w.w >= dp.thr) << 3);
+}
+
+// Value of x held by lane U of this lane's group of four (DPP quad_perm).
+template <int U>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, U * 0x55, 0xF, 0xF, false);
+}
+
+// Keep bits for a lane that owns query i (lane % 32 = i % 32, so the four
+// lanes of a DPP quad own the queries 4*(i/4) .. +3) and the four keys
+// j0 .. j0+3: bit u = keep(i, j0 + u). Each lane of the quad draws the Philox
+// block of one key (j0 + lane % 4) covering all four queries; the 4 x 4 bit
+// block is then transposed across the quad.
+__device__ __forceinline__ uint32_t keep_bits_query_lane(const DropParams& dp, uint32_t j0,
+                                                         uint32_t i, uint32_t bh) {
+    const uint32_t q = i & 3u;
+    const uint32_t nib = keep_nibble(dp, j0 + q, i >> 2, bh);
+    const uint32_t n0 = quad_bcast<0>(nib), n1 = quad_bcast<1>(nib);
+    const uint32_t n2 = quad_bcast<2>(nib), n3 = quad_bcast<3>(nib);
+    return ((n0 >> q) & 1u) | (((n1 >> q) & 1u) << 1) | (((n2 >> q) & 1u) << 2) |
+           (((n3 >> q) & 1u) << 3);
+}
+
 }  // namespace attn

@@ -48,7 +48,7 @@
 
 namespace attn {
 
-template <int DT, int D, int MASK, int NW>
+template <int DT, int D, int MASK, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, (D <= 128 ? 2 : 1))
 void fwd_kernel(FwdParams p) {
     constexpr int T = NW * 64;
@@ -234,6 +234,21 @@ void fwd_kernel(FwdParams p) {
 
             e16x8 pb[PVS];
             float lsum = 0.0f;
+            // Dropout: keep bits of this lane's query for every key of the
+            // step (bit r of keep[kt] belongs to register r of s[kt]). The
+            // row sum l takes every probability; only the product with V
+            // sees the dropped ones as zero, and O is scaled by 1/(1-p).
+            uint32_t keep[NKT];
+            if constexpr (DROP) {
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    keep[kt] = 0;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        keep[kt] |= keep_bits_query_lane(p.drop, kv0 + kt * 32 + 8 * g + 4 * h, qrow, bh)
+                                    << (4 * g);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < PVS; ++u) {
                 const int kt = u >> 1;
@@ -243,8 +258,12 @@ void fwd_kernel(FwdParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const float a0 = fast_exp2(fmaf(s[kt][r0 + 2 * e], c, -m_new));
                     const float a1 = fast_exp2(fmaf(s[kt][r0 + 2 * e + 1], c, -m_new));
-                    pr[e] = cvt2<DT>(a0, a1);
                     lsum += a0 + a1;
+                    if constexpr (DROP)
+                        pr[e] = cvt2<DT>(((keep[kt] >> (r0 + 2 * e)) & 1u) ? a0 : 0.0f,
+                                         ((keep[kt] >> (r0 + 2 * e + 1)) & 1u) ? a1 : 0.0f);
+                    else
+                        pr[e] = cvt2<DT>(a0, a1);
                 }
                 pb[u] = cat8(pr[0], pr[1], pr[2], pr[3]);
             }
@@ -266,7 +285,7 @@ void fwd_kernel(FwdParams p) {
 
     // Epilogue: combine the two half-row sums, normalise, store O and LSE.
     const float lt = sum_across_halves(l);
-    const float inv = 1.0f / lt;
+    const float inv = (DROP ? p.drop.scale : 1.0f) / lt;
     if (qrow < N) {
         e16* orow = static_cast<e16*>(p.o) + b * p.so.b + hq * p.so.h + qrow * p.so.n;
 #pragma unroll
@@ -282,17 +301,23 @@ void fwd_kernel(FwdParams p) {
     }
 }
 
-template <int DT, int D, int MASK>
-static hipError_t launch_fwd_dm(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
+template <int DT, int D, int MASK, bool DROP>
+static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
     const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
     if constexpr (D <= 128) {
         if (plan.waves == 8) {
-            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 4, DROP>), grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+template <int DT, int D, int MASK>
+static hipError_t launch_fwd_dm(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
+    return p.drop.thr != 0 ? launch_fwd_dmd<DT, D, MASK, true>(p, plan, stream)
+                           : launch_fwd_dmd<DT, D, MASK, false>(p, plan, stream);
 }
 
 template <int DT, int D>

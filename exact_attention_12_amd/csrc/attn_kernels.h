@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn_device.h"
+
 namespace attn {
 
 // Head dimensions with a kernel instantiation (multiples of 16: one MFMA
@@ -73,6 +75,7 @@ struct FwdParams {
     int nqb;      // query blocks per head
     int window;   // causal band width in keys (query i sees i-window < j <= i); 0 = none
     float c;      // scale * log2(e)
+    DropParams drop;
 };
 
 struct BwdParams {
@@ -95,6 +98,7 @@ struct BwdParams {
     int window;    // causal band width in keys; 0 = none
     float scale;
     float c;       // scale * log2(e)
+    DropParams drop;
 };
 
 struct FwdPlan {

@@ -82,7 +82,8 @@ typedef enum attn_status {
                                 without the causal mask */
     ATTN_ERR_STRIDE = 10,    /* a stride is negative */
     ATTN_ERR_DTYPE = 11,     /* unknown element type */
-    ATTN_ERR_PASSES = 12     /* passes is 0 or has bits other than ATTN_BWD_ALL */
+    ATTN_ERR_PASSES = 12,    /* passes is 0 or has bits other than ATTN_BWD_ALL */
+    ATTN_ERR_DROPOUT = 13    /* dropout_p is not in [0, 1) */
 } attn_status;
 
 /* Head dimensions with a specialised kernel: 32, 64, 80, 96, 128, 192, 256. */
@@ -214,6 +215,21 @@ typedef struct attn_problem {
     int mask;    /* attn_mask_kind */
     int window;  /* W >= 1 with ATTN_MASK_SLIDING_WINDOW, 0 otherwise */
     int dtype;   /* attn_dtype of q, k, v, o, dout, dq, dk, dv */
+    /*
+     * Fused dropout on the attention weights (training; "FlashAttention in
+     * CANN ops-transformer on the Ascend NPU", tuning section on dropout):
+     * O = (P * M / (1 - dropout_p)) V with a keep mask M drawn from a
+     * counter-based generator, so the backward redraws the same mask from
+     * (seed, offset) instead of storing it. Weight (b, h, i, j) is kept when
+     * 32-bit word i % 4 of Philox-4x32-10 (Salmon et al., SC'11) with counter
+     * (j, i / 4, b * Hq + h, offset) and key (seed & 0xffffffff, seed >> 32)
+     * is >= floor(dropout_p * 2^32). lse is that of the softmax (dropout
+     * does not change it). 0 turns dropout off; the backward must be given
+     * the forward's dropout_p, seed and offset.
+     */
+    float dropout_p;          /* in [0, 1) */
+    unsigned long long seed;
+    unsigned int offset;      /* e.g. a per-call counter, so calls draw fresh masks */
 } attn_problem;
 
 /*

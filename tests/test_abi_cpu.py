@@ -46,7 +46,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for code in range(13):
+    for code in range(14):
         s = ea.status_string(code)
         assert s and s != "unknown status"
     assert ea.status_string(99) == "unknown status"
@@ -187,7 +187,7 @@ def T(data=P, sb=1 << 12, sh=1 << 10, sn=64):
 
 def prob(**kw):
     base = dict(B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125, mask=ea.MASK_CAUSAL, window=0,
-                dtype=ea.DTYPE_BF16)
+                dtype=ea.DTYPE_BF16, dropout_p=0.0, seed=0, offset=0)
     base.update(kw)
     return ea.AttnProblem(*[base[f] for f, _ in ea.AttnProblem._fields_])
 
@@ -260,6 +260,13 @@ def test_bwd_ex_validation(L):
     assert bwd_ex(L, pr=prob(mask=ea.MASK_NONE, window=3)) == 9
     assert bwd_ex(L, pr=prob(mask=ea.MASK_NONE, window=3), passes=1, ws=None) == 7  # no mask in pre
     assert bwd_ex(L, pr=prob(d=100)) == 4
+    for bad in (1.0, -0.1, float("nan"), float("inf"), 2.0):
+        assert bwd_ex(L, pr=prob(dropout_p=bad)) == 13
+        assert bwd_ex(L, pr=prob(dropout_p=bad), passes=1, ws=None) == 7  # preprocess ignores it
+        assert fwd_ex(L, pr=prob(dropout_p=bad)) == 13
+    # the dropout check comes after shape / scale / mask / dtype
+    assert fwd_ex(L, pr=prob(dropout_p=2.0, dtype=4)) == 11
+    assert fwd_ex(L, pr=prob(dropout_p=0.5), lse=P + 4) == 6
 
 
 def test_head_dims_have_plans(L):
