@@ -227,13 +227,16 @@ def cpu_baseline(w, inputs, budget_s):
             k = si.to_f64(inputs["k"][b:b + 1, hk:hk + 1])
             v = si.to_f64(inputs["v"][b:b + 1, hk:hk + 1])
             t0 = time.perf_counter()
+            # one-head arrays: the dropout stream of head (b, h) is head 0 of
+            # a stream whose seed is unchanged, so the timing leg uses the
+            # same amount of work, not the same mask
             if w.Nq is not None:
                 oracle.ref_decode(q, k, v, w.scale, w.causal, window=w.window)
             else:
-                oracle.ref_fwd(q, k, v, w.scale, w.causal, window=w.window)
+                oracle.ref_fwd(q, k, v, w.scale, w.causal, window=w.window, dropout=w.dropout)
             if w.backward:
                 do = si.to_f64(inputs["do"][b:b + 1, h:h + 1])
-                oracle.ref_bwd(q, k, v, do, w.scale, w.causal, window=w.window)
+                oracle.ref_bwd(q, k, v, do, w.scale, w.causal, window=w.window, dropout=w.dropout)
             secs += time.perf_counter() - t0
             heads += 1
             if secs * (heads + 1) / heads > budget_s:
@@ -262,6 +265,7 @@ def parity_sample(w, inputs, o, lse):
     import numpy as np
 
     import oracle
+    from oracle import philox
     b, h = w.B - 1, w.Hq - 1
     hk = h // w.G
     if w.Nq is not None:  # decoding: every query head of the last sequence
@@ -278,7 +282,12 @@ def parity_sample(w, inputs, o, lse):
     lg = lse[b, h].double().cpu().numpy()
     eo, el = 0.0, 0.0
     for r in rows:
-        O, L = oracle.ref_fwd_head(q[r:r + 1], k, v, w.scale, w.causal, row0=int(r), window=w.window)
+        keep, p = None, 0.0
+        if w.dropout is not None:
+            keep = philox.dropout_keep(b * w.Hq + h, [int(r)], np.arange(w.N), *w.dropout)
+            p = w.dropout[0]
+        O, L = oracle.ref_fwd_head(q[r:r + 1], k, v, w.scale, w.causal, row0=int(r), window=w.window,
+                                   keep=keep, p_drop=p)
         eo = max(eo, float(np.abs(og[r] - O[0]).max()))
         el = max(el, float(abs(lg[r] - L[0])))
     return {"head": [int(b), int(h)], "rows": int(len(rows)), "o_max_abs_err": eo, "lse_max_abs_err": el}
@@ -365,22 +374,26 @@ def main():
         ws = torch.empty(ea.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8,
                          device="cuda")
 
+    drop_kw = {}
+    if w.dropout is not None:
+        drop_kw = dict(dropout_p=w.dropout[0], seed=w.dropout[1], offset=w.dropout[2])
+
     def run_fwd():
         if w.Nq is not None:
             ea.decode(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
                       layout=w.layout, out=o, lse=lse, workspace=dws)
             return
         ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
-               layout=w.layout, out=o, lse=lse)
+               layout=w.layout, out=o, lse=lse, **drop_kw)
 
     def run_bwd():
         ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal,
-               window=w.window, layout=w.layout, workspace=ws, dq=dq, dk=dk, dv=dv)
+               window=w.window, layout=w.layout, workspace=ws, dq=dq, dk=dk, dv=dv, **drop_kw)
 
     def bwd_pass(name):
         return lambda: ea.bwd_passes(g["q"], g["k"], g["v"], o, lse, g["do"], dq, dk, dv, ws,
                                      scale=w.scale, causal=w.causal, window=w.window,
-                                     layout=w.layout, passes=(name,))
+                                     layout=w.layout, passes=(name,), **drop_kw)
 
     # One step = the forward, then the backward's three passes through their
     # own entry points (the kernels attn_bwd launches, in its order). A HIP
@@ -490,6 +503,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "window": w.window, "layout": w.layout, "Nq": w.Nq,
+                   "dropout_p": w.dropout_p,
                    "passes": "fwd+bwd" if w.backward else "fwd",
                    "seed": w.seed, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

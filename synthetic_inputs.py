@@ -36,6 +36,7 @@ class Workload:
     dtype: str = "bf16"        # "bf16" or "fp16"
     layout: str = "bhsd"       # "bhsd" or "bshd"
     Nq: int | None = None      # decoding: Nq new queries against a cache of N rows
+    dropout_p: float = 0.0     # fused dropout probability (seed = workload seed, offset 0)
 
     @property
     def scale(self) -> float:
@@ -59,6 +60,14 @@ class Workload:
             W = self.window
             return W * (W + 1) // 2 + (self.N - W) * W
         return self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+
+    @property
+    def dropout(self):
+        """(p, seed, offset) of the dropout stream, or None."""
+        if not self.dropout_p:
+            return None
+        import numpy as np
+        return float(np.float32(self.dropout_p)), self.seed, 0
 
     @property
     def mask(self) -> str:
@@ -93,8 +102,9 @@ class Workload:
 
 
 def _w(name, B, Hq, Hkv, N, d, causal, backward, seed, note="", window=None, dtype="bf16",
-       layout="bhsd", Nq=None):
-    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window, dtype, layout, Nq)
+       layout="bhsd", Nq=None, dropout_p=0.0):
+    return Workload(name, B, Hq, Hkv, N, d, causal, backward, seed, note, window, dtype, layout, Nq,
+                    dropout_p)
 
 
 # The five workload families (index k gives seed 1000 + k; the sequence sweep
@@ -132,6 +142,10 @@ WORKLOADS = {
         # GQA page), one new token per sequence.
         _w("c8_decode_70b", 32, 64, 8, 4096, 128, True, False, 1008,
            "decode, 1 new token, KV cache 4096, GQA G=8", Nq=1),
+        # Training with the fused dropout of the CANN FlashAttention page's
+        # tuning section: the C5 shape with p = 0.1.
+        _w("c9_dropout_d128", 1, 16, 16, 16384, 128, True, True, 1009,
+           "fwd+bwd, dropout p=0.1", dropout_p=0.1),
     ]
 }
 

@@ -24,6 +24,7 @@ FWD_HEADS = {
     "c5_bwd_d80": [(0, 0), (0, 5), (0, 15)],
     "c6_window_d128": [(0, 0), (0, 31)],
     "c7_fp16_bshd_d128": [(0, 0), (0, 15)],
+    "c9_dropout_d128": [(0, 2), (0, 15)],
 }
 BWD_KV_HEADS = {
     "c4_gqa_70b_bwd": [(0, 3)],
@@ -31,6 +32,7 @@ BWD_KV_HEADS = {
     "c5_bwd_d80": [(0, 0), (0, 15)],
     "c6_window_d128": [(0, 5)],
     "c7_fp16_bshd_d128": [(0, 7)],
+    "c9_dropout_d128": [(0, 11)],
 }
 
 
@@ -48,20 +50,21 @@ def test_workload(name):
                f"{w.dtype} {w.layout}")
     inp = si.workload_inputs(w)
     g = {key: si.in_layout(t.cuda(), w.layout) for key, t in inp.items()}
+    dk = {} if w.dropout is None else dict(dropout_p=w.dropout[0], seed=w.dropout[1], offset=w.dropout[2])
     o, lse = ea.fwd(g["q"], g["k"], g["v"], scale=w.scale, causal=w.causal, window=w.window,
-                    layout=w.layout)
+                    layout=w.layout, **dk)
     torch.cuda.synchronize()
     if w.layout == "bshd":  # back to [B, H, N, d] for the checks
         o = o.transpose(1, 2)
         g = {key: t.transpose(1, 2) for key, t in g.items()}
     heads = FWD_HEADS[name] or [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    parity.check_fwd(inp, o, lse, w.scale, w.causal, heads, name, window=w.window)
+    parity.check_fwd(inp, o, lse, w.scale, w.causal, heads, name, window=w.window, dropout=w.dropout)
     if w.backward:
         grads = ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=w.scale, causal=w.causal,
-                       window=w.window)  # BHSD views of the same memory
+                       window=w.window, **dk)  # BHSD views of the same memory
         torch.cuda.synchronize()
         parity.check_bwd(inp, grads, w.scale, w.causal, BWD_KV_HEADS[name], w.Hq, w.Hkv, name,
-                         window=w.window)
+                         window=w.window, dropout=w.dropout)
         # Identities that hold for every head: rows of P sum to one, so the
         # key-sum of dV equals the query-sum of dO over each group; shifting
         # all keys leaves O unchanged, so the key-sum of dK vanishes.
