@@ -117,9 +117,14 @@ attn_status check_null(const attn_tensor* const* ts, int n) {
         if (!ts[i] || !ts[i]->data) return ATTN_ERR_NULL;
     return ATTN_OK;
 }
-attn_status check_layout(const attn_tensor* const* ts, int n) {
+// rows > 0: the kernels address a head's rows through 32-bit byte offsets,
+// so (rows - 1) * stride_n + d elements must stay under 2^31.
+attn_status check_layout(const attn_tensor* const* ts, int n, int rows = 0, int d = 0) {
     for (int i = 0; i < n; ++i)
         if (ts[i]->stride_b < 0 || ts[i]->stride_h < 0 || ts[i]->stride_n < 0) return ATTN_ERR_STRIDE;
+    if (rows > 0)
+        for (int i = 0; i < n; ++i)
+            if ((double)(rows - 1) * (double)ts[i]->stride_n + d >= 2147483648.0) return ATTN_ERR_STRIDE;
     for (int i = 0; i < n; ++i) {
         const attn_tensor& t = *ts[i];
         if (!aligned16(t.data) || (t.stride_b | t.stride_h | t.stride_n) & 7) return ATTN_ERR_ALIGN;
@@ -145,7 +150,7 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     attn::DropParams drop;
     st = make_drop(*pr, &drop);
     if (st != ATTN_OK) return st;
-    st = check_layout(ts, 4);
+    st = check_layout(ts, 4, pr->N, pr->d);
     if (st != ATTN_OK) return st;
     if (!aligned16(lse)) return ATTN_ERR_ALIGN;
 
@@ -219,7 +224,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     }
     if (!workspace || workspace_bytes < workspace_bytes_for(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d))
         return ATTN_ERR_WORKSPACE;
-    st = check_layout(ts, n);
+    st = check_layout(ts, n, pr->N, pr->d);
     if (st != ATTN_OK) return st;
     if ((main && !aligned16(lse)) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
 

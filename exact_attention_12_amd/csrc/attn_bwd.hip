@@ -80,7 +80,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int NDT = (D + 31) / 32;
     constexpr int QP = sw_pitch(D);    // Q, dO tiles: row reads and transposing reads
     constexpr int TILE = BQ * QP;
-    constexpr int BUF = 2 * TILE * 2 + 2 * BQ * 4;  // bytes: Q, dO, lse2, D
+    constexpr int BUF = 2 * TILE * 2 + T * 4;  // bytes: Q, dO, lse2, D, spare row terms
 
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * BUF];
 
@@ -136,7 +136,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int total = p.G * nq_iter;
 
     TileIO<D, BQ, T> qio, doio;
-    float lse_r = 0.0f, del_r = 0.0f;
+    // Row terms of the step: threads 0 .. BQ-1 fetch log2-domain LSE, BQ ..
+    // 2BQ-1 the D_i; the others repeat a D_i fetch into a spare LDS slot, so
+    // the loop body has no branch.
+    float row_r = 0.0f;
+    const int rt_kind = tid / BQ;        // 0: LSE, 1: D_i, 2+: spare
+    const int rt_row = tid - rt_kind * BQ;
     auto load_step = [&](int it) {
         const int g = it / nq_iter;
         const int qb = qb_start + (it - g * nq_iter);
@@ -145,19 +150,15 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int r0 = qb * BQ;
         qio.load(static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h, p.sq.n, r0, N, tid);
         doio.load(static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h, p.sdo.n, r0, N, tid);
-        if (tid < BQ) {
-            const int r = r0 + tid;
-            lse_r = (r < N) ? p.lse[row_off + r] * kLog2e : __builtin_huge_valf();
-        } else if (tid < 2 * BQ) {
-            const int r = r0 + tid - BQ;
-            del_r = (r < N) ? p.delta[row_off + r] : 0.0f;
-        }
+        const int r = r0 + rt_row;
+        const size_t rc = row_off + min(r, N - 1);
+        const float x = rt_kind == 0 ? p.lse[rc] : p.delta[rc];
+        row_r = rt_kind == 0 ? (r < N ? x * kLog2e : __builtin_huge_valf()) : (r < N ? x : 0.0f);
     };
     auto store_step = [&](int bufi) {
         qio.store_sw(qtile(bufi), QP, tid);
         doio.store_sw(dotile(bufi), QP, tid);
-        if (tid < BQ) lsetile(bufi)[tid] = lse_r;
-        else if (tid < 2 * BQ) deltile(bufi)[tid - BQ] = del_r;
+        lsetile(bufi)[tid] = row_r;  // LSE tile, then D_i tile, then the spare slots
     };
 
     f32x16 dkacc[NDT], dvacc[NDT];
@@ -178,8 +179,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     for (int it = 0; it < total; ++it) {
         const int bufi = it & 1;
-        const bool has_next = it + 1 < total;
-        if (has_next) load_step(it + 1);
+        // The last step reloads its own tiles into the idle buffer (never
+        // read), which keeps the body free of branches.
+        load_step(min(it + 1, total - 1));
 
         const int g = it / nq_iter;
         const int q0 = (qb_start + (it - g * nq_iter)) * BQ;
@@ -192,8 +194,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             const float* Ls = lsetile(bufi);
             const float* Ds = deltile(bufi);
             f32x16 s[NQT], dp[NQT];
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt) {
+            // S = Q K^T and dP = dO V^T for the 32 queries of tile qt.
+            auto mma_sd = [&](int qt) {
                 s[qt] = f32x16{};
                 dp[qt] = f32x16{};
 #pragma unroll
@@ -202,7 +204,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                     s[qt] = mfma32<DT>(lds_read8(Qs + off), kf[ks], s[qt]);
                     dp[qt] = mfma32<DT>(lds_read8(dOs + off), vf[ks], dp[qt]);
                 }
-            }
+            };
             // P = exp2(c*S - LSE2) and dS = P (dP - D), packed to 16 bits in the
             // B-operand order of the dV/dK products. Under the causal mask the
             // query of register r (local offset qoff(r) + 4h) is masked for
@@ -210,62 +212,57 @@ void bwd_dkdv_kernel(BwdParams p) {
             // constant per element), and under a sliding window also when
             // qoff(r) > key - q0 - 4h + W - 1.
             e16x8 pb[PVS], dsb[PVS];
-            {
-                const int kq = key - q0 - 4 * h;
-                const int kq_w = kq + W - 1;
-                // Dropout: the lane's key meets 4 consecutive queries per
-                // register group, exactly one Philox block each (bit r of
-                // keep[qt] for register r). dV takes P * M / (1-p); dP is
-                // scaled the same way before the softmax step.
-                uint32_t keep[NQT];
-                if constexpr (DROP) {
-                    const uint32_t bh = (uint32_t)(b * p.Hq + hkv * p.G + g);
+            e16x2 pp[PVS][4], dd[PVS][4];
+            const int kq = key - q0 - 4 * h;
+            const int kq_w = kq + W - 1;
+            // Dropout: the lane's key meets 4 consecutive queries per
+            // register group, exactly one Philox block each (bit r of
+            // keep[qt] for register r). dV takes P * M / (1-p); dP is
+            // scaled the same way before the softmax step.
+            uint32_t keep[NQT];
+            if constexpr (DROP) {
+                const uint32_t bh = (uint32_t)(b * p.Hq + hkv * p.G + g);
 #pragma unroll
-                    for (int qt = 0; qt < NQT; ++qt) {
-                        keep[qt] = 0;
+                for (int qt = 0; qt < NQT; ++qt) {
+                    keep[qt] = 0;
 #pragma unroll
-                        for (int gg = 0; gg < 4; ++gg)
-                            keep[qt] |= keep_nibble(p.drop, (uint32_t)key,
-                                                    (uint32_t)(q0 + qt * 32 + 8 * gg + 4 * h) >> 2, bh)
-                                        << (4 * gg);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < PVS; ++u) {
-                    const int qt = u >> 1;
-                    const int r0 = (u & 1) * 8;
-                    e16x2 pp[4], dd[4];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        float pv[2], dv[2];
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            const int r = r0 + 2 * e2 + w;
-                            const int qoff = qt * 32 + (r >> 2) * 8 + (r & 3);
-                            const int ql = qoff + h * 4;
-                            float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
-                            if (CAUSAL && kq > qoff) pe = 0.0f;
-                            if (WINDOW && qoff > kq_w) pe = 0.0f;
-                            if constexpr (DROP) {
-                                const bool kept = (keep[qt] >> r) & 1u;
-                                pv[w] = kept ? pe * p.drop.scale : 0.0f;
-                                dv[w] = pe * ((kept ? dp[qt][r] * p.drop.scale : 0.0f) - Ds[ql]);
-                            } else {
-                                pv[w] = pe;
-                                dv[w] = pe * (dp[qt][r] - Ds[ql]);
-                            }
-                        }
-                        pp[e2] = cvt2<DT>(pv[0], pv[1]);
-                        dd[e2] = cvt2<DT>(dv[0], dv[1]);
-                    }
-                    pb[u] = cat8(pp[0], pp[1], pp[2], pp[3]);
-                    dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
+                    for (int gg = 0; gg < 4; ++gg)
+                        keep[qt] |= keep_nibble(p.drop, (uint32_t)key,
+                                                (uint32_t)(q0 + qt * 32 + 8 * gg + 4 * h) >> 2, bh)
+                                    << (4 * gg);
                 }
             }
-            // dV^T += dO^T P and dK^T += Q^T dS. The transposed operands of
-            // contraction step u+1 are read from LDS before the products of
-            // step u are issued, so the reads overlap the matrix work.
-            e16x8 a_do[NDT], a_q[NDT];
+            // One pair of registers (r, r+1) of contraction step u.
+            auto softmax_pair = [&](int u, int e2) {
+                const int qt = u >> 1;
+                const int r0 = (u & 1) * 8;
+                float pv[2], dv[2];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const int r = r0 + 2 * e2 + w;
+                    const int qoff = qt * 32 + (r >> 2) * 8 + (r & 3);
+                    const int ql = qoff + h * 4;
+                    float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
+                    if (CAUSAL && kq > qoff) pe = 0.0f;
+                    if (WINDOW && qoff > kq_w) pe = 0.0f;
+                    if constexpr (DROP) {
+                        const bool kept = (keep[qt] >> r) & 1u;
+                        pv[w] = kept ? pe * p.drop.scale : 0.0f;
+                        dv[w] = pe * ((kept ? dp[qt][r] * p.drop.scale : 0.0f) - Ds[ql]);
+                    } else {
+                        pv[w] = pe;
+                        dv[w] = pe * (dp[qt][r] - Ds[ql]);
+                    }
+                }
+                pp[u][e2] = cvt2<DT>(pv[0], pv[1]);
+                dd[u][e2] = cvt2<DT>(dv[0], dv[1]);
+            };
+            auto pack = [&](int u) {
+                pb[u] = cat8(pp[u][0], pp[u][1], pp[u][2], pp[u][3]);
+                dsb[u] = cat8(dd[u][0], dd[u][1], dd[u][2], dd[u][3]);
+            };
+            // dV^T += dO^T P and dK^T += Q^T dS for contraction step u, with
+            // dO^T and Q^T read transposed from the row-major tiles.
             auto read_ops = [&](int u, e16x8* ado, e16x8* aq) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
@@ -275,26 +272,128 @@ void bwd_dkdv_kernel(BwdParams p) {
                     aq[dt] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o0 + 8 * QP));
                 }
             };
-            // (d = 256 has no registers to spare for the look-ahead copy.)
-            constexpr bool LOOKAHEAD = NDT <= 4;
-            read_ops(0, a_do, a_q);
+            if constexpr (NQT == 2) {
+                // Software pipeline of one step (d <= 128), pinned in order by
+                // scheduling barriers between small chunks:
+                //   A0: S/dP products of query tile 0, their row reads kept
+                //       two steps ahead;
+                //   A1: those of tile 1, with the softmax of tile 0 and the
+                //       transposed reads of the first dV/dK step in their
+                //       shadow;
+                //   C0: the first two dV/dK steps, with the softmax of tile 1
+                //       and the next transposed reads in their shadow;
+                //   C1: the last two dV/dK steps.
+                constexpr int NA = 2 * KS;  // row-read pairs of both tiles
+                e16x8 ra_q[3], ra_d[3];     // ring of prefetched row operands
+                auto rd = [&](int idx) {
+                    const int qt = idx / KS, ks = idx % KS;
+                    const int off = sw_off(qt * 32 + l32, ks * 16 + h * 8, QP);
+                    ra_q[idx % 3] = lds_read8(Qs + off);
+                    ra_d[idx % 3] = lds_read8(dOs + off);
+                };
+                auto mma_step = [&](int idx) {
+                    const int qt = idx / KS, ks = idx % KS;
+                    s[qt] = mfma32<DT>(ra_q[idx % 3], kf[ks], s[qt]);
+                    dp[qt] = mfma32<DT>(ra_d[idx % 3], vf[ks], dp[qt]);
+                };
+                e16x8 opA_d[NDT], opA_q[NDT], opB_d[NDT], opB_q[NDT];
+                auto tr_read = [&](int u, int dt, e16x8* ado, e16x8* aq) {
+                    const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, QP);
+                    ado[dt] = join8(lds_read_tr4(dOs + o0), lds_read_tr4(dOs + o0 + 8 * QP));
+                    aq[dt] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o0 + 8 * QP));
+                };
+                s[0] = f32x16{};
+                dp[0] = f32x16{};
+                s[1] = f32x16{};
+                dp[1] = f32x16{};
+                rd(0);
+                rd(1);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-                e16x8 n_do[NDT], n_q[NDT];
-                if (LOOKAHEAD && u + 1 < PVS) read_ops(u + 1, n_do, n_q);
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    mfma32_agpr<DT>(dvacc[dt], a_do[dt], pb[u]);
-                    mfma32_agpr<DT>(dkacc[dt], a_q[dt], dsb[u]);
+                for (int ks = 0; ks < KS; ++ks) {  // A0
+                    rd(ks + 2);
+                    mma_step(ks);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                if (!LOOKAHEAD && u + 1 < PVS) read_ops(u + 1, a_do, a_q);
-                if (LOOKAHEAD && u + 1 < PVS) {
+                constexpr int PAIRS_A1 = (8 + KS - 1) / KS;  // softmax pairs per A1 chunk
+                constexpr int TR_A1 = (NDT + KS - 1) / KS;   // transposed-read groups per chunk
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) { a_do[dt] = n_do[dt]; a_q[dt] = n_q[dt]; }
+                for (int ks = 0; ks < KS; ++ks) {  // A1
+                    if (KS + ks + 2 < NA) rd(KS + ks + 2);
+                    mma_step(KS + ks);
+#pragma unroll
+                    for (int j = 0; j < PAIRS_A1; ++j) {
+                        const int pr = ks * PAIRS_A1 + j;
+                        if (pr < 8) softmax_pair(pr / 4, pr % 4);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TR_A1; ++j) {
+                        const int dt = ks * TR_A1 + j;
+                        if (dt < NDT) tr_read(0, dt, opA_d, opA_q);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                pack(0);
+                pack(1);
+                // C0: dV/dK steps u = 0 (operands A) and u = 1 (operands B);
+                // the reads for u = 1 go into B while u = 0 runs, those for
+                // u = 2 into A while u = 1 runs.
+#pragma unroll
+                for (int k = 0; k < 2 * NDT; ++k) {
+                    const int u = k / NDT, dt = k % NDT;
+                    if (u == 0) {
+                        mfma32_agpr<DT>(dvacc[dt], opA_d[dt], pb[0]);
+                        mfma32_agpr<DT>(dkacc[dt], opA_q[dt], dsb[0]);
+                        tr_read(1, dt, opB_d, opB_q);
+                    } else {
+                        mfma32_agpr<DT>(dvacc[dt], opB_d[dt], pb[1]);
+                        mfma32_agpr<DT>(dkacc[dt], opB_q[dt], dsb[1]);
+                        tr_read(2, dt, opA_d, opA_q);
+                    }
+#pragma unroll
+                    for (int j = 0; j < (8 + 2 * NDT - 1) / (2 * NDT); ++j) {
+                        const int pr = k * ((8 + 2 * NDT - 1) / (2 * NDT)) + j;
+                        if (pr < 8) softmax_pair(2 + pr / 4, pr % 4);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                pack(2);
+                pack(3);
+#pragma unroll
+                for (int k = 0; k < 2 * NDT; ++k) {  // C1: u = 2 (A), u = 3 (B)
+                    const int u = 2 + k / NDT, dt = k % NDT;
+                    if (u == 2) {
+                        mfma32_agpr<DT>(dvacc[dt], opA_d[dt], pb[2]);
+                        mfma32_agpr<DT>(dkacc[dt], opA_q[dt], dsb[2]);
+                        tr_read(3, dt, opB_d, opB_q);
+                    } else {
+                        mfma32_agpr<DT>(dvacc[dt], opB_d[dt], pb[3]);
+                        mfma32_agpr<DT>(dkacc[dt], opB_q[dt], dsb[3]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int qt = 0; qt < NQT; ++qt) mma_sd(qt);
+#pragma unroll
+                for (int u = 0; u < PVS; ++u) {
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) softmax_pair(u, e2);
+                    pack(u);
+                }
+                e16x8 a_do[NDT], a_q[NDT];
+#pragma unroll
+                for (int u = 0; u < PVS; ++u) {
+                    read_ops(u, a_do, a_q);
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        mfma32_agpr<DT>(dvacc[dt], a_do[dt], pb[u]);
+                        mfma32_agpr<DT>(dkacc[dt], a_q[dt], dsb[u]);
+                    }
                 }
             }
         }
-        if (has_next) store_step(bufi ^ 1);
+        store_step(bufi ^ 1);
         __syncthreads();
     }
 

@@ -16,16 +16,19 @@ struct TileIO {
     static constexpr int NCH = (CHUNKS + T - 1) / T;
     uint4 r[NCH];
 
+    // Rows r0 .. r0+ROWS-1 through a buffer resource that ends with row
+    // N - 1, so rows at or past N read as zeros with no per-row arithmetic
+    // or branch. Requires (N - 1) * sn * 2 + D * 2 < 2^32 and r0 < N.
     __device__ __forceinline__ void load(const e16* head, long long sn, int r0, int N, int tid) {
+        const uint32_t sn2 = (uint32_t)sn * 2u;
+        const auto rsrc = buf_rsrc(head + (long long)r0 * sn, (uint32_t)(N - r0 - 1) * sn2 + D * 2);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * T;
             if (CHUNKS % T == 0 || c < CHUNKS) {
                 const int row = c / CPR;
                 const int col = c - row * CPR;
-                r[i] = (r0 + row < N)
-                           ? *reinterpret_cast<const uint4*>(head + (r0 + row) * sn + col * 8)
-                           : zero4();
+                r[i] = buf_load16(rsrc, (uint32_t)row * sn2 + (uint32_t)col * 16u);
             }
         }
     }

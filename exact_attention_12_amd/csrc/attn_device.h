@@ -135,6 +135,19 @@ __device__ __forceinline__ e16x8 join8(e16x4 a, e16x4 b) {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Raw buffer access: a resource over `bytes` bytes from `base` (wave-uniform);
+// 16-byte loads at byte offsets at or past `bytes` return zeros (the buffer
+// unit's range check), so tile loaders need no per-row bounds arithmetic.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Stores four fp32 values as four 16-bit values (8 bytes).
 template <int DT>
 __device__ __forceinline__ void store4(e16* dst, float a, float b, float c, float d) {
