@@ -80,7 +80,9 @@ typedef enum attn_status {
     ATTN_ERR_HIP = 8,        /* the HIP runtime refused a launch */
     ATTN_ERR_WINDOW = 9,     /* unknown mask kind, window < 0, or a window (>= 1)
                                 without the causal mask */
-    ATTN_ERR_STRIDE = 10,    /* a stride is negative */
+    ATTN_ERR_STRIDE = 10,    /* a stride is negative, or one head's N rows span 2^31
+                                elements or more (rows are addressed with 32-bit
+                                byte offsets) */
     ATTN_ERR_DTYPE = 11,     /* unknown element type */
     ATTN_ERR_PASSES = 12,    /* passes is 0 or has bits other than ATTN_BWD_ALL */
     ATTN_ERR_DROPOUT = 13    /* dropout_p is not in [0, 1) */
@@ -197,7 +199,8 @@ typedef enum attn_mask_kind {
  * One [B, H, N, d] operand in device memory: element (b, h, n, e) is at
  * data + b*stride_b + h*stride_h + n*stride_n + e, strides counted in
  * elements, the d elements of a row contiguous. Strides must be >= 0 and
- * multiples of 8 (every row starts 16-byte aligned), data 16-byte aligned.
+ * multiples of 8 (every row starts 16-byte aligned), data 16-byte aligned,
+ * and (N - 1) * stride_n + d < 2^31.
  *   contiguous BHSD: stride_b = H*N*d, stride_h = N*d, stride_n = d
  *   contiguous BSHD: stride_b = N*H*d, stride_h = d,   stride_n = H*d
  * Output views must not overlap each other or the inputs.
