@@ -124,21 +124,20 @@ void fwd_kernel(FwdParams p) {
     const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
 
     uint4 kreg[NCH], vreg[NCH];
+    // K/V rows kv0 .. kv0+BC-1 through buffer resources ending at row N-1:
+    // rows past the end read as zeros, with no per-row bounds arithmetic.
     auto load_tile = [&](int kv0) {
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * T;
             if (CHUNKS % T == 0 || c < CHUNKS) {
                 const int row = c / CPR;
                 const int col = c - row * CPR;
-                const int key = kv0 + row;
-                if (key < N) {
-                    kreg[i] = *reinterpret_cast<const uint4*>(Kh + key * skn + col * 8);
-                    vreg[i] = *reinterpret_cast<const uint4*>(Vh + key * svn + col * 8);
-                } else {
-                    kreg[i] = zero4();
-                    vreg[i] = zero4();
-                }
+                kreg[i] = buf_load16(rk, (uint32_t)row * sk2 + (uint32_t)col * 16u);
+                vreg[i] = buf_load16(rv, (uint32_t)row * sv2 + (uint32_t)col * 16u);
             }
         }
     };
@@ -157,8 +156,59 @@ void fwd_kernel(FwdParams p) {
         }
     };
 
-    load_tile(kb_begin * BC);
-    store_tile(kb_begin & 1);
+    // d <= 128 (64-key tiles): tiles go straight from memory to LDS. Each
+    // 64-lane buffer load with the LDS flag writes 64 consecutive 16-byte
+    // chunks; lane i of load j covers chunk 64j + i of the padded tile, i.e.
+    // row (64j + i) / (pitch / 8), chunk (64j + i) % (pitch / 8). Padding
+    // chunks get an offset past the end of the buffer, so they are written
+    // with zeros, and so are rows at or past N. No registers or LDS stores
+    // are spent on staging.
+    constexpr bool DIRECT = BC == 64;
+    constexpr int CKK = KP / 8, CKV = VP / 8;           // chunks per padded row
+    constexpr int NLK = BC * CKK / 64, NLV = BC * CKV / 64;  // loads per tile
+    constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
+    static_assert(!DIRECT || (BC * CKK % 64 == 0 && BC * CKV % 64 == 0), "tile must be whole loads");
+    uint32_t offk[DIRECT ? LPWK : 1], offv[DIRECT ? LPWV : 1];
+    if constexpr (DIRECT) {
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKK, ch = chunk - row * CKK;
+            offk[i] = ch < CPR ? (uint32_t)row * sk2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKV, ch = chunk - row * CKV;
+            offv[i] = ch < CPR ? (uint32_t)row * sv2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+        }
+    }
+    auto issue_tile = [&](int kv0, int bufi) {
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
+        char* kb_lds = reinterpret_cast<char*>(smem + bufi * BUF);
+        char* vb_lds = kb_lds + BC * KP * 2;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int j = wave + i * NW;
+            if (j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int j = wave + i * NW;
+            if (j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
+        }
+    };
+
+    if constexpr (DIRECT) {
+        issue_tile(kb_begin * BC, kb_begin & 1);
+        __builtin_amdgcn_s_waitcnt(0);
+    } else {
+        load_tile(kb_begin * BC);
+        store_tile(kb_begin & 1);
+    }
     __syncthreads();
 
     f32x16 oacc[NDT];
@@ -176,8 +226,12 @@ void fwd_kernel(FwdParams p) {
 
     for (int kb = kb_begin; kb < kb_end; ++kb) {
         const int bufi = kb & 1;
-        const bool has_next = kb + 1 < kb_end;
-        if (has_next) load_tile((kb + 1) * BC);
+        // The last step reloads its own tile into the idle buffer (never
+        // read again), so the loads and stores need no branch.
+        if constexpr (DIRECT)
+            issue_tile(min(kb + 1, kb_end - 1) * BC, bufi ^ 1);
+        else
+            load_tile(min(kb + 1, kb_end - 1) * BC);
 
         const int kv0 = kb * BC;
         const e16* Ks = smem + bufi * BUF;
@@ -185,12 +239,35 @@ void fwd_kernel(FwdParams p) {
         const bool active = !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
         if (active) {
             f32x16 s[NKT];
+            if constexpr (D <= 128) {
+                // S^T = K Q^T with the K row reads kept two products ahead,
+                // pinned in order by scheduling barriers.
+                constexpr int NS = NKT * KS;
+                e16x8 kr[3];
+                auto rdk = [&](int idx) {
+                    const int kt = idx / KS, ks = idx % KS;
+                    kr[idx % 3] = lds_read8(Ks + (kt * 32 + l32) * KP + h * 8 + ks * 16);
+                };
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                s[kt] = f32x16{};
-                const e16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
+                for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
+                rdk(0);
+                rdk(1);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32<DT>(lds_read8(kp + ks * 16), qf[ks], s[kt]);
+                for (int idx = 0; idx < NS; ++idx) {
+                    if (idx + 2 < NS) rdk(idx + 2);
+                    s[idx / KS] = mfma32<DT>(kr[idx % 3], qf[idx % KS], s[idx / KS]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    s[kt] = f32x16{};
+                    const e16* kp = Ks + (kt * 32 + l32) * KP + h * 8;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        s[kt] = mfma32<DT>(lds_read8(kp + ks * 16), qf[ks], s[kt]);
+                }
             }
             // Keys outside [lo, hi] (relative to kv0 + 4h) are masked: the
             // tail beyond N, keys after the row (causal) and keys before its
@@ -249,37 +326,70 @@ void fwd_kernel(FwdParams p) {
                                     << (4 * g);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < PVS; ++u) {
+            // Probabilities of register pair (2e, 2e+1) of contraction step u
+            // (16 keys), packed in the B-operand order of O^T += V^T P^T.
+            e16x2 pr[PVS][4];
+            auto exp_pair = [&](int u, int e) {
                 const int kt = u >> 1;
-                const int r0 = (u & 1) * 8;
-                e16x2 pr[4];
+                const int r = (u & 1) * 8 + 2 * e;
+                const float a0 = fast_exp2(fmaf(s[kt][r], c, -m_new));
+                const float a1 = fast_exp2(fmaf(s[kt][r + 1], c, -m_new));
+                lsum += a0 + a1;
+                if constexpr (DROP)
+                    pr[u][e] = cvt2<DT>(((keep[kt] >> r) & 1u) ? a0 : 0.0f,
+                                        ((keep[kt] >> (r + 1)) & 1u) ? a1 : 0.0f);
+                else
+                    pr[u][e] = cvt2<DT>(a0, a1);
+            };
+            auto v_op = [&](int u, int dt) {
+                const e16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
+                return join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32));
+            };
+            if constexpr (D <= 128) {
+                // The products of step u run with the exponentials of step
+                // u + 1 and its transposed V reads in their shadow.
+                constexpr int EPD = (4 + NDT - 1) / NDT;  // exp pairs per product
+                e16x8 va[2][NDT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a0 = fast_exp2(fmaf(s[kt][r0 + 2 * e], c, -m_new));
-                    const float a1 = fast_exp2(fmaf(s[kt][r0 + 2 * e + 1], c, -m_new));
-                    lsum += a0 + a1;
-                    if constexpr (DROP)
-                        pr[e] = cvt2<DT>(((keep[kt] >> (r0 + 2 * e)) & 1u) ? a0 : 0.0f,
-                                         ((keep[kt] >> (r0 + 2 * e + 1)) & 1u) ? a1 : 0.0f);
-                    else
-                        pr[e] = cvt2<DT>(a0, a1);
+                for (int e = 0; e < 4; ++e) exp_pair(0, e);
+                pb[0] = cat8(pr[0][0], pr[0][1], pr[0][2], pr[0][3]);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) va[0][dt] = v_op(0, dt);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < PVS; ++u) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        oacc[dt] = mfma32<DT>(va[u & 1][dt], pb[u], oacc[dt]);
+                        if (u + 1 < PVS) {
+                            va[(u + 1) & 1][dt] = v_op(u + 1, dt);
+#pragma unroll
+                            for (int j = 0; j < EPD; ++j)
+                                if (dt * EPD + j < 4) exp_pair(u + 1, dt * EPD + j);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (u + 1 < PVS)
+                        pb[u + 1] = cat8(pr[u + 1][0], pr[u + 1][1], pr[u + 1][2], pr[u + 1][3]);
                 }
-                pb[u] = cat8(pr[0], pr[1], pr[2], pr[3]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < PVS; ++u) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) exp_pair(u, e);
+                    pb[u] = cat8(pr[u][0], pr[u][1], pr[u][2], pr[u][3]);
+                }
+#pragma unroll
+                for (int u = 0; u < PVS; ++u)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32<DT>(v_op(u, dt), pb[u], oacc[dt]);
             }
             l += lsum;
-
-#pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-                const e16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const e16x8 a = join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32));
-                    oacc[dt] = mfma32<DT>(a, pb[u], oacc[dt]);
-                }
-            }
         }
-        if (has_next) store_tile(bufi ^ 1);
+        if constexpr (DIRECT)
+            __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
+        else
+            store_tile(bufi ^ 1);
         __syncthreads();
     }
 
