@@ -134,7 +134,7 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     L.attn_bwd_ex.argtypes = [pp, tp, tp, tp, tp, vp, tp, tp, tp, tp, vp, sz, u, vp]
-    L.attn_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+    L.attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, vp]
     L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     dp = ctypes.POINTER(AttnDecodeProblem)
@@ -391,7 +391,8 @@ def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal
                 if not bits & PASS_BITS[p]:
                     continue
                 if p == "pre":
-                    _check(L.attn_bwd_preprocess(ov.data_ptr(), dov.data_ptr(), ws, wsb, B, Hq, Hkv, N, d, st))
+                    _check(L.attn_bwd_preprocess(ov.data_ptr(), dov.data_ptr(), lse.data_ptr(), ws, wsb,
+                                                 B, Hq, Hkv, N, d, st))
                 elif p == "dkdv":
                     _check(L.attn_bwd_dkdv(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), lse.data_ptr(),
                                            dov.data_ptr(), dkv.data_ptr(), dvv.data_ptr(), ws, wsb,

@@ -179,10 +179,16 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     return hip_status(attn::launch_fwd(p, pr->dtype, pr->d, mask, plan, static_cast<hipStream_t>(stream)));
 }
 
-size_t workspace_bytes_for(int B, int Hq, int Hkv, int N, int d) {
-    if (check_shape(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
+// Two float32 per query row, each array 256-byte aligned: D_i, then
+// LSE_i * log2(e).
+size_t row_terms_bytes(int B, int Hq, int N) {
     const size_t bytes = (size_t)B * Hq * N * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
+}
+
+size_t workspace_bytes_for(int B, int Hq, int Hkv, int N, int d) {
+    if (check_shape(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
+    return 2 * row_terms_bytes(B, Hq, N);
 }
 
 // Shared validation and dispatch of every backward entry point. Only the
@@ -206,7 +212,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     if (kv) { ts[n++] = dk; ts[n++] = dv; }
     attn_status st = check_null(ts, n);
     if (st != ATTN_OK) return st;
-    if (main && !lse) return ATTN_ERR_NULL;
+    if (!lse) return ATTN_ERR_NULL;  // every pass reads it (the preprocess rescales it)
     st = check_shape(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d);
     if (st != ATTN_OK) return st;
     int mask = 0, window = 0;
@@ -226,7 +232,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
         return ATTN_ERR_WORKSPACE;
     st = check_layout(ts, n, pr->N, pr->d);
     if (st != ATTN_OK) return st;
-    if ((main && !aligned16(lse)) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
+    if (!aligned16(lse) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
 
     const attn_tensor none = {nullptr, 0, 0, 0};
     auto or_none = [&](const attn_tensor* t, bool used) -> const attn_tensor& {
@@ -237,12 +243,14 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.k = or_none(k, main).data;
     p.v = or_none(v, main).data;
     p.o = or_none(o, pre).data;
-    p.lse = main ? lse : nullptr;
+    p.lse = lse;
     p.dout = dout->data;
     p.dq = or_none(dq, qq).data;
     p.dk = or_none(dk, kv).data;
     p.dv = or_none(dv, kv).data;
     p.delta = static_cast<float*>(const_cast<void*>(workspace));
+    p.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                      row_terms_bytes(pr->B, pr->Hq, pr->N));
     p.sq = strides_of(or_none(q, main));
     p.sk = strides_of(or_none(k, main));
     p.sv = strides_of(or_none(v, main));
@@ -447,10 +455,10 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
                      scale, 1, window, stream, attn::kBwdAll);
 }
 
-attn_status attn_bwd_preprocess(const void* o, const void* dout, void* workspace,
+attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                                 void* stream) {
-    return bwd_plain(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr, nullptr, workspace,
+    return bwd_plain(nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr, nullptr, workspace,
                      workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, 0, stream, attn::kBwdPre);
 }
 

@@ -60,7 +60,10 @@ void bwd_pre_kernel(BwdParams p, long long rows) {
     acc += __shfl_xor(acc, 4);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 1);
-    if (row < rows && j == 0) p.delta[row] = acc;
+    if (row < rows && j == 0) {
+        p.delta[row] = acc;
+        p.lse2[row] = p.lse[row] * kLog2e;  // the dK/dV pass's log2-domain LSE
+    }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -135,6 +138,62 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int nq_iter = qb_stop - qb_start;
     const int total = p.G * nq_iter;
 
+    // d <= 128: tiles go straight from memory to LDS. Each 64-lane buffer
+    // load with the LDS flag fills 64 consecutive 16-byte chunks; lane i of
+    // load j covers physical chunk (64j + i) % (QP / 8) of row (64j + i) /
+    // (QP / 8), which holds logical chunk (physical ^ (row & 7)) of the
+    // swizzled layout. Chunks past d (padding) and rows past N get offsets
+    // beyond the buffer and read as zeros. The row terms (log2-domain LSE
+    // and D_i, written by the preprocess) arrive the same way, 4 bytes per
+    // lane; past N they read as zeros, which is harmless because those Q
+    // and dO rows are zero too.
+    constexpr bool DIRECT = BQ == 64;
+    constexpr int CKQ = QP / 8;
+    constexpr int NLQ = BQ * CKQ / 64;
+    constexpr int LPWQ = (NLQ + NW - 1) / NW;
+    static_assert(!DIRECT || BQ * CKQ % 64 == 0, "tile must be whole loads");
+    uint32_t offq[DIRECT ? LPWQ : 1], offd[DIRECT ? LPWQ : 1];
+    if constexpr (DIRECT) {
+        const uint32_t sq2 = (uint32_t)p.sq.n * 2u, sd2 = (uint32_t)p.sdo.n * 2u;
+#pragma unroll
+        for (int i = 0; i < LPWQ; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKQ;
+            const int lc = (chunk - row * CKQ) ^ (row & 7);
+            offq[i] = lc < D / 8 ? (uint32_t)row * sq2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+            offd[i] = lc < D / 8 ? (uint32_t)row * sd2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+        }
+    }
+    auto issue_step = [&](int it, int bufi) {
+        const int g = it / nq_iter;
+        const int qb = qb_start + (it - g * nq_iter);
+        const int hq = hkv * p.G + g;
+        const size_t row_off = ((size_t)b * p.Hq + hq) * N;
+        const int r0 = qb * BQ;
+        const uint32_t sq2 = (uint32_t)p.sq.n * 2u, sd2 = (uint32_t)p.sdo.n * 2u;
+        const auto rq = buf_rsrc(static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h +
+                                     (long long)r0 * p.sq.n,
+                                 (uint32_t)(N - r0 - 1) * sq2 + D * 2);
+        const auto rd = buf_rsrc(static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h +
+                                     (long long)r0 * p.sdo.n,
+                                 (uint32_t)(N - r0 - 1) * sd2 + D * 2);
+        char* qt_lds = reinterpret_cast<char*>(qtile(bufi));
+        char* dt_lds = reinterpret_cast<char*>(dotile(bufi));
+#pragma unroll
+        for (int i = 0; i < LPWQ; ++i) {
+            const int j = wave + i * NW;
+            if (j < NLQ) {
+                buf_load16_to_lds(rq, qt_lds + j * 1024, offq[i]);
+                buf_load16_to_lds(rd, dt_lds + j * 1024, offd[i]);
+            }
+        }
+        if (wave < 2) {
+            const float* src = (wave == 0 ? p.lse2 : p.delta) + row_off + r0;
+            const auto rr = buf_rsrc(src, (uint32_t)(N - r0) * 4u);
+            buf_load4_to_lds(rr, wave == 0 ? lsetile(bufi) : deltile(bufi), (uint32_t)lane * 4u);
+        }
+    };
+
     TileIO<D, BQ, T> qio, doio;
     // Row terms of the step: threads 0 .. BQ-1 fetch log2-domain LSE, BQ ..
     // 2BQ-1 the D_i; the others repeat a D_i fetch into a spare LDS slot, so
@@ -152,8 +211,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         doio.load(static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h, p.sdo.n, r0, N, tid);
         const int r = r0 + rt_row;
         const size_t rc = row_off + min(r, N - 1);
-        const float x = rt_kind == 0 ? p.lse[rc] : p.delta[rc];
-        row_r = rt_kind == 0 ? (r < N ? x * kLog2e : __builtin_huge_valf()) : (r < N ? x : 0.0f);
+        const float x = rt_kind == 0 ? p.lse2[rc] : p.delta[rc];
+        row_r = rt_kind == 0 ? (r < N ? x : __builtin_huge_valf()) : (r < N ? x : 0.0f);
     };
     auto store_step = [&](int bufi) {
         qio.store_sw(qtile(bufi), QP, tid);
@@ -172,8 +231,13 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
 
     if (total > 0) {
-        load_step(0);
-        store_step(0);
+        if constexpr (DIRECT) {
+            issue_step(0, 0);
+            __builtin_amdgcn_s_waitcnt(0);
+        } else {
+            load_step(0);
+            store_step(0);
+        }
     }
     __syncthreads();
 
@@ -181,7 +245,10 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int bufi = it & 1;
         // The last step reloads its own tiles into the idle buffer (never
         // read), which keeps the body free of branches.
-        load_step(min(it + 1, total - 1));
+        if constexpr (DIRECT)
+            issue_step(min(it + 1, total - 1), bufi ^ 1);
+        else
+            load_step(min(it + 1, total - 1));
 
         const int g = it / nq_iter;
         const int q0 = (qb_start + (it - g * nq_iter)) * BQ;
@@ -393,7 +460,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                 }
             }
         }
-        store_step(bufi ^ 1);
+        if constexpr (DIRECT)
+            __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed in LDS
+        else
+            store_step(bufi ^ 1);
         __syncthreads();
     }
 

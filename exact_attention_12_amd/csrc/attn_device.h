@@ -147,6 +147,12 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// 4-byte variant: the 64 lanes fill 256 consecutive bytes of LDS.
+__device__ __forceinline__ void buf_load4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_dst,
+                                                 uint32_t byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 4,
+                                             byte_off, 0, 0, 0);
+}
 // The same load written straight to LDS: the 64 lanes of the wave store
 // their 16 bytes to 64 consecutive chunks starting at lds_dst (wave-uniform).
 __device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_dst,

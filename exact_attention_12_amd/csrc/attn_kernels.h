@@ -89,6 +89,7 @@ struct BwdParams {
     void* dk;
     void* dv;
     float* delta;  // [B, Hq, N] workspace: D_i = <dO_i, O_i>
+    float* lse2;   // [B, Hq, N] workspace: LSE_i * log2(e), written with D_i
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     int N;
     int Hq;

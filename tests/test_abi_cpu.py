@@ -92,7 +92,7 @@ def test_fwd_misaligned(L, which):
 
 def test_bwd_errors(L):
     need = L.attn_bwd_workspace_bytes(1, 2, 1, 8, 64)
-    assert need == 256
+    assert need == 512  # D_i and base-2 LSE, 256 bytes each
     assert bwd(L, ws=None) == 7
     assert bwd(L, ws_bytes=need - 1) == 7
     for i in range(9):
@@ -109,9 +109,9 @@ def test_bwd_errors(L):
 
 
 def test_workspace_bytes(L):
-    assert L.attn_bwd_workspace_bytes(1, 16, 16, 16384, 128) == 16 * 16384 * 4
-    assert L.attn_bwd_workspace_bytes(1, 1, 1, 1, 64) == 256
-    assert L.attn_bwd_workspace_bytes(2, 3, 1, 100, 80) == 2560  # 2400 rounded up to 256
+    assert L.attn_bwd_workspace_bytes(1, 16, 16, 16384, 128) == 2 * 16 * 16384 * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 1, 64) == 512
+    assert L.attn_bwd_workspace_bytes(2, 3, 1, 100, 80) == 2 * 2560  # 2400 rounded up to 256, twice
     assert L.attn_bwd_workspace_bytes(1, 3, 2, 100, 80) == 0
     assert L.attn_bwd_workspace_bytes(1, 2, 2, 100, 112) == 0
 
@@ -132,13 +132,15 @@ def test_fwd_plan(L):
 
 def test_pass_entry_points_validate(L):
     ws, wsb = P, 1 << 20
-    # preprocess: o, dout, workspace
-    assert L.attn_bwd_preprocess(None, P, ws, wsb, 1, 2, 1, 8, 64, None) == 1
-    assert L.attn_bwd_preprocess(P, None, ws, wsb, 1, 2, 1, 8, 64, None) == 1
-    assert L.attn_bwd_preprocess(P, P, None, wsb, 1, 2, 1, 8, 64, None) == 7
-    assert L.attn_bwd_preprocess(P, P + 2, ws, wsb, 1, 2, 1, 8, 64, None) == 6
-    assert L.attn_bwd_preprocess(P, P, ws, 4, 1, 2, 1, 8, 64, None) == 7
-    assert L.attn_bwd_preprocess(P, P, ws, wsb, 1, 2, 1, 8, 112, None) == 4
+    # preprocess: o, dout, lse, workspace
+    assert L.attn_bwd_preprocess(None, P, P, ws, wsb, 1, 2, 1, 8, 64, None) == 1
+    assert L.attn_bwd_preprocess(P, None, P, ws, wsb, 1, 2, 1, 8, 64, None) == 1
+    assert L.attn_bwd_preprocess(P, P, None, ws, wsb, 1, 2, 1, 8, 64, None) == 1
+    assert L.attn_bwd_preprocess(P, P, P, None, wsb, 1, 2, 1, 8, 64, None) == 7
+    assert L.attn_bwd_preprocess(P, P + 2, P, ws, wsb, 1, 2, 1, 8, 64, None) == 6
+    assert L.attn_bwd_preprocess(P, P, P + 4, ws, wsb, 1, 2, 1, 8, 64, None) == 6
+    assert L.attn_bwd_preprocess(P, P, P, ws, 4, 1, 2, 1, 8, 64, None) == 7
+    assert L.attn_bwd_preprocess(P, P, P, ws, wsb, 1, 2, 1, 8, 112, None) == 4
     # dK/dV pass: q, k, v, lse, dout, dk, dv, workspace
     for i in range(7):
         a = [P] * 7
@@ -253,7 +255,7 @@ def test_bwd_ex_validation(L):
                 ts[i] = T(sn=12)
                 assert bwd_ex(L, ts=ts, passes=bits) == 6, (bits, n)
     assert bwd_ex(L, lse=None, passes=2) == 1
-    assert bwd_ex(L, lse=None, passes=1, ws=None) == 7   # preprocess needs no lse
+    assert bwd_ex(L, lse=None, passes=1, ws=None) == 1   # the preprocess rescales lse too
     assert bwd_ex(L, wsb=16) == 7
     assert bwd_ex(L, ws=P + 8) == 6
     assert bwd_ex(L, pr=prob(dtype=5)) == 11
