@@ -57,7 +57,6 @@ void bwd_dq_kernel(BwdParams p) {
     const int qw0 = q0 + wave * 32;
     const int qrow = qw0 + l32;
 
-    for (int bufi = 0; bufi < 2; ++bufi) zero_pad_cols_sw<D>(smem + bufi * BUF, BC, KP, tid, T);
 
     e16x8 qf[KS], gf[KS];
     float lse2 = __builtin_huge_valf(), del = 0.0f;
@@ -83,11 +82,54 @@ void bwd_dq_kernel(BwdParams p) {
     const int W = WINDOW ? p.window : 0;
     const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
 
-    TileIO<D, BC, T> kio, vio;
-    kio.load(Kh, p.sk.n, kb_begin * BC, N, tid);
-    vio.load(Vh, p.sv.n, kb_begin * BC, N, tid);
-    kio.store_sw(smem + (kb_begin & 1) * BUF, KP, tid);
-    vio.store(smem + (kb_begin & 1) * BUF + BC * KP, VP, tid);
+    // K/V tiles go straight from memory to LDS: each 64-lane buffer load
+    // with the LDS flag fills 64 consecutive 16-byte chunks; lane i of load j
+    // covers chunk 64j + i of the padded tile (row = chunk / pitch-chunks).
+    // The K tile is swizzled, so that slot holds logical chunk slot ^ (row &
+    // 7). Chunks past d (padding) and rows past N read as zeros; lanes past
+    // the end of a tile whose chunk count is not a multiple of 64 are idle.
+    constexpr int CKK = KP / 8, CKV = VP / 8;
+    constexpr int NLK = (BC * CKK + 63) / 64, NLV = (BC * CKV + 63) / 64;
+    constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
+    uint32_t offk[LPWK], offv[LPWV];
+    {
+        const uint32_t sk2 = (uint32_t)p.sk.n * 2u, sv2 = (uint32_t)p.sv.n * 2u;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKK;
+            const int lc = (chunk - row * CKK) ^ (row & 7);
+            offk[i] = lc < D / 8 ? (uint32_t)row * sk2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKV;
+            const int lc = chunk - row * CKV;
+            offv[i] = lc < D / 8 ? (uint32_t)row * sv2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+        }
+    }
+    auto issue_tile = [&](int kv0, int bufi) {
+        const uint32_t sk2 = (uint32_t)p.sk.n * 2u, sv2 = (uint32_t)p.sv.n * 2u;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * p.sk.n, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * p.sv.n, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
+        char* k_lds = reinterpret_cast<char*>(smem + bufi * BUF);
+        char* v_lds = k_lds + BC * KP * 2;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int j = wave + i * NW;
+            if (j < NLK && (BC * CKK % 64 == 0 || j * 64 + lane < BC * CKK))
+                buf_load16_to_lds(rk, k_lds + j * 1024, offk[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int j = wave + i * NW;
+            if (j < NLV && (BC * CKV % 64 == 0 || j * 64 + lane < BC * CKV))
+                buf_load16_to_lds(rv, v_lds + j * 1024, offv[i]);
+        }
+    };
+    issue_tile(kb_begin * BC, kb_begin & 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     f32x16 dqacc[NDT];
@@ -101,27 +143,38 @@ void bwd_dq_kernel(BwdParams p) {
 
     for (int kb = kb_begin; kb < kb_end; ++kb) {
         const int bufi = kb & 1;
-        const bool has_next = kb + 1 < kb_end;
-        if (has_next) {
-            kio.load(Kh, p.sk.n, (kb + 1) * BC, N, tid);
-            vio.load(Vh, p.sv.n, (kb + 1) * BC, N, tid);
-        }
+        // The last step reloads its own tile into the idle buffer (never
+        // read again), so the loads need no branch.
+        issue_tile(min(kb + 1, kb_end - 1) * BC, bufi ^ 1);
         const int kv0 = kb * BC;
         const e16* Ks = smem + bufi * BUF;
         const e16* Vs = Ks + BC * KP;
         // Branch-free step: blocks past a wave's last query are masked to zero.
         {
             f32x16 s[NKT], dp[NKT];
+            // S^T = K Q^T and dP^T = V dO^T with the K and V row reads kept
+            // two products ahead, pinned in order by scheduling barriers.
+            constexpr int NS = NKT * KS;
+            e16x8 kr[3], vr[3];
+            auto rd = [&](int idx) {
+                const int kt = idx / KS, ks = idx % KS;
+                kr[idx % 3] = lds_read8(Ks + sw_off(kt * 32 + l32, ks * 16 + h * 8, KP));
+                vr[idx % 3] = lds_read8(Vs + (kt * 32 + l32) * VP + h * 8 + ks * 16);
+            };
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 s[kt] = f32x16{};
                 dp[kt] = f32x16{};
-                const e16* vp = Vs + (kt * 32 + l32) * VP + h * 8;
+            }
+            rd(0);
+            if (NS > 1) rd(1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    s[kt] = mfma32<DT>(lds_read8(Ks + sw_off(kt * 32 + l32, ks * 16 + h * 8, KP)), qf[ks], s[kt]);
-                    dp[kt] = mfma32<DT>(lds_read8(vp + ks * 16), gf[ks], dp[kt]);
-                }
+            for (int idx = 0; idx < NS; ++idx) {
+                if (idx + 2 < NS) rd(idx + 2);
+                s[idx / KS] = mfma32<DT>(kr[idx % 3], qf[idx % KS], s[idx / KS]);
+                dp[idx / KS] = mfma32<DT>(vr[idx % 3], gf[idx % KS], dp[idx / KS]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to 16 bits
             // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
@@ -180,10 +233,7 @@ void bwd_dq_kernel(BwdParams p) {
                 }
             }
         }
-        if (has_next) {
-            kio.store_sw(smem + (bufi ^ 1) * BUF, KP, tid);
-            vio.store(smem + (bufi ^ 1) * BUF + BC * KP, VP, tid);
-        }
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
         __syncthreads();
     }
 
