@@ -37,8 +37,10 @@
 //  * Scores are kept in the log2 domain: exp(scale*s - m) = exp2(c*s - m')
 //    with c = scale * log2(e).
 //  * K/V tiles are double buffered in LDS: the next tile's global loads are
-//    issued before the current tile's math and written to the other buffer
-//    after it, one barrier per step.
+//    issued before the current tile's math, one barrier per step. For
+//    d <= 128 buffer loads with the LDS flag write them straight into the
+//    other buffer (no staging registers, no LDS stores); larger d stage
+//    them in registers and store them after the math.
 //  * Causal: key blocks after the workgroup's last query are never loaded; a
 //    wave skips the math of blocks after its own last query; the diagonal
 //    blocks are masked per element. Heavy (late) query blocks are launched
