@@ -44,7 +44,7 @@ void bwd_dq_kernel(BwdParams p) {
     const int BH = p.B * p.Hq;
     const int nqb = (N + BQ - 1) / BQ;
     const int bid = blockIdx.x;
-    const int bh = bid % BH;
+    const int bh = xcd_head(bid % BH, BH);
     const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
     const int b = bh / p.Hq;
     const int hq = bh - b * p.Hq;

@@ -12,7 +12,7 @@
 // (batch, head, query block); the yunthe.com GQA page gives the KV-head
 // sharing (query head h reads KV head h / (Hq/Hkv)).
 //
-// Mapping onto the CDNA4 compute unit (4 waves per workgroup, 32 query rows
+// Mapping onto the CDNA4 compute unit (4 or 8 waves per workgroup, 32 query rows
 // per wave, BLOCK_KV keys per step):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (_f16 for fp16 inputs): K (from
 //    LDS) is the A operand, the wave's 32 query rows (kept in registers for
@@ -81,7 +81,7 @@ void fwd_kernel(FwdParams p) {
     // Workgroup -> (query block, batch*head). Under the causal mask the
     // latest (heaviest) query blocks come first.
     const int bid = blockIdx.x;
-    const int bh = bid % p.BH;
+    const int bh = xcd_head(bid % p.BH, p.BH);
     const int qb = CAUSAL ? (p.nqb - 1 - bid / p.BH) : (bid / p.BH);
     const int b = bh / p.Hq;
     const int hq = bh - b * p.Hq;

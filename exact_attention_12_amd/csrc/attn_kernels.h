@@ -50,6 +50,27 @@ __host__ __device__ constexpr int sw_off(int row, int col, int pitch) {
     return row * pitch + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
 }
 
+// Head index of a workgroup whose index has j = bid % BH as its fastest
+// part. The 8 XCDs of the chip (each with its own L2) receive workgroups
+// round robin, so XCD x gets the j = x mod 8; when BH is a multiple of 8 the
+// heads are renumbered so that XCD x runs the contiguous heads
+// x * BH/8 .. (x+1) * BH/8 - 1, i.e. whole GQA groups, whose query heads then
+// read their shared K and V through one L2.
+__host__ __device__ constexpr int xcd_head(int j, int BH) {
+    return BH % 8 == 0 ? (j % 8) * (BH / 8) + j / 8 : j;
+}
+
+constexpr bool xcd_head_is_permutation(int BH) {
+    for (int h = 0; h < BH; ++h) {
+        int hits = 0;
+        for (int j = 0; j < BH; ++j) hits += xcd_head(j, BH) == h;
+        if (hits != 1) return false;
+    }
+    return true;
+}
+static_assert(xcd_head_is_permutation(8) && xcd_head_is_permutation(32) &&
+              xcd_head_is_permutation(64) && xcd_head_is_permutation(12), "");
+
 // Mask modes, one kernel instantiation each: none, causal (keys j <= i) and
 // the causal sliding window (keys i - window < j <= i).
 enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
