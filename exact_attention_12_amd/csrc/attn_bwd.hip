@@ -141,7 +141,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     // d <= 128: tiles go straight from memory to LDS. Each 64-lane buffer
     // load with the LDS flag fills 64 consecutive 16-byte chunks; lane i of
     // load j covers physical chunk (64j + i) % (QP / 8) of row (64j + i) /
-    // (QP / 8), which holds logical chunk (physical ^ (row & 7)) of the
+    // (QP / 8), which holds logical chunk (physical ^ sw_swizzle(row)) of the
     // swizzled layout. Chunks past d (padding) and rows past N get offsets
     // beyond the buffer and read as zeros. The row terms (log2-domain LSE
     // and D_i, written by the preprocess) arrive the same way, 4 bytes per
@@ -159,7 +159,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         for (int i = 0; i < LPWQ; ++i) {
             const int chunk = (wave + i * NW) * 64 + lane;
             const int row = chunk / CKQ;
-            const int lc = (chunk - row * CKQ) ^ (row & 7);
+            const int lc = (chunk - row * CKQ) ^ sw_swizzle(row);
             offq[i] = lc < D / 8 ? (uint32_t)row * sq2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
             offd[i] = lc < D / 8 ? (uint32_t)row * sd2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
@@ -229,6 +229,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int j16 = lane & 15;
     const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
+    // Per-lane offsets into the swizzled Q and dO tiles; the other row and
+    // column blocks are immediate offsets (sw_off repeats every 16 rows and
+    // 32 columns). Row reads: chunk 2ks + h, ks even / odd. Transposing
+    // reads: rows tr_row and tr_row + 8.
+    const int qrd[2] = {sw_off(l32, h * 8, QP), sw_off(l32, 16 + h * 8, QP)};
+    const int qtr0 = sw_off(tr_row, tr_col, QP), qtr1 = sw_off(tr_row + 8, tr_col, QP);
 
     if (total > 0) {
         if constexpr (DIRECT) {
@@ -267,7 +273,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                 dp[qt] = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int off = sw_off(qt * 32 + l32, ks * 16 + h * 8, QP);
+                    const int off = qrd[ks & 1] + qt * 32 * QP + (ks >> 1) * 32;
                     s[qt] = mfma32<DT>(lds_read8(Qs + off), kf[ks], s[qt]);
                     dp[qt] = mfma32<DT>(lds_read8(dOs + off), vf[ks], dp[qt]);
                 }
@@ -333,10 +339,9 @@ void bwd_dkdv_kernel(BwdParams p) {
             auto read_ops = [&](int u, e16x8* ado, e16x8* aq) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    // Rows u*16 + tr_row and +8 share (row & 7) = tr_row.
-                    const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, QP);
-                    ado[dt] = join8(lds_read_tr4(dOs + o0), lds_read_tr4(dOs + o0 + 8 * QP));
-                    aq[dt] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o0 + 8 * QP));
+                    const int ob = u * 16 * QP + dt * 32;
+                    ado[dt] = join8(lds_read_tr4(dOs + qtr0 + ob), lds_read_tr4(dOs + qtr1 + ob));
+                    aq[dt] = join8(lds_read_tr4(Qs + qtr0 + ob), lds_read_tr4(Qs + qtr1 + ob));
                 }
             };
             if constexpr (NQT == 2) {
@@ -354,7 +359,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                 e16x8 ra_q[3], ra_d[3];     // ring of prefetched row operands
                 auto rd = [&](int idx) {
                     const int qt = idx / KS, ks = idx % KS;
-                    const int off = sw_off(qt * 32 + l32, ks * 16 + h * 8, QP);
+                    const int off = qrd[ks & 1] + qt * 32 * QP + (ks >> 1) * 32;
                     ra_q[idx % 3] = lds_read8(Qs + off);
                     ra_d[idx % 3] = lds_read8(dOs + off);
                 };
@@ -365,9 +370,9 @@ void bwd_dkdv_kernel(BwdParams p) {
                 };
                 e16x8 opA_d[NDT], opA_q[NDT], opB_d[NDT], opB_q[NDT];
                 auto tr_read = [&](int u, int dt, e16x8* ado, e16x8* aq) {
-                    const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, QP);
-                    ado[dt] = join8(lds_read_tr4(dOs + o0), lds_read_tr4(dOs + o0 + 8 * QP));
-                    aq[dt] = join8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o0 + 8 * QP));
+                    const int ob = u * 16 * QP + dt * 32;
+                    ado[dt] = join8(lds_read_tr4(dOs + qtr0 + ob), lds_read_tr4(dOs + qtr1 + ob));
+                    aq[dt] = join8(lds_read_tr4(Qs + qtr0 + ob), lds_read_tr4(Qs + qtr1 + ob));
                 };
                 s[0] = f32x16{};
                 dp[0] = f32x16{};

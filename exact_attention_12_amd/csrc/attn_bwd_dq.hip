@@ -98,7 +98,7 @@ void bwd_dq_kernel(BwdParams p) {
         for (int i = 0; i < LPWK; ++i) {
             const int chunk = (wave + i * NW) * 64 + lane;
             const int row = chunk / CKK;
-            const int lc = (chunk - row * CKK) ^ (row & 7);
+            const int lc = (chunk - row * CKK) ^ sw_swizzle(row);
             offk[i] = lc < D / 8 ? (uint32_t)row * sk2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
 #pragma unroll
@@ -140,6 +140,12 @@ void bwd_dq_kernel(BwdParams p) {
     const int j16 = lane & 15;
     const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
+    // Per-lane offsets into the swizzled K tile; the other row and column
+    // blocks are immediate offsets (sw_off repeats every 16 rows and 32
+    // columns). Row reads: chunk 2ks + h, ks even / odd. Transposing reads:
+    // rows tr_row and tr_row + 8.
+    const int krd[2] = {sw_off(l32, h * 8, KP), sw_off(l32, 16 + h * 8, KP)};
+    const int ktr0 = sw_off(tr_row, tr_col, KP), ktr1 = sw_off(tr_row + 8, tr_col, KP);
 
     for (int kb = kb_begin; kb < kb_end; ++kb) {
         const int bufi = kb & 1;
@@ -158,7 +164,7 @@ void bwd_dq_kernel(BwdParams p) {
             e16x8 kr[3], vr[3];
             auto rd = [&](int idx) {
                 const int kt = idx / KS, ks = idx % KS;
-                kr[idx % 3] = lds_read8(Ks + sw_off(kt * 32 + l32, ks * 16 + h * 8, KP));
+                kr[idx % 3] = lds_read8(Ks + krd[ks & 1] + kt * 32 * KP + (ks >> 1) * 32);
                 vr[idx % 3] = lds_read8(Vs + (kt * 32 + l32) * VP + h * 8 + ks * 16);
             };
 #pragma unroll
@@ -227,8 +233,8 @@ void bwd_dq_kernel(BwdParams p) {
             for (int u = 0; u < PVS; ++u) {
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const int o0 = sw_off(u * 16 + tr_row, dt * 32 + tr_col, KP);
-                    const e16x8 a = join8(lds_read_tr4(Ks + o0), lds_read_tr4(Ks + o0 + 8 * KP));
+                    const int ob = u * 16 * KP + dt * 32;
+                    const e16x8 a = join8(lds_read_tr4(Ks + ktr0 + ob), lds_read_tr4(Ks + ktr1 + ob));
                     dqacc[dt] = mfma32<DT>(a, dsb[u], dqacc[dt]);
                 }
             }

@@ -33,9 +33,14 @@ template <int D> struct FwdTile {
 //    groups per cycle) is conflict free when the pitch is 64 or 192 bytes
 //    modulo 256: v_pitch;
 //  * a tile read both ways uses the 64-mod-256 pitch with its 16-byte chunks
-//    XOR-swizzled by (row & 7), which keeps both patterns at their floor:
-//    sw_pitch and sw_off. The swizzle permutes chunks inside aligned groups
-//    of 8, so the pitch must hold round_up(chunks, 8) chunks.
+//    XOR-swizzled by bits 2..3 of the row: sw_pitch and sw_off. With that
+//    pitch rows r, r+4, r+8, r+12 start on the same bank; the swizzle moves
+//    them to four different 16-byte slots, so the 16 rows of a row read hit
+//    every bank once (4 cycles per 16-byte read instead of 8 with a swizzle
+//    by (row & 7), counted with SQ_LDS_BANK_CONFLICT), while each transposing
+//    read still sees one swizzle value per 4-row group (2 cycles, no
+//    conflicts). The swizzle permutes chunks inside aligned groups of 4, and
+//    the pitch holds round_up(chunks, 8) chunks.
 constexpr int k_pitch(int d) { return d + 8; }
 constexpr int pitch_64mod256(int row_bytes) {
     return (row_bytes + (((64 - row_bytes) % 128) + 128) % 128) / 2;
@@ -46,9 +51,24 @@ static_assert(v_pitch(64) == 96 && v_pitch(80) == 96 && v_pitch(128) == 160 && v
 static_assert(sw_pitch(64) == 96 && sw_pitch(80) == 160 && sw_pitch(128) == 160 && sw_pitch(256) == 288, "");
 
 // Element offset of (row, col) in a swizzled tile (chunk = 8 elements).
+__host__ __device__ constexpr int sw_swizzle(int row) { return (row >> 2) & 3; }
 __host__ __device__ constexpr int sw_off(int row, int col, int pitch) {
-    return row * pitch + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+    return row * pitch + (((col >> 3) ^ sw_swizzle(row)) << 3) + (col & 7);
 }
+// The swizzle repeats every 16 rows and stays inside 32-column groups, so
+// for 0 <= c < 32: sw_off(r + 16a, c + 32b) = sw_off(r, c) + 16a*pitch + 32b.
+// Kernels compute sw_off(r, c) once per lane and reach the other row and
+// column blocks through immediate offsets.
+constexpr bool sw_off_is_periodic(int pitch) {
+    for (int r = 0; r < 16; ++r)
+        for (int c = 0; c < 32; ++c)
+            for (int a = 0; a < 4; ++a)
+                for (int b = 0; b < 8; ++b)
+                    if (sw_off(r + 16 * a, c + 32 * b, pitch) != sw_off(r, c, pitch) + 16 * a * pitch + 32 * b)
+                        return false;
+    return true;
+}
+static_assert(sw_off_is_periodic(96) && sw_off_is_periodic(160) && sw_off_is_periodic(288), "");
 
 // Head index of a workgroup whose index has j = bid % BH as its fastest
 // part. The 8 XCDs of the chip (each with its own L2) receive workgroups
