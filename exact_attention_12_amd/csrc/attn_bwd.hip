@@ -27,6 +27,8 @@
 //     lane, so LSE_i and D_i are per-lane scalars; dQ^T += K^T dS^T with K^T
 //     read transposed from the K tile.
 
+#include <type_traits>
+
 #include "attn_bwd_common.h"
 
 namespace attn {
@@ -89,7 +91,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer resources
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int N = p.N;
@@ -137,6 +139,32 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int qb_stop = WINDOW ? min(nqb, (k0 + BK - 1 + W - 1) / BQ + 1) : nqb;
     const int nq_iter = qb_stop - qb_start;
     const int total = p.G * nq_iter;
+    // Query blocks that need no per-element mask form [qu_begin, qu_end):
+    // every query is at or after every key of the workgroup (q0 >= k0 + BK
+    // - 1) and, under a window, every key lies in every query's band
+    // (q0 + BQ - 1 < k0 + W). Rows past N need no mask either: their Q, dO
+    // and row terms read as zeros, so they add nothing to dK or dV. The
+    // masked blocks of all G heads run first, then the unmasked ones, each
+    // phase with its own copy of the step.
+    int qu_begin = qb_start, qu_end = qb_stop;
+    if (CAUSAL) qu_begin = min(qb_stop, max(qb_start, (k0 + BK - 1 + BQ - 1) / BQ));
+    if (WINDOW) {
+        const int t = k0 + W - BQ;
+        qu_end = max(qu_begin, min(qb_stop, t >= 0 ? t / BQ + 1 : 0));
+    }
+    const int nm_lo = qu_begin - qb_start;
+    const int nu = qu_end - qu_begin;
+    const int nm = nq_iter - nu;
+    const int nmG = p.G * nm;
+    const int nm1 = max(nm, 1), nu1 = max(nu, 1);
+    auto step_g = [&](int it) { return it < nmG ? it / nm1 : (it - nmG) / nu1; };
+    auto step_qb = [&](int it) {
+        if (it < nmG) {
+            const int r = it % nm1;
+            return r < nm_lo ? qb_start + r : qu_end + (r - nm_lo);
+        }
+        return qu_begin + (it - nmG) % nu1;
+    };
 
     // d <= 128: tiles go straight from memory to LDS. Each 64-lane buffer
     // load with the LDS flag fills 64 consecutive 16-byte chunks; lane i of
@@ -165,8 +193,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     }
     auto issue_step = [&](int it, int bufi) {
-        const int g = it / nq_iter;
-        const int qb = qb_start + (it - g * nq_iter);
+        const int g = step_g(it);
+        const int qb = step_qb(it);
         const int hq = hkv * p.G + g;
         const size_t row_off = ((size_t)b * p.Hq + hq) * N;
         const int r0 = qb * BQ;
@@ -182,7 +210,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < LPWQ; ++i) {
             const int j = wave + i * NW;
-            if (j < NLQ) {
+            if (NLQ % NW == 0 || j < NLQ) {
                 buf_load16_to_lds(rq, qt_lds + j * 1024, offq[i]);
                 buf_load16_to_lds(rd, dt_lds + j * 1024, offd[i]);
             }
@@ -202,8 +230,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int rt_kind = tid / BQ;        // 0: LSE, 1: D_i, 2+: spare
     const int rt_row = tid - rt_kind * BQ;
     auto load_step = [&](int it) {
-        const int g = it / nq_iter;
-        const int qb = qb_start + (it - g * nq_iter);
+        const int g = step_g(it);
+        const int qb = step_qb(it);
         const int hq = hkv * p.G + g;
         const size_t row_off = ((size_t)b * p.Hq + hq) * N;  // LSE, D_i: contiguous
         const int r0 = qb * BQ;
@@ -247,7 +275,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    for (int it = 0; it < total; ++it) {
+    auto run_step = [&](int it, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int bufi = it & 1;
         // The last step reloads its own tiles into the idle buffer (never
         // read), which keeps the body free of branches.
@@ -256,8 +285,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         else
             load_step(min(it + 1, total - 1));
 
-        const int g = it / nq_iter;
-        const int q0 = (qb_start + (it - g * nq_iter)) * BQ;
+        const int g = step_g(it);
+        const int q0 = step_qb(it) * BQ;
         // Every step runs for every wave (no data-dependent branch in the
         // loop body): a wave whose keys all lie after this query block just
         // contributes zeros through the mask.
@@ -316,8 +345,8 @@ void bwd_dkdv_kernel(BwdParams p) {
                     const int qoff = qt * 32 + (r >> 2) * 8 + (r & 3);
                     const int ql = qoff + h * 4;
                     float pe = fast_exp2(fmaf(s[qt][r], c, -Ls[ql]));
-                    if (CAUSAL && kq > qoff) pe = 0.0f;
-                    if (WINDOW && qoff > kq_w) pe = 0.0f;
+                    if (MASKED && CAUSAL && kq > qoff) pe = 0.0f;
+                    if (MASKED && WINDOW && qoff > kq_w) pe = 0.0f;
                     if constexpr (DROP) {
                         const bool kept = (keep[qt] >> r) & 1u;
                         pv[w] = kept ? pe * p.drop.scale : 0.0f;
@@ -470,7 +499,10 @@ void bwd_dkdv_kernel(BwdParams p) {
         else
             store_step(bufi ^ 1);
         __syncthreads();
-    }
+    };
+    int it = 0;
+    for (; it < nmG; ++it) run_step(it, std::true_type{});
+    for (; it < total; ++it) run_step(it, std::false_type{});
 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {

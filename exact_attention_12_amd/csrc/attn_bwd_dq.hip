@@ -36,7 +36,7 @@ void bwd_dq_kernel(BwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer resources
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int N = p.N;
@@ -118,13 +118,13 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
             const int j = wave + i * NW;
-            if (j < NLK && (BC * CKK % 64 == 0 || j * 64 + lane < BC * CKK))
+            if ((NLK % NW == 0 || j < NLK) && (BC * CKK % 64 == 0 || j * 64 + lane < BC * CKK))
                 buf_load16_to_lds(rk, k_lds + j * 1024, offk[i]);
         }
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
             const int j = wave + i * NW;
-            if (j < NLV && (BC * CKV % 64 == 0 || j * 64 + lane < BC * CKV))
+            if ((NLV % NW == 0 || j < NLV) && (BC * CKV % 64 == 0 || j * 64 + lane < BC * CKV))
                 buf_load16_to_lds(rv, v_lds + j * 1024, offv[i]);
         }
     };

@@ -73,7 +73,7 @@ void fwd_kernel(FwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer resources
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int N = p.N;
@@ -195,12 +195,12 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
             const int j = wave + i * NW;
-            if (j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
+            if (NLK % NW == 0 || j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
         }
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
             const int j = wave + i * NW;
-            if (j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
+            if (NLV % NW == 0 || j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
         }
     };
 
