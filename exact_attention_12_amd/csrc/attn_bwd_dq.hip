@@ -81,12 +81,24 @@ void bwd_dq_kernel(BwdParams p) {
     // Sliding window: keys before the first row's band are skipped.
     const int W = WINDOW ? p.window : 0;
     const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
+    // Key blocks that need no per-element mask form [ku_begin, ku_end): all
+    // keys at or before the workgroup's first query (kv0 + BC - 1 <= q0),
+    // inside its last query's band (kv0 >= q0 + BQ - W) and before N. Keys
+    // past N must stay masked: their zero scores would give exp2(-LSE2),
+    // which overflows for rows with a very negative LSE.
+    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
+    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
+    if (WINDOW) {
+        const int t = q0 + BQ - W;
+        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
+    }
+    ku_end = max(ku_end, ku_begin);
 
     // K/V tiles go straight from memory to LDS: each 64-lane buffer load
     // with the LDS flag fills 64 consecutive 16-byte chunks; lane i of load j
     // covers chunk 64j + i of the padded tile (row = chunk / pitch-chunks).
-    // The K tile is swizzled, so that slot holds logical chunk slot ^ (row &
-    // 7). Chunks past d (padding) and rows past N read as zeros; lanes past
+    // The K tile is swizzled, so that slot holds logical chunk slot ^
+    // sw_swizzle(row). Chunks past d (padding) and rows past N read as zeros; lanes past
     // the end of a tile whose chunk count is not a multiple of 64 are idle.
     constexpr int CKK = KP / 8, CKV = VP / 8;
     constexpr int NLK = (BC * CKK + 63) / 64, NLV = (BC * CKV + 63) / 64;
@@ -147,7 +159,8 @@ void bwd_dq_kernel(BwdParams p) {
     const int krd[2] = {sw_off(l32, h * 8, KP), sw_off(l32, 16 + h * 8, KP)};
     const int ktr0 = sw_off(tr_row, tr_col, KP), ktr1 = sw_off(tr_row + 8, tr_col, KP);
 
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
+    auto run_step = [&](int kb, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int bufi = kb & 1;
         // The last step reloads its own tile into the idle buffer (never
         // read again), so the loads need no branch.
@@ -155,7 +168,8 @@ void bwd_dq_kernel(BwdParams p) {
         const int kv0 = kb * BC;
         const e16* Ks = smem + bufi * BUF;
         const e16* Vs = Ks + BC * KP;
-        // Branch-free step: blocks past a wave's last query are masked to zero.
+        // Branch-free step: in the masked blocks, keys past a wave's last
+        // query are masked to zero.
         {
             f32x16 s[NKT], dp[NKT];
             // S^T = K Q^T and dP^T = V dO^T with the K and V row reads kept
@@ -202,7 +216,6 @@ void bwd_dq_kernel(BwdParams p) {
                                                              bh) << (4 * g);
                     }
                 }
-                const bool MASKED = CAUSAL || (kv0 + BC > N);
                 const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
                 const int lo = qrow - W + 1 - kv0 - 4 * h;
 #pragma unroll
@@ -219,7 +232,7 @@ void bwd_dq_kernel(BwdParams p) {
                             const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
                             float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
                             if (MASKED && koff > lim) pe = 0.0f;
-                            if (WINDOW && koff < lo) pe = 0.0f;
+                            if (MASKED && WINDOW && koff < lo) pe = 0.0f;
                             float dpe = dp[kt][r];
                             if constexpr (DROP) dpe = ((keep[kt] >> r) & 1u) ? dpe * p.drop.scale : 0.0f;
                             dv[w] = pe * (dpe - del);
@@ -241,7 +254,11 @@ void bwd_dq_kernel(BwdParams p) {
         }
         __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
         __syncthreads();
-    }
+    };
+    int kb = kb_begin;
+    for (; kb < ku_begin; ++kb) run_step(kb, std::true_type{});
+    for (; kb < ku_end; ++kb) run_step(kb, std::false_type{});
+    for (; kb < kb_end; ++kb) run_step(kb, std::true_type{});
 
     if (qrow < N) {
         e16* dqrow = static_cast<e16*>(p.dq) + b * p.sdq.b + hq * p.sdq.h + qrow * p.sdq.n;
