@@ -45,6 +45,8 @@
 //    wave skips the math of blocks after its own last query; the diagonal
 //    blocks are masked per element. Heavy (late) query blocks are launched
 //    first.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -226,7 +228,8 @@ void fwd_kernel(FwdParams p) {
     const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
 
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
+    auto run_step = [&](int kb, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int bufi = kb & 1;
         // The last step reloads its own tile into the idle buffer (never
         // read again), so the loads and stores need no branch.
@@ -238,7 +241,7 @@ void fwd_kernel(FwdParams p) {
         const int kv0 = kb * BC;
         const e16* Ks = smem + bufi * BUF;
         const e16* Vs = Ks + BC * KP;
-        const bool active = !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
+        const bool active = !MASKED || !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
         if (active) {
             f32x16 s[NKT];
             if constexpr (D <= 128) {
@@ -274,8 +277,8 @@ void fwd_kernel(FwdParams p) {
             // Keys outside [lo, hi] (relative to kv0 + 4h) are masked: the
             // tail beyond N, keys after the row (causal) and keys before its
             // band (sliding window).
-            const bool need_mask = (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N) ||
-                                   (WINDOW && kv0 < qw0 + 32 - W);
+            const bool need_mask = MASKED && ((CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N) ||
+                                              (WINDOW && kv0 < qw0 + 32 - W));
             if (need_mask) {
                 const int hi = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
                 const int lo = (WINDOW ? qrow - W + 1 : 0) - kv0 - 4 * h;
@@ -393,7 +396,22 @@ void fwd_kernel(FwdParams p) {
         else
             store_tile(bufi ^ 1);
         __syncthreads();
+    };
+    // Key blocks [ku_begin, ku_end) need neither the per-wave skip nor a
+    // mask: every key is at or before the workgroup's first query (kv0 + BC
+    // - 1 <= q0), inside its last query's band (kv0 >= q0 + BQ - W) and
+    // before N. They run in a copy of the step without those tests.
+    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
+    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
+    if (WINDOW) {
+        const int t = q0 + BQ - W;
+        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
     }
+    ku_end = max(ku_end, ku_begin);
+    int kb = kb_begin;
+    for (; kb < ku_begin; ++kb) run_step(kb, std::true_type{});
+    for (; kb < ku_end; ++kb) run_step(kb, std::false_type{});
+    for (; kb < kb_end; ++kb) run_step(kb, std::true_type{});
 
     // Epilogue: combine the two half-row sums, normalise, store O and LSE.
     const float lt = sum_across_halves(l);
