@@ -13,7 +13,8 @@
 // with dK, dV summed over the query heads that share a KV head (GQA).
 //
 // Three kernels on one stream, no atomics (bitwise deterministic):
-//  1. bwd_pre: D_i for every query row (memory bound).
+//  1. bwd_pre: -D_i (stored negated) and the base-2 LSE for every query row
+//     (memory bound).
 //  2. bwd_dkdv: one workgroup per (batch, KV head, 128-key block); each wave
 //     owns 32 keys with K and V held as MFMA operands in VGPRs and dK^T,
 //     dV^T accumulated in AGPRs, looping over the G query heads of the
@@ -63,7 +64,7 @@ void bwd_pre_kernel(BwdParams p, long long rows) {
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 1);
     if (row < rows && j == 0) {
-        p.delta[row] = acc;
+        p.delta[row] = -acc;  // -D_i: the dK/dV pass starts its dP sums from it
         p.lse2[row] = p.lse[row] * kLog2e;  // the dK/dV pass's log2-domain LSE
     }
 }
@@ -152,19 +153,54 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int t = k0 + W - BQ;
         qu_end = max(qu_begin, min(qb_stop, t >= 0 ? t / BQ + 1 : 0));
     }
-    const int nm_lo = qu_begin - qb_start;
     const int nu = qu_end - qu_begin;
-    const int nm = nq_iter - nu;
-    const int nmG = p.G * nm;
-    const int nm1 = max(nm, 1), nu1 = max(nu, 1);
-    auto step_g = [&](int it) { return it < nmG ? it / nm1 : (it - nmG) / nu1; };
-    auto step_qb = [&](int it) {
-        if (it < nmG) {
-            const int r = it % nm1;
-            return r < nm_lo ? qb_start + r : qu_end + (r - nm_lo);
-        }
-        return qu_begin + (it - nmG) % nu1;
+    const int nmG = p.G * (nq_iter - nu);
+    // Step cursor (head g of the group, query block qb), advanced with a few
+    // scalar compares instead of dividing the step index every step. Masked
+    // phase, per head: qb_start .. qu_begin-1, then qu_end .. qb_stop-1.
+    // Unmasked phase, per head: qu_begin .. qu_end-1.
+    // The cursor also carries the head's Q and dO base pointers and its
+    // offset in the row-term arrays, updated only when the head changes; the
+    // row offsets r0 * stride fit in 32 bits (a view's row span is < 2^31).
+    struct Step {
+        int g, qb;
+        const e16* qh;
+        const e16* dh;
+        size_t rt;
     };
+    const int hq0 = hkv * p.G;
+    const Step head0{0, 0, static_cast<const e16*>(p.q) + b * p.sq.b + hq0 * p.sq.h,
+                     static_cast<const e16*>(p.dout) + b * p.sdo.b + hq0 * p.sdo.h,
+                     ((size_t)b * p.Hq + hq0) * N};  // row terms: contiguous [B, Hq, N]
+    const int qm_first = qb_start < qu_begin ? qb_start : qu_end;
+    auto next_head = [&](Step st, int qb) {
+        st.g += 1;
+        st.qb = qb;
+        st.qh += p.sq.h;
+        st.dh += p.sdo.h;
+        st.rt += N;
+        return st;
+    };
+    auto next_step = [&](Step st, int it_next) {
+        if (it_next >= total) return st;  // the last step reloads its own tiles
+        const int qb = st.qb + 1;
+        if (it_next < nmG) {
+            const int qn = qb == qu_begin ? qu_end : qb;
+            if (qn == qb_stop) return next_head(st, qm_first);
+            st.qb = qn;
+            return st;
+        }
+        if (it_next == nmG) {
+            Step h = head0;
+            h.qb = qu_begin;
+            return h;
+        }
+        if (qb == qu_end) return next_head(st, qu_begin);
+        st.qb = qb;
+        return st;
+    };
+    Step first = head0;
+    first.qb = nmG > 0 ? qm_first : qu_begin;
 
     // d <= 128: tiles go straight from memory to LDS. Each 64-lane buffer
     // load with the LDS flag fills 64 consecutive 16-byte chunks; lane i of
@@ -192,19 +228,12 @@ void bwd_dkdv_kernel(BwdParams p) {
             offd[i] = lc < D / 8 ? (uint32_t)row * sd2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
     }
-    auto issue_step = [&](int it, int bufi) {
-        const int g = step_g(it);
-        const int qb = step_qb(it);
-        const int hq = hkv * p.G + g;
-        const size_t row_off = ((size_t)b * p.Hq + hq) * N;
-        const int r0 = qb * BQ;
+    auto issue_step = [&](const Step& st, int bufi) {
+        const int r0 = st.qb * BQ;
+        const size_t row_off = st.rt;
         const uint32_t sq2 = (uint32_t)p.sq.n * 2u, sd2 = (uint32_t)p.sdo.n * 2u;
-        const auto rq = buf_rsrc(static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h +
-                                     (long long)r0 * p.sq.n,
-                                 (uint32_t)(N - r0 - 1) * sq2 + D * 2);
-        const auto rd = buf_rsrc(static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h +
-                                     (long long)r0 * p.sdo.n,
-                                 (uint32_t)(N - r0 - 1) * sd2 + D * 2);
+        const auto rq = buf_rsrc(st.qh + r0 * (int)p.sq.n, (uint32_t)(N - r0 - 1) * sq2 + D * 2);
+        const auto rd = buf_rsrc(st.dh + r0 * (int)p.sdo.n, (uint32_t)(N - r0 - 1) * sd2 + D * 2);
         char* qt_lds = reinterpret_cast<char*>(qtile(bufi));
         char* dt_lds = reinterpret_cast<char*>(dotile(bufi));
 #pragma unroll
@@ -229,14 +258,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     float row_r = 0.0f;
     const int rt_kind = tid / BQ;        // 0: LSE, 1: D_i, 2+: spare
     const int rt_row = tid - rt_kind * BQ;
-    auto load_step = [&](int it) {
-        const int g = step_g(it);
-        const int qb = step_qb(it);
-        const int hq = hkv * p.G + g;
-        const size_t row_off = ((size_t)b * p.Hq + hq) * N;  // LSE, D_i: contiguous
-        const int r0 = qb * BQ;
-        qio.load(static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h, p.sq.n, r0, N, tid);
-        doio.load(static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h, p.sdo.n, r0, N, tid);
+    auto load_step = [&](const Step& st) {
+        const size_t row_off = st.rt;
+        const int r0 = st.qb * BQ;
+        qio.load(st.qh, p.sq.n, r0, N, tid);
+        doio.load(st.dh, p.sdo.n, r0, N, tid);
         const int r = r0 + rt_row;
         const size_t rc = row_off + min(r, N - 1);
         const float x = rt_kind == 0 ? p.lse2[rc] : p.delta[rc];
@@ -266,27 +292,30 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     if (total > 0) {
         if constexpr (DIRECT) {
-            issue_step(0, 0);
+            issue_step(first, 0);
             __builtin_amdgcn_s_waitcnt(0);
         } else {
-            load_step(0);
+            load_step(first);
             store_step(0);
         }
     }
     __syncthreads();
 
-    auto run_step = [&](int it, auto masked_tag) {
+    // Step it works on `cur` (whose tiles are in LDS) and moves `cur` on to
+    // the next step, whose loads it issues. The last step reloads its own
+    // tiles into the idle buffer (never read), which keeps the body free of
+    // branches.
+    auto run_step = [&](int it, Step& cur, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int bufi = it & 1;
-        // The last step reloads its own tiles into the idle buffer (never
-        // read), which keeps the body free of branches.
+        const int g = cur.g;
+        const int q0 = cur.qb * BQ;
+        cur = next_step(cur, it + 1);
         if constexpr (DIRECT)
-            issue_step(min(it + 1, total - 1), bufi ^ 1);
+            issue_step(cur, bufi ^ 1);
         else
-            load_step(min(it + 1, total - 1));
+            load_step(cur);
 
-        const int g = step_g(it);
-        const int q0 = step_qb(it) * BQ;
         // Every step runs for every wave (no data-dependent branch in the
         // loop body): a wave whose keys all lie after this query block just
         // contributes zeros through the mask.
@@ -296,10 +325,26 @@ void bwd_dkdv_kernel(BwdParams p) {
             const float* Ls = lsetile(bufi);
             const float* Ds = deltile(bufi);
             f32x16 s[NQT], dp[NQT];
+            // Start value of the dP sums of tile qt: -D_i of each register's
+            // query (registers 4k .. 4k+3 hold queries 8k + 4h .. +3), so the
+            // products leave dP - D_i. Dropout scales dP alone, so it starts
+            // from zero and subtracts D_i later.
+            auto dp_init = [&](int qt) {
+                f32x16 a{};
+                if constexpr (!DROP) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const f32x4 v = *reinterpret_cast<const f32x4*>(Ds + qt * 32 + 8 * k + 4 * h);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[4 * k + e] = v[e];
+                    }
+                }
+                return a;
+            };
             // S = Q K^T and dP = dO V^T for the 32 queries of tile qt.
             auto mma_sd = [&](int qt) {
                 s[qt] = f32x16{};
-                dp[qt] = f32x16{};
+                dp[qt] = dp_init(qt);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int off = qrd[ks & 1] + qt * 32 * QP + (ks >> 1) * 32;
@@ -350,10 +395,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                     if constexpr (DROP) {
                         const bool kept = (keep[qt] >> r) & 1u;
                         pv[w] = kept ? pe * p.drop.scale : 0.0f;
-                        dv[w] = pe * ((kept ? dp[qt][r] * p.drop.scale : 0.0f) - Ds[ql]);
+                        dv[w] = pe * ((kept ? dp[qt][r] * p.drop.scale : 0.0f) + Ds[ql]);
                     } else {
                         pv[w] = pe;
-                        dv[w] = pe * (dp[qt][r] - Ds[ql]);
+                        dv[w] = pe * dp[qt][r];  // dp already holds dP - D_i
                     }
                 }
                 pp[u][e2] = cvt2<DT>(pv[0], pv[1]);
@@ -404,9 +449,9 @@ void bwd_dkdv_kernel(BwdParams p) {
                     aq[dt] = join8(lds_read_tr4(Qs + qtr0 + ob), lds_read_tr4(Qs + qtr1 + ob));
                 };
                 s[0] = f32x16{};
-                dp[0] = f32x16{};
+                dp[0] = dp_init(0);
                 s[1] = f32x16{};
-                dp[1] = f32x16{};
+                dp[1] = dp_init(1);
                 rd(0);
                 rd(1);
                 __builtin_amdgcn_sched_barrier(0);
@@ -501,8 +546,9 @@ void bwd_dkdv_kernel(BwdParams p) {
         __syncthreads();
     };
     int it = 0;
-    for (; it < nmG; ++it) run_step(it, std::true_type{});
-    for (; it < total; ++it) run_step(it, std::false_type{});
+    Step cur = first;
+    for (; it < nmG; ++it) run_step(it, cur, std::true_type{});
+    for (; it < total; ++it) run_step(it, cur, std::false_type{});
 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {

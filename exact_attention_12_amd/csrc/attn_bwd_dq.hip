@@ -59,7 +59,7 @@ void bwd_dq_kernel(BwdParams p) {
 
 
     e16x8 qf[KS], gf[KS];
-    float lse2 = __builtin_huge_valf(), del = 0.0f;
+    float lse2 = __builtin_huge_valf(), ndel = 0.0f;  // ndel = -D_i, as the preprocess stores it
     if (qrow < N) {
         const e16* qp = static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h + qrow * p.sq.n + h * 8;
         const e16* gp =
@@ -70,7 +70,7 @@ void bwd_dq_kernel(BwdParams p) {
             gf[ks] = *reinterpret_cast<const e16x8*>(gp + ks * 16);
         }
         lse2 = p.lse[row_off + qrow] * kLog2e;
-        del = p.delta[row_off + qrow];
+        ndel = p.delta[row_off + qrow];
     } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) { qf[ks] = e16x8{}; gf[ks] = e16x8{}; }
@@ -235,7 +235,7 @@ void bwd_dq_kernel(BwdParams p) {
                             if (MASKED && WINDOW && koff < lo) pe = 0.0f;
                             float dpe = dp[kt][r];
                             if constexpr (DROP) dpe = ((keep[kt] >> r) & 1u) ? dpe * p.drop.scale : 0.0f;
-                            dv[w] = pe * (dpe - del);
+                            dv[w] = pe * (dpe + ndel);
                         }
                         dd[e2] = cvt2<DT>(dv[0], dv[1]);
                     }

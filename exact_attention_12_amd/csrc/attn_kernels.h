@@ -129,7 +129,7 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;  // [B, Hq, N] workspace: D_i = <dO_i, O_i>
+    float* delta;  // [B, Hq, N] workspace: -D_i = -<dO_i, O_i>
     float* lse2;   // [B, Hq, N] workspace: LSE_i * log2(e), written with D_i
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     int N;

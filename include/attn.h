@@ -117,8 +117,8 @@ attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o
 
 /*
  * Bytes of device workspace attn_bwd needs: two float32 per query row, the
- * row term D_i = <dO_i, O_i> and the LSE in base 2, each array rounded up to
- * 256 bytes. Returns 0 if the shape is invalid.
+ * row term D_i = <dO_i, O_i> (stored negated) and the LSE in base 2, each
+ * array rounded up to 256 bytes. Returns 0 if the shape is invalid.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
@@ -159,8 +159,8 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
  * for attn_bwd; each validates them the same way and enqueues one kernel.
  * window: 0 for the mask `causal` selects, or W >= 1 (with causal != 0) for
  * the sliding window of attn_bwd_window.
- *   attn_bwd_preprocess: workspace <- D_i = <dout_i, o_i> and lse_i * log2(e)
- *     per query row.
+ *   attn_bwd_preprocess: workspace <- -D_i = -<dout_i, o_i> and
+ *     lse_i * log2(e) per query row.
  *   attn_bwd_dkdv: dk, dv from q, k, v, lse, dout and the workspace.
  *   attn_bwd_dq:   dq from q, k, v, lse, dout and the workspace.
  * The dK/dV and dQ passes read the workspace the preprocess wrote, so they
