@@ -21,8 +21,7 @@ LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-# Sources and their extra flags. (The dK/dV pass orders its instructions with
-# scheduling-group hints in the source.)
+# Sources and their extra flags.
 SOURCES = {
     "attn_api.cpp": [],
     "attn_fwd.hip": [],
@@ -64,11 +63,43 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# Sources with inline-assembly MFMAs, whose VALU -> MFMA wait states the
+# compiler does not track: their device assembly is checked (hazards.py).
+HAZARD_CHECKED = ["attn_bwd.hip"]
+
+
+def _check_hazards(src: str) -> None:
+    asm = os.path.join(BUILD_DIR, os.path.basename(src) + ".gfx950.s")
+    cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCES[src], "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", asm]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{res.stdout}{res.stderr}")
+    sys.path.insert(0, PKG)
+    try:
+        import hazards
+    finally:
+        sys.path.pop(0)
+    with open(asm) as f:
+        found = hazards.check(f.read())
+    if found:
+        name, seq = found[0]
+        raise RuntimeError(f"{src}: {len(found)} VALU -> MFMA operand hazard(s) in the generated code, "
+                           f"first in {name}:\n  " + "\n  ".join(seq))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libattn.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    jobs = [("c", s) for s in SOURCES] + [("h", s) for s in HAZARD_CHECKED]
+
+    def run(job):
+        kind, src = job
+        return _compile(src, verbose) if kind == "c" else _check_hazards(src)
+
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(run, jobs))
+    objs = [r for (kind, _), r in zip(jobs, results) if kind == "c"]
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -81,6 +81,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int BK = NW * 32;        // keys per workgroup
     constexpr int BQ = (D <= 128) ? 64 : 32;  // queries per step
     constexpr int NQT = BQ / 32;
+    // d = 32: the compiler sinks part of the P / dS packing past the region
+    // gaps, so every dV/dK product carries its own two wait states.
+    constexpr bool ACC_GAP = D <= 32;
     constexpr int PVS = BQ / 16;
     constexpr int KS = D / 16;
     constexpr int NDT = (D + 31) / 32;
@@ -481,6 +484,7 @@ void bwd_dkdv_kernel(BwdParams p) {
                 }
                 pack(0);
                 pack(1);
+                valu_mfma_gap();
                 // C0: dV/dK steps u = 0 (operands A) and u = 1 (operands B);
                 // the reads for u = 1 go into B while u = 0 runs, those for
                 // u = 2 into A while u = 1 runs.
@@ -488,12 +492,12 @@ void bwd_dkdv_kernel(BwdParams p) {
                 for (int k = 0; k < 2 * NDT; ++k) {
                     const int u = k / NDT, dt = k % NDT;
                     if (u == 0) {
-                        mfma32_agpr<DT>(dvacc[dt], opA_d[dt], pb[0]);
-                        mfma32_agpr<DT>(dkacc[dt], opA_q[dt], dsb[0]);
+                        mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opA_d[dt], pb[0]);
+                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opA_q[dt], dsb[0]);
                         tr_read(1, dt, opB_d, opB_q);
                     } else {
-                        mfma32_agpr<DT>(dvacc[dt], opB_d[dt], pb[1]);
-                        mfma32_agpr<DT>(dkacc[dt], opB_q[dt], dsb[1]);
+                        mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opB_d[dt], pb[1]);
+                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opB_q[dt], dsb[1]);
                         tr_read(2, dt, opA_d, opA_q);
                     }
 #pragma unroll
@@ -505,16 +509,17 @@ void bwd_dkdv_kernel(BwdParams p) {
                 }
                 pack(2);
                 pack(3);
+                valu_mfma_gap();
 #pragma unroll
                 for (int k = 0; k < 2 * NDT; ++k) {  // C1: u = 2 (A), u = 3 (B)
                     const int u = 2 + k / NDT, dt = k % NDT;
                     if (u == 2) {
-                        mfma32_agpr<DT>(dvacc[dt], opA_d[dt], pb[2]);
-                        mfma32_agpr<DT>(dkacc[dt], opA_q[dt], dsb[2]);
+                        mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opA_d[dt], pb[2]);
+                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opA_q[dt], dsb[2]);
                         tr_read(3, dt, opB_d, opB_q);
                     } else {
-                        mfma32_agpr<DT>(dvacc[dt], opB_d[dt], pb[3]);
-                        mfma32_agpr<DT>(dkacc[dt], opB_q[dt], dsb[3]);
+                        mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opB_d[dt], pb[3]);
+                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opB_q[dt], dsb[3]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -527,14 +532,15 @@ void bwd_dkdv_kernel(BwdParams p) {
                     for (int e2 = 0; e2 < 4; ++e2) softmax_pair(u, e2);
                     pack(u);
                 }
+                valu_mfma_gap();
                 e16x8 a_do[NDT], a_q[NDT];
 #pragma unroll
                 for (int u = 0; u < PVS; ++u) {
                     read_ops(u, a_do, a_q);
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        mfma32_agpr<DT>(dvacc[dt], a_do[dt], pb[u]);
-                        mfma32_agpr<DT>(dkacc[dt], a_q[dt], dsb[u]);
+                        mfma32_agpr<DT, ACC_GAP>(dvacc[dt], a_do[dt], pb[u]);
+                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], a_q[dt], dsb[u]);
                     }
                 }
             }

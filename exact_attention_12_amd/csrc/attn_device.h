@@ -59,19 +59,40 @@ __device__ __forceinline__ f32x16 mfma32(e16x8 a, e16x8 b, f32x16 c) {
 // Used for long-lived accumulators that only matrix instructions touch inside
 // a loop, so that they do not compete with the loop's working set for VGPRs.
 // Written as inline assembly, so the compiler's hazard tracking does not see
-// it; the hazards it can meet are handled here:
-//  * a VALU write of an A/B operand VGPR followed by the MFMA read needs two
-//    wait states: the s_nop 1 in front of the instruction;
+// it; the hazards it can meet:
+//  * a VALU write of an A/B operand VGPR (or of the AGPRs) followed by the
+//    MFMA read needs two wait states. Callers produce the operands in an
+//    earlier scheduling region and separate the regions with
+//    valu_mfma_gap(); the build checks the generated code for any VALU
+//    write closer than two wait states to an MFMA that reads it (a nop in
+//    every call would cost an issue slot per product). GAP = true puts the
+//    two wait states in front of every product instead, for kernels where
+//    the compiler moves operand writes past the region boundary;
 //  * back-to-back accumulation into the same registers (srcC == vdst) is
 //    interlocked by the hardware;
 //  * reading the result with VALU instructions needs the MFMA to have drained:
 //    call agpr_acc_ready() on the accumulator before any such read.
-template <int DT>
+template <int DT, bool GAP = false>
 __device__ __forceinline__ void mfma32_agpr(f32x16& acc, e16x8 a, e16x8 b) {
-    if constexpr (DT == kBF16)
-        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-    else
-        asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    if constexpr (GAP) {
+        if constexpr (DT == kBF16)
+            asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+        else
+            asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    } else {
+        if constexpr (DT == kBF16)
+            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+        else
+            asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
+}
+
+// Two wait states between everything scheduled before this point and
+// everything after it (the VALU -> MFMA operand gap of mfma32_agpr).
+__device__ __forceinline__ void valu_mfma_gap() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wait states after the last mfma32_agpr into `acc` before VALU reads of it
