@@ -1,7 +1,8 @@
-"""The build's static VALU -> MFMA wait-state check (exact_attention_12_amd/hazards.py)
-on small hand-written gfx950 listings: it must flag a write one or two
-instructions before an MFMA operand read, and accept the same code once two
-wait states separate them."""
+"""The build's static wait-state checks (exact_attention_12_amd/hazards.py) on
+small hand-written gfx950 listings: a VALU write one or two instructions
+before an MFMA operand read, and a VALU access to an AGPR accumulator too
+soon after the product that writes it, must be flagged; the same code with
+enough wait states in between must pass."""
 
 import importlib.util
 import os
@@ -45,6 +46,15 @@ MFMA = "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]"
     ("v_accvgpr_write_b32 a16, v1\n" + MFMA, 0),
     # a VGPR pair range overlapping the operand
     ("v_lshlrev_b64 v[10:11], 1, v[2:3]\n" + MFMA, 1),
+    # an AGPR accumulator copied while the product is still being written
+    (MFMA + "\ns_nop 7\nv_accvgpr_mov_b32 a40, a15", 1),
+    (MFMA + "\nv_accvgpr_read_b32 v1, a3", 1),
+    (MFMA + "\ns_nop 7\ns_nop 7\ns_nop 1\nv_accvgpr_mov_b32 a40, a15", 0),
+    # other registers, or past an unconditional branch
+    (MFMA + "\nv_accvgpr_mov_b32 a40, a16", 0),
+    (MFMA + "\ns_branch .LBB0_2\nv_accvgpr_read_b32 v1, a3", 0),
+    # compiler-managed products (VGPR results) are not the check's business
+    ("v_mfma_f32_32x32x16_bf16 v[16:31], v[4:7], v[8:11], v[16:31]\nv_mov_b32 v40, v16", 0),
 ])
 def test_hazard_rule(body, n):
     assert len(_hazards().check(_func(body))) == n
