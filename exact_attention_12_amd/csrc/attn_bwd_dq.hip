@@ -23,7 +23,9 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int NW = 4;
     constexpr int T = NW * 64;
     constexpr int BQ = NW * 32;
-    constexpr int BC = 32;  // keys per step: keeps two waves per SIMD without spills
+    // Keys per step: 64 halves the per-step overhead while two waves per SIMD
+    // still fit without spills; dropout (its keep bits) and d > 128 take 32.
+    constexpr int BC = (D <= 128 && !DROP) ? 64 : 32;
     constexpr int KS = D / 16;
     constexpr int NDT = (D + 31) / 32;
     constexpr int NKT = BC / 32;
