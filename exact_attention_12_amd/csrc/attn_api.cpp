@@ -90,9 +90,11 @@ attn::Strides strides_of(const attn_tensor& t) { return {t.stride_b, t.stride_h,
 attn_status make_drop(const attn_problem& pr, attn::DropParams* d) {
     const float pd = pr.dropout_p;
     if (!std::isfinite(pd) || pd < 0.0f || pd >= 1.0f) return ATTN_ERR_DROPOUT;
-    const double t = std::floor((double)pd * 4294967296.0);
-    d->thr = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
-    d->scale = 1.0f / (1.0f - pd);
+    // 16-bit threshold: the realised drop probability is thr / 2^16, and the
+    // kept weights are scaled by its complement's inverse (unbiased).
+    const double t = std::floor((double)pd * 65536.0);
+    d->thr = t >= 65535.0 ? 65535u : (uint32_t)t;
+    d->scale = (float)(1.0 / (1.0 - d->thr / 65536.0));
     d->seed_lo = (uint32_t)(pr.seed & 0xffffffffull);
     d->seed_hi = (uint32_t)(pr.seed >> 32);
     d->offset = pr.offset;

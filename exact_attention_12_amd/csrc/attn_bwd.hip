@@ -366,21 +366,16 @@ void bwd_dkdv_kernel(BwdParams p) {
             const int kq = key - q0 - 4 * h;
             const int kq_w = kq + W - 1;
             // Dropout: the lane's key meets 4 consecutive queries per
-            // register group, exactly one Philox block each (bit r of
-            // keep[qt] for register r). dV takes P * M / (1-p); dP is
-            // scaled the same way before the softmax step.
+            // register group (bit r of keep[qt] for register r); a Philox
+            // block covers them for this key and the neighbouring one, so
+            // each lane pair shares its four blocks. dV takes P * M / (1-p);
+            // dP is scaled the same way before the softmax step.
             uint32_t keep[NQT];
             if constexpr (DROP) {
                 const uint32_t bh = (uint32_t)(b * p.Hq + hkv * p.G + g);
 #pragma unroll
-                for (int qt = 0; qt < NQT; ++qt) {
-                    keep[qt] = 0;
-#pragma unroll
-                    for (int gg = 0; gg < 4; ++gg)
-                        keep[qt] |= keep_nibble(p.drop, (uint32_t)key,
-                                                (uint32_t)(q0 + qt * 32 + 8 * gg + 4 * h) >> 2, bh)
-                                    << (4 * gg);
-                }
+                for (int qt = 0; qt < NQT; ++qt)
+                    keep[qt] = keep_bits_key_lane(p.drop, (uint32_t)key, (uint32_t)(q0 + qt * 32 + 4 * h) >> 2, bh);
             }
             // One pair of registers (r, r+1) of contraction step u.
             auto softmax_pair = [&](int u, int e2) {

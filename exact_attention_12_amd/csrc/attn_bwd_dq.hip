@@ -213,9 +213,9 @@ void bwd_dq_kernel(BwdParams p) {
                     for (int kt = 0; kt < NKT; ++kt) {
                         keep[kt] = 0;
 #pragma unroll
-                        for (int g = 0; g < 4; ++g)
-                            keep[kt] |= keep_bits_query_lane(p.drop, kv0 + kt * 32 + 8 * g + 4 * h, qrow,
-                                                             bh) << (4 * g);
+                        for (int gp = 0; gp < 2; ++gp)
+                            keep[kt] |= keep_bits_query_lane(p.drop, kv0 + kt * 32 + 16 * gp + 4 * h, qrow,
+                                                             bh) << (8 * gp);
                     }
                 }
                 const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;

@@ -219,20 +219,43 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     return make_uint4(c0, c1, c2, c3);
 }
 
-// Dropout stream: score (bh, i, j) is kept when word i % 4 of
-// philox4x32_10(j, i / 4, bh, offset; seed) is >= thr = floor(p * 2^32).
+// Dropout stream: score (bh, i, j) is kept when the 16-bit half j % 2 (0:
+// low, 1: high) of word i % 4 of philox4x32_10(j / 2, i / 4, bh, offset;
+// seed) is >= thr = floor(p * 2^16). One Philox block thus decides a block of
+// 4 queries x 2 keys.
 struct DropParams {
     uint32_t thr;     // 0 = no dropout
-    float scale;      // 1 / (1 - p)
+    float scale;      // 1 / (1 - thr / 2^16)
     uint32_t seed_lo, seed_hi, offset;
 };
 
-// Keep bits of the four queries 4*(i/4) .. +3 at key j (bit k: query 4*(i/4)+k).
-__device__ __forceinline__ uint32_t keep_nibble(const DropParams& dp, uint32_t j, uint32_t iq,
-                                                uint32_t bh) {
-    const uint4 w = philox4x32_10(j, iq, bh, dp.offset, dp.seed_lo, dp.seed_hi);
-    return (uint32_t)(w.x >= dp.thr) | ((uint32_t)(w.y >= dp.thr) << 1) |
-           ((uint32_t)(w.z >= dp.thr) << 2) | ((uint32_t)(w.w >= dp.thr) << 3);
+// Keep bits of queries 4*iq .. +3 (k) at keys 2*jp and 2*jp + 1 (jj):
+// bit k + 4*jj.
+__device__ __forceinline__ uint32_t keep_block(const DropParams& dp, uint32_t jp, uint32_t iq,
+                                               uint32_t bh) {
+    const uint4 w = philox4x32_10(jp, iq, bh, dp.offset, dp.seed_lo, dp.seed_hi);
+    const uint32_t t = dp.thr;
+    return (uint32_t)((w.x & 0xFFFFu) >= t) | ((uint32_t)((w.y & 0xFFFFu) >= t) << 1) |
+           ((uint32_t)((w.z & 0xFFFFu) >= t) << 2) | ((uint32_t)((w.w & 0xFFFFu) >= t) << 3) |
+           ((uint32_t)((w.x >> 16) >= t) << 4) | ((uint32_t)((w.y >> 16) >= t) << 5) |
+           ((uint32_t)((w.z >> 16) >= t) << 6) | ((uint32_t)((w.w >> 16) >= t) << 7);
+}
+
+// Keep bits for a lane that owns key j (lane % 32 = j % 32, so lanes 2m and
+// 2m+1 own an even key and the next one) and the query quads iq0 + 2*gg
+// (gg = 0..3): bits 4gg .. 4gg+3 = the four queries of quad gg. Each lane of
+// the pair draws two of the four blocks, which cover both keys, and hands the
+// other key's half to its partner.
+__device__ __forceinline__ uint32_t keep_bits_key_lane(const DropParams& dp, uint32_t j,
+                                                       uint32_t iq0, uint32_t bh) {
+    const uint32_t jj = j & 1u;
+    const uint32_t b0 = keep_block(dp, j >> 1, iq0 + 4u * jj, bh);      // quad gg = 2jj
+    const uint32_t b1 = keep_block(dp, j >> 1, iq0 + 4u * jj + 2u, bh); // quad gg = 2jj + 1
+    const uint32_t mine = ((b0 >> (4u * jj)) & 0xFu) | (((b1 >> (4u * jj)) & 0xFu) << 4);
+    const uint32_t other = ((b0 >> (4u - 4u * jj)) & 0xFu) | (((b1 >> (4u - 4u * jj)) & 0xFu) << 4);
+    // partner's value (DPP quad_perm [1, 0, 3, 2]: lanes 2m <-> 2m+1)
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0xB1, 0xF, 0xF, false);
+    return jj ? (recv | (mine << 8)) : (mine | (recv << 8));
 }
 
 // Value of x held by lane U of this lane's group of four (DPP quad_perm).
@@ -242,18 +265,22 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
 }
 
 // Keep bits for a lane that owns query i (lane % 32 = i % 32, so the four
-// lanes of a DPP quad own the queries 4*(i/4) .. +3) and the four keys
-// j0 .. j0+3: bit u = keep(i, j0 + u). Each lane of the quad draws the Philox
-// block of one key (j0 + lane % 4) covering all four queries; the 4 x 4 bit
-// block is then transposed across the quad.
+// lanes of a DPP quad own the queries 4*(i/4) .. +3) and the keys j0 .. j0+3
+// (bits 0..3) and j0+8 .. j0+11 (bits 4..7), j0 a multiple of 4. Lane t of
+// the quad draws the block of key pair t (j0/2 + t for t < 2, j0/2 + 4 + t - 2
+// after), covering all four queries; the bits are then gathered across the
+// quad.
 __device__ __forceinline__ uint32_t keep_bits_query_lane(const DropParams& dp, uint32_t j0,
                                                          uint32_t i, uint32_t bh) {
     const uint32_t q = i & 3u;
-    const uint32_t nib = keep_nibble(dp, j0 + q, i >> 2, bh);
-    const uint32_t n0 = quad_bcast<0>(nib), n1 = quad_bcast<1>(nib);
-    const uint32_t n2 = quad_bcast<2>(nib), n3 = quad_bcast<3>(nib);
-    return ((n0 >> q) & 1u) | (((n1 >> q) & 1u) << 1) | (((n2 >> q) & 1u) << 2) |
-           (((n3 >> q) & 1u) << 3);
+    const uint32_t jp = (j0 >> 1) + (q < 2u ? q : q + 2u);
+    const uint32_t blk = keep_block(dp, jp, i >> 2, bh);
+    const uint32_t x0 = quad_bcast<0>(blk), x1 = quad_bcast<1>(blk);
+    const uint32_t x2 = quad_bcast<2>(blk), x3 = quad_bcast<3>(blk);
+    // key j0 + u (u < 4): block of lane u / 2, bit q + 4 * (u % 2)
+    return ((x0 >> q) & 1u) | (((x0 >> (q + 4u)) & 1u) << 1) | (((x1 >> q) & 1u) << 2) |
+           (((x1 >> (q + 4u)) & 1u) << 3) | (((x2 >> q) & 1u) << 4) | (((x2 >> (q + 4u)) & 1u) << 5) |
+           (((x3 >> q) & 1u) << 6) | (((x3 >> (q + 4u)) & 1u) << 7);
 }
 
 }  // namespace attn

@@ -222,14 +222,16 @@ typedef struct attn_problem {
     /*
      * Fused dropout on the attention weights (training; "FlashAttention in
      * CANN ops-transformer on the Ascend NPU", tuning section on dropout):
-     * O = (P * M / (1 - dropout_p)) V with a keep mask M drawn from a
+     * O = (P * M / (1 - p')) V with a keep mask M drawn from a
      * counter-based generator, so the backward redraws the same mask from
      * (seed, offset) instead of storing it. Weight (b, h, i, j) is kept when
-     * 32-bit word i % 4 of Philox-4x32-10 (Salmon et al., SC'11) with counter
-     * (j, i / 4, b * Hq + h, offset) and key (seed & 0xffffffff, seed >> 32)
-     * is >= floor(dropout_p * 2^32). lse is that of the softmax (dropout
-     * does not change it). 0 turns dropout off; the backward must be given
-     * the forward's dropout_p, seed and offset.
+     * the 16-bit half j % 2 (0: low) of 32-bit word i % 4 of Philox-4x32-10
+     * (Salmon et al., SC'11) with counter (j / 2, i / 4, b * Hq + h, offset)
+     * and key (seed & 0xffffffff, seed >> 32) is >= T = floor(dropout_p *
+     * 2^16), so the realised drop probability is p' = T / 2^16 (dropout_p
+     * below 2^-16 drops nothing). lse is that of the softmax (dropout does not
+     * change it). 0 turns dropout off; the backward must be given the
+     * forward's dropout_p, seed and offset.
      */
     float dropout_p;          /* in [0, 1) */
     unsigned long long seed;

@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .philox import dropout_keep
+from .philox import dropout_keep, effective_p
 
 __all__ = [
     "kv_head_of",
@@ -107,11 +107,13 @@ def _dropped(P, keep, p_drop):
 
 
 def _keep_rows(dropout, bh, r0, r1, N):
-    """Keep mask of rows r0..r1-1 of head bh under dropout = (p, seed, offset)."""
+    """Keep mask of rows r0..r1-1 of head bh under dropout = (p, seed, offset),
+    and the drop probability the mask realises (p rounded down to a multiple
+    of 2^-16), by which the kept weights are rescaled."""
     if dropout is None:
         return None, 0.0
     p, seed, offset = dropout
-    return dropout_keep(bh, np.arange(r0, r1), np.arange(N), p, seed, offset), float(p)
+    return dropout_keep(bh, np.arange(r0, r1), np.arange(N), p, seed, offset), effective_p(p)
 
 
 def ref_fwd_head(q, k, v, scale, causal=False, row0=0, return_sp=False, window=None, keep=None,

@@ -18,10 +18,12 @@ stream can be computed on its own, which is what lets a tiled kernel and this
 plain reference draw identical dropout masks.
 
 The dropout stream (``dropout_keep``): the keep decision for score element
-(bh, i, j) of head bh = b * Hq + hq uses the 32-bit word i mod 4 of
-Philox-4x32-10 with counter (j, floor(i / 4), bh, offset) and key
-(seed mod 2^32, floor(seed / 2^32)); the element is kept when that word is
->= floor(p * 2^32), so it is dropped with probability p (to within 2^-32).
+(bh, i, j) of head bh = b * Hq + hq uses the 16-bit half j mod 2 (0: low
+bits, 1: high bits) of the 32-bit word i mod 4 of Philox-4x32-10 with counter
+(floor(j / 2), floor(i / 4), bh, offset) and key (seed mod 2^32,
+floor(seed / 2^32)); the element is kept when that half is
+>= T = floor(p * 2^16). It is dropped with probability exactly T / 2^16
+(``effective_p``), the value the kept weights are rescaled by.
 """
 
 from __future__ import annotations
@@ -89,11 +91,16 @@ def philox4x32(counter, key, rounds=10):
 
 
 def keep_threshold(p: float) -> int:
-    """floor(p * 2^32): words below it are dropped. p is taken as the exact
-    value it has (callers pass the float32 the kernels see)."""
+    """floor(p * 2^16): 16-bit values below it are dropped. p is taken as the
+    exact value it has (callers pass the float32 the kernels see)."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(np.floor(np.float64(p) * 4294967296.0)), 4294967295)
+    return min(int(np.floor(np.float64(p) * 65536.0)), 65535)
+
+
+def effective_p(p: float) -> float:
+    """The drop probability the stream realises: keep_threshold(p) / 2^16."""
+    return keep_threshold(p) / 65536.0
 
 
 def dropout_keep(bh: int, rows, cols, p: float, seed: int, offset: int) -> np.ndarray:
@@ -106,7 +113,8 @@ def dropout_keep(bh: int, rows, cols, p: float, seed: int, offset: int) -> np.nd
         return np.ones((rows.size, cols.size), dtype=bool)
     i = rows[:, None]
     j = cols[None, :]
-    words = philox4x32((j, i // 4, np.int64(bh), np.int64(offset)),
+    words = philox4x32((j // 2, i // 4, np.int64(bh), np.int64(offset)),
                        (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF), rounds=10)
-    w = np.choose((i % 4) * np.ones_like(j), words)
-    return w.astype(np.uint64) >= t
+    w = np.choose((i % 4) * np.ones_like(j), words).astype(np.uint64)
+    half = (w >> (16 * (j % 2)).astype(np.uint64)) & np.uint64(0xFFFF)
+    return half >= t

@@ -554,11 +554,26 @@ def check_philox32_stream(philox, philox4x32):
     assert [int(x) for x in z] == [1, 2, 3, 4]
 
 
+def _p_realised(p):
+    """Drop probability of a 16-bit threshold floor(p * 2^16)."""
+    return math.floor(float(p) * 65536.0) / 65536.0
+
+
 def check_keep_mask(dropout_keep, keep_threshold):
     """Keep fraction 1 - p (5 sigma), p = 0 keeps everything, masks depend on
-    head, seed and offset, and are reproducible."""
-    assert keep_threshold(0.0) == 0 and keep_threshold(0.5) == 2**31
-    assert keep_threshold(np.float32(0.1)) == int(np.floor(np.float64(np.float32(0.1)) * 2**32))
+    head, seed and offset, and are reproducible; the two keys that share a
+    Philox word (its two 16-bit halves) decide independently."""
+    assert keep_threshold(0.0) == 0 and keep_threshold(0.5) == 2**15
+    assert keep_threshold(np.float32(0.1)) == int(np.floor(np.float64(np.float32(0.1)) * 2**16))
+    assert keep_threshold(1.0 - 2.0**-20) == 65535
+    both = dropout_keep(5, np.arange(256), np.arange(512), 0.5, 99, 1)
+    pair = both[:, 0::2] & both[:, 1::2]
+    sd = np.sqrt(0.25 * 0.75 / pair.size)
+    assert abs(pair.mean() - 0.25) < 5 * sd
+    # rows of one query quad (different words of one block) agree half the time
+    agree = both[0::4] == both[1::4]
+    sd = np.sqrt(0.25 / agree.size)
+    assert abs(agree.mean() - 0.5) < 5 * sd
     for p in (0.1, 0.5, 0.9):
         m = dropout_keep(3, np.arange(512), np.arange(512), p, 1234, 7)
         sd = np.sqrt(p * (1 - p) / m.size)
@@ -604,7 +619,8 @@ def check_dropout_forward(fwd_d, fwd, dropout_keep):
     for causal in (False, True):
         O, L = fwd_d(q, k, v, 0.7, causal, (p, seed, off))
         Ob, Lb = brute_force_dropout_fwd(q, k, v, 0.7, causal,
-                                         lambda bh, N: dropout_keep(bh, np.arange(N), np.arange(N), p, seed, off), p)
+                                         lambda bh, N: dropout_keep(bh, np.arange(N), np.arange(N), p, seed, off),
+                                         _p_realised(p))
         np.testing.assert_allclose(O, Ob, rtol=RTOL_EXACT, atol=1e-13)
         np.testing.assert_allclose(L, Lb, rtol=RTOL_EXACT, atol=1e-13)
         O0, L0 = fwd_d(q, k, v, 0.7, causal, (0.0, seed, off))

@@ -99,3 +99,36 @@ def test_mutant_is_caught(name):
     mod = load_mutant(*MUTANTS[name])
     with pytest.raises(Exception):
         run_all_pins(mod)
+
+
+# Planted mistakes in a copy of oracle/philox.py (the dropout stream), each
+# rejected by the stream pins.
+PHILOX_SRC = os.path.join(os.path.dirname(SRC), "philox.py")
+PHILOX_MUTANTS = {
+    "both_keys_same_half": ("(16 * (j % 2))", "(16 * (j % 1))"),
+    "row_word_from_key": ("np.choose((i % 4) * np.ones_like(j), words)", "np.choose((j % 4) * np.ones_like(i), words)"),
+    "threshold_32_bit": ("np.float64(p) * 65536.0)), 65535)", "np.float64(p) * 4294967296.0)), 4294967295)"),
+}
+
+
+def load_philox_mutant(old, new):
+    src = open(PHILOX_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("philox_mutant")
+    exec(compile(src.replace(old, new), "philox_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def run_stream_pins(mod):
+    pins.check_keep_mask(mod.dropout_keep, mod.keep_threshold)
+
+
+def test_unmutated_philox_passes():
+    run_stream_pins(load_philox_mutant("def effective_p(", "def effective_p("))
+
+
+@pytest.mark.parametrize("name", sorted(PHILOX_MUTANTS))
+def test_philox_mutant_is_caught(name):
+    mod = load_philox_mutant(*PHILOX_MUTANTS[name])
+    with pytest.raises(Exception):
+        run_stream_pins(mod)
