@@ -35,6 +35,18 @@ namespace {
 constexpr int kDecThreads = 64;  // one wave per workgroup
 constexpr int kDecBC = 32;       // keys per tile
 
+// Maximum and sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 }  // namespace
 
 // Two waves per SIMD at D <= 128 (for D = 128 the compiler then spills a few
@@ -249,17 +261,29 @@ void decode_split_kernel(DecParams p) {
     }
 }
 
-// One wave per query row: lanes cover d (4 consecutive values each).
+// One wave per query row: lanes cover d (4 consecutive values each). The
+// row index is wave-uniform, so the split LSEs are scalar loads; the maximum
+// and the weight sum run across lanes (split s on lane s % 64), and the
+// partial outputs are fetched eight splits at a time.
 template <int DT, int D>
 __global__ __launch_bounds__(256)
 void decode_merge_kernel(DecParams p, long long rows) {
-    const long long prow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long prow =
+        (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     if (prow >= rows) return;
     const int S = p.S;
     const float* pl = p.part_lse + prow * S;
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pl[s]);
+    float mloc = -__builtin_huge_valf();
+    for (int s = lane; s < S; s += 64) mloc = fmaxf(mloc, pl[s]);
+    const float M = wave_max(mloc);
+    const bool any = M != -__builtin_huge_valf();  // some split saw an allowed key
+    float wl = 0.0f;
+    for (int s = lane; s < S; s += 64) {
+        const float ls = pl[s];
+        wl += (any && ls != -__builtin_huge_valf()) ? fast_exp2(ls - M) : 0.0f;
+    }
+    const float wsum = wave_sum(wl);
     const long long bhk = prow / p.R;
     const int r = (int)(prow - bhk * p.R);
     const int b = (int)(bhk / p.Hkv);
@@ -268,19 +292,24 @@ void decode_merge_kernel(DecParams p, long long rows) {
     const int i = r - g * p.Nq;
     const int hq = hkv * p.G + g;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float wsum = 0.0f;
     const int d0 = lane * 4;
-    if (M != -__builtin_huge_valf()) {
-        for (int s = 0; s < S; ++s) {
-            const float ls = pl[s];
-            if (ls == -__builtin_huge_valf()) continue;
-            const float w = fast_exp2(ls - M);
-            wsum += w;
-            if (d0 < D) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(p.part_o + (prow * S + s) * D + d0);
+    if (any && d0 < D) {
+        const float* po = p.part_o + prow * S * D + d0;
+        for (int s0 = 0; s0 < S; s0 += 8) {
+            f32x4 x[8];
+            float w[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u;
+                const float ls = s < S ? pl[s] : -__builtin_huge_valf();
+                w[u] = ls != -__builtin_huge_valf() ? fast_exp2(ls - M) : 0.0f;
+                // empty splits wrote no partial O: their slot is read but not used
+                x[u] = s < S ? *reinterpret_cast<const f32x4*>(po + (long long)s * D) : f32x4{};
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[u], w[u] > 0.0f ? x[u][e] : 0.0f, acc[e]);
         }
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
