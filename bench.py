@@ -426,7 +426,7 @@ def main():
     rows = w.B * w.Hq * w.N
     work = {"fwd_kernel": (credit["fwd"], w.fwd_bytes()),
             DECODE_UNIT: (credit["fwd"], w.fwd_bytes()),
-            "bwd_pre_kernel": (0.0, 2 * rows * w.d * 2 + 4 * rows),
+            "bwd_pre_kernel": (0.0, 2 * rows * w.d * 2 + 12 * rows),  # O, dO, LSE in; -D, LSE2 out
             "bwd_dkdv_kernel": (credit["bwd_dkdv"], None),
             "bwd_dq_kernel": (credit["bwd_dq"], None)}
     kernels = {}
