@@ -188,70 +188,146 @@ void bwd_dq_kernel(BwdParams p) {
                 s[kt] = f32x16{};
                 dp[kt] = f32x16{};
             }
-            rd(0);
-            if (NS > 1) rd(1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int idx = 0; idx < NS; ++idx) {
-                if (idx + 2 < NS) rd(idx + 2);
-                s[idx / KS] = mfma32<DT>(kr[idx % 3], qf[idx % KS], s[idx / KS]);
-                dp[idx / KS] = mfma32<DT>(vr[idx % 3], gf[idx % KS], dp[idx / KS]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
             // dS^T = P^T (dP^T - D) with P^T = exp2(c*S^T - LSE2), packed to 16 bits
             // in the B-operand order of dQ^T += K^T dS^T. Key kv0 + koff(r) + 4h
             // is masked when it is >= N, (causal) > qrow or (sliding window)
             // < qrow - W + 1: compares with a constant per element, skipped
             // when the block needs no mask.
-            e16x8 dsb[PVS];
-            {
-                // Dropout: dP of a dropped score is zero and a kept one is
-                // scaled by 1/(1-p); P itself (and the row term) are not.
-                uint32_t keep[NKT];
-                if constexpr (DROP) {
+            // Dropout: dP of a dropped score is zero and a kept one is
+            // scaled by 1/(1-p); P itself (and the row term) are not.
+            uint32_t keep[NKT];
+            if constexpr (DROP) {
 #pragma unroll
-                    for (int kt = 0; kt < NKT; ++kt) {
-                        keep[kt] = 0;
+                for (int kt = 0; kt < NKT; ++kt) {
+                    keep[kt] = 0;
 #pragma unroll
-                        for (int gp = 0; gp < 2; ++gp)
-                            keep[kt] |= keep_bits_query_lane(p.drop, kv0 + kt * 32 + 16 * gp + 4 * h, qrow,
-                                                             bh) << (8 * gp);
-                    }
-                }
-                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
-                const int lo = qrow - W + 1 - kv0 - 4 * h;
-#pragma unroll
-                for (int u = 0; u < PVS; ++u) {
-                    const int kt = u >> 1;
-                    const int r0 = (u & 1) * 8;
-                    e16x2 dd[4];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        float dv[2];
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            const int r = r0 + 2 * e2 + w;
-                            const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
-                            float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
-                            if (MASKED && koff > lim) pe = 0.0f;
-                            if (MASKED && WINDOW && koff < lo) pe = 0.0f;
-                            float dpe = dp[kt][r];
-                            if constexpr (DROP) dpe = ((keep[kt] >> r) & 1u) ? dpe * p.drop.scale : 0.0f;
-                            dv[w] = pe * (dpe + ndel);
-                        }
-                        dd[e2] = cvt2<DT>(dv[0], dv[1]);
-                    }
-                    dsb[u] = cat8(dd[0], dd[1], dd[2], dd[3]);
+                    for (int gp = 0; gp < 2; ++gp)
+                        keep[kt] |= keep_bits_query_lane(p.drop, kv0 + kt * 32 + 16 * gp + 4 * h, qrow,
+                                                         bh) << (8 * gp);
                 }
             }
+            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
+            const int lo = qrow - W + 1 - kv0 - 4 * h;
+            e16x2 dd[PVS][4];
+            e16x8 dsb[PVS];
+            // dS^T of registers (r, r+1) of contraction step u (key tile u >> 1).
+            auto sm_pair = [&](int u, int e2) {
+                const int kt = u >> 1;
+                const int r0 = (u & 1) * 8;
+                float dv[2];
 #pragma unroll
-            for (int u = 0; u < PVS; ++u) {
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int ob = u * 16 * KP + dt * 32;
-                    const e16x8 a = join8(lds_read_tr4(Ks + ktr0 + ob), lds_read_tr4(Ks + ktr1 + ob));
-                    dqacc[dt] = mfma32<DT>(a, dsb[u], dqacc[dt]);
+                for (int w = 0; w < 2; ++w) {
+                    const int r = r0 + 2 * e2 + w;
+                    const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
+                    float pe = fast_exp2(fmaf(s[kt][r], c, -lse2));
+                    if (MASKED && koff > lim) pe = 0.0f;
+                    if (MASKED && WINDOW && koff < lo) pe = 0.0f;
+                    float dpe = dp[kt][r];
+                    if constexpr (DROP) dpe = ((keep[kt] >> r) & 1u) ? dpe * p.drop.scale : 0.0f;
+                    dv[w] = pe * (dpe + ndel);
                 }
+                dd[u][e2] = cvt2<DT>(dv[0], dv[1]);
+            };
+            auto pack = [&](int u) { dsb[u] = cat8(dd[u][0], dd[u][1], dd[u][2], dd[u][3]); };
+            // K^T operand of contraction step u, 32-row tile dt.
+            auto ktr = [&](int u, int dt) {
+                const int ob = u * 16 * KP + dt * 32;
+                return join8(lds_read_tr4(Ks + ktr0 + ob), lds_read_tr4(Ks + ktr1 + ob));
+            };
+            if constexpr (NKT == 2) {
+                // Software pipeline of one step, pinned in order by
+                // scheduling barriers between small chunks:
+                //   A0: S^T/dP^T of key tile 0, row reads two products ahead;
+                //   A1: those of tile 1, with tile 0's dS^T and the first
+                //       transposed K reads in their shadow;
+                //   C0: the dQ^T products of contraction steps 0 and 1, with
+                //       tile 1's dS^T and the next transposed reads;
+                //   C1: those of steps 2 and 3.
+                rd(0);
+                rd(1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {  // A0
+                    rd(ks + 2);
+                    s[0] = mfma32<DT>(kr[ks % 3], qf[ks], s[0]);
+                    dp[0] = mfma32<DT>(vr[ks % 3], gf[ks], dp[0]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                e16x8 opA[NDT], opB[NDT];
+                constexpr int PRA = (8 + KS - 1) / KS;
+                constexpr int TRA = (NDT + KS - 1) / KS;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {  // A1
+                    const int idx = KS + ks;
+                    if (idx + 2 < NS) rd(idx + 2);
+                    s[1] = mfma32<DT>(kr[idx % 3], qf[ks], s[1]);
+                    dp[1] = mfma32<DT>(vr[idx % 3], gf[ks], dp[1]);
+#pragma unroll
+                    for (int j = 0; j < PRA; ++j) {
+                        const int pr = ks * PRA + j;
+                        if (pr < 8) sm_pair(pr / 4, pr % 4);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TRA; ++j) {
+                        const int dt = ks * TRA + j;
+                        if (dt < NDT) opA[dt] = ktr(0, dt);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                pack(0);
+                pack(1);
+                constexpr int PRC = (8 + 2 * NDT - 1) / (2 * NDT);
+#pragma unroll
+                for (int k = 0; k < 2 * NDT; ++k) {  // C0: u = 0 (operands A), u = 1 (B)
+                    const int dt = k % NDT;
+                    if (k < NDT) {
+                        dqacc[dt] = mfma32<DT>(opA[dt], dsb[0], dqacc[dt]);
+                        opB[dt] = ktr(1, dt);
+                    } else {
+                        dqacc[dt] = mfma32<DT>(opB[dt], dsb[1], dqacc[dt]);
+                        opA[dt] = ktr(2, dt);
+                    }
+#pragma unroll
+                    for (int j = 0; j < PRC; ++j) {
+                        const int pr = k * PRC + j;
+                        if (pr < 8) sm_pair(2 + pr / 4, pr % 4);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                pack(2);
+                pack(3);
+#pragma unroll
+                for (int k = 0; k < 2 * NDT; ++k) {  // C1: u = 2 (A), u = 3 (B)
+                    const int dt = k % NDT;
+                    if (k < NDT) {
+                        dqacc[dt] = mfma32<DT>(opA[dt], dsb[2], dqacc[dt]);
+                        opB[dt] = ktr(3, dt);
+                    } else {
+                        dqacc[dt] = mfma32<DT>(opB[dt], dsb[3], dqacc[dt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                rd(0);
+                if (NS > 1) rd(1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int idx = 0; idx < NS; ++idx) {
+                    if (idx + 2 < NS) rd(idx + 2);
+                    s[idx / KS] = mfma32<DT>(kr[idx % 3], qf[idx % KS], s[idx / KS]);
+                    dp[idx / KS] = mfma32<DT>(vr[idx % 3], gf[idx % KS], dp[idx / KS]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int u = 0; u < PVS; ++u) {
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) sm_pair(u, e2);
+                    pack(u);
+                }
+#pragma unroll
+                for (int u = 0; u < PVS; ++u)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = mfma32<DT>(ktr(u, dt), dsb[u], dqacc[dt]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
