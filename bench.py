@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
                          "into a traffic summary file and exit")
+    ap.add_argument("--summarize-busy", nargs=3, metavar=("GRBM_DIR", "MFMA_DIR", "OUT"),
+                    help="turn two rocprofv3 --pmc runs of this script (GRBM_GUI_ACTIVE, then "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES) into a clock and matrix-core "
+                         "busy summary and exit")
     return ap.parse_args()
 
 
@@ -192,6 +196,67 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload, mib):
             f.write(f"source_sha256 = {source_hash(kernel)}\n")
         written.append(path)
     print("\n".join(written))
+
+
+XCDS = 8            # MI355X: 8 accelerator complex dies, 32 CUs each
+SIMDS = 256 * 4     # 4 SIMDs per compute unit
+
+
+def summarize_busy(grbm_dir, mfma_dir, out, workload):
+    """Effective clock and matrix-core busy fraction of each attention kernel
+    from two rocprofv3 --pmc runs. GRBM_GUI_ACTIVE comes back summed over the
+    XCDs, so the cycles of one kernel are its value / XCDS and the clock is
+    that over the dispatch's own start/end timestamps.
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD, so / SIMDS gives the
+    busy cycles of the average SIMD; its ratio to the kernel's cycles is the
+    share of the time the matrix cores work."""
+    import csv
+    import glob
+
+    def rows(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            yield from csv.DictReader(open(f))
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            acc.setdefault(r["Kernel_Name"], []).append((float(r["Counter_Value"]), dur))
+        return acc
+
+    grbm = per_kernel(grbm_dir, "GRBM_GUI_ACTIVE")
+    mfma = per_kernel(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    with open(out, "w") as f:
+        f.write(f"# Clock and matrix-core busy fraction on {workload}, from rocprofv3 counters.\n")
+        f.write("# Commands (run from the repository root on the MI355X box):\n")
+        f.write(f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE -f csv -d <grbm_dir> -- python bench.py "
+                f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+        f.write(f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d <mfma_dir> -- "
+                f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+        f.write(f"#   python bench.py --workload {workload} --summarize-busy <grbm_dir> <mfma_dir> <this file>\n")
+        f.write(f"# cycles = GRBM_GUI_ACTIVE / {XCDS} XCDs; clock = cycles / dispatch duration;\n")
+        f.write(f"# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / {SIMDS} SIMDs, as a share of the cycles.\n")
+        f.write("# The counter window is a little longer than the dispatch, so kernels shorter than\n"
+                "# about 0.1 ms read a clock above the real one; the long kernels are not affected.\n")
+        f.write("kernel | dispatches | avg us | clock GHz (min-max) | cycles | MFMA busy cycles per SIMD | busy share\n")
+        for name, v in sorted(grbm.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+            if "attn::" not in name:
+                continue
+            dur = sum(d for _, d in v) / len(v)
+            cyc = sum(c for c, _ in v) / len(v) / XCDS
+            clk = [c / XCDS / d for c, d in v]
+            line = f"{name.split('(')[0]} | {len(v)} | {dur / 1e3:.1f} | {sum(clk) / len(clk):.3f} ({min(clk):.3f}-{max(clk):.3f}) | {cyc:.0f}"
+            m = mfma.get(name)
+            if m:
+                mb = sum(c for c, _ in m) / len(m) / SIMDS
+                line += f" | {mb:.0f} | {mb / cyc:.3f}"
+            f.write(line + "\n")
+    print(out)
 
 
 def time_loop(fn, steps, stream):
@@ -337,6 +402,9 @@ def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.workload)
+        return
+    if args.summarize_busy:
+        summarize_busy(*args.summarize_busy, args.workload)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.workload, args.calibration_copy_mib)
