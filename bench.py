@@ -58,6 +58,9 @@ def parse():
                     help="turn two rocprofv3 --pmc runs of this script (GRBM_GUI_ACTIVE, then "
                          "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES) into a clock and matrix-core "
                          "busy summary and exit")
+    ap.add_argument("--summarize-waves", nargs=2, metavar=("PMC_DIR", "OUT"),
+                    help="turn a rocprofv3 --pmc run of this script with the SQ wave-state "
+                         "counters into a per-kernel breakdown of wave time and exit")
     return ap.parse_args()
 
 
@@ -259,6 +262,50 @@ def summarize_busy(grbm_dir, mfma_dir, out, workload):
     print(out)
 
 
+WAVE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+                 "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+                 "SQ_VALU_MFMA_COEXEC_CYCLES")
+
+
+def summarize_waves(pmc_dir, out, workload):
+    """Where the waves of each attention kernel spend their time, from one
+    rocprofv3 --pmc run with the SQ wave-state counters (all summed over the
+    waves, in units of 4 cycles): issuing an instruction (ACTIVE_INST_ANY),
+    holding a ready instruction that is not issued yet (WAIT_INST_ANY: the
+    unit it needs is busy, e.g. the matrix core), and waiting on a counter
+    or barrier (WAIT_ANY: LDS or memory results, s_barrier). The three add
+    up to SQ_WAVE_CYCLES, which the summary checks."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "attn::" in r["Kernel_Name"] and r["Counter_Name"] in WAVE_COUNTERS:
+                acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    with open(out, "w") as f:
+        f.write(f"# Wave time of each kernel on {workload}, from rocprofv3 SQ counters.\n")
+        f.write("# Commands (run from the repository root on the MI355X box):\n")
+        f.write(f"#   rocprofv3 --pmc {' '.join(WAVE_COUNTERS)} -f csv -d <pmc_dir> -- python bench.py "
+                f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+        f.write(f"#   python bench.py --workload {workload} --summarize-waves <pmc_dir> <this file>\n")
+        f.write("# Shares of SQ_WAVE_CYCLES: issuing = ACTIVE_INST_ANY, ready-not-issued = WAIT_INST_ANY,\n"
+                "# waiting on counters/barrier = WAIT_ANY; the VALU (matrix products included) and LDS\n"
+                "# issue shares are parts of 'issuing'.\n")
+        f.write("kernel | issuing | ready, not issued | waiting on counters/barrier | sum | VALU issue | LDS issue\n")
+        for name, c in sorted(acc.items()):
+            avg = {k: sum(v) / len(v) for k, v in c.items()}
+            wc = avg["SQ_WAVE_CYCLES"]
+            a, wi, wa = avg["SQ_ACTIVE_INST_ANY"] / wc, avg["SQ_WAIT_INST_ANY"] / wc, avg["SQ_WAIT_ANY"] / wc
+            f.write(f"{name.split('(')[0]} | {a:.3f} | {wi:.3f} | {wa:.3f} | {a + wi + wa:.3f} | "
+                    f"{avg['SQ_ACTIVE_INST_VALU'] / wc:.3f} | {avg['SQ_ACTIVE_INST_LDS'] / wc:.3f}\n")
+    print(out)
+
+
 def time_loop(fn, steps, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -402,6 +449,9 @@ def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.workload)
+        return
+    if args.summarize_waves:
+        summarize_waves(*args.summarize_waves, args.workload)
         return
     if args.summarize_busy:
         summarize_busy(*args.summarize_busy, args.workload)
