@@ -231,12 +231,29 @@ void bwd_dkdv_kernel(BwdParams p) {
             offd[i] = lc < D / 8 ? (uint32_t)row * sd2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
     }
-    auto issue_step = [&](const Step& st, int bufi) {
+    // Buffer bases and sizes of a step's loads; the unmasked steps of a head
+    // advance them by one query block instead of recomputing them.
+    struct Issue {
+        const e16* bq;
+        const e16* bd;
+        const float* br;
+        uint32_t nq, nd, nr;
+    };
+    auto issue_params = [&](const Step& st) {
         const int r0 = st.qb * BQ;
-        const size_t row_off = st.rt;
         const uint32_t sq2 = (uint32_t)p.sq.n * 2u, sd2 = (uint32_t)p.sdo.n * 2u;
-        const auto rq = buf_rsrc(st.qh + r0 * (int)p.sq.n, (uint32_t)(N - r0 - 1) * sq2 + D * 2);
-        const auto rd = buf_rsrc(st.dh + r0 * (int)p.sdo.n, (uint32_t)(N - r0 - 1) * sd2 + D * 2);
+        Issue x;
+        x.bq = st.qh + r0 * (int)p.sq.n;
+        x.bd = st.dh + r0 * (int)p.sdo.n;
+        x.nq = (uint32_t)(N - r0 - 1) * sq2 + D * 2;
+        x.nd = (uint32_t)(N - r0 - 1) * sd2 + D * 2;
+        x.br = (wave == 0 ? p.lse2 : p.delta) + st.rt + r0;
+        x.nr = (uint32_t)(N - r0) * 4u;
+        return x;
+    };
+    auto issue_loads = [&](const Issue& x, int bufi) {
+        const auto rq = buf_rsrc(x.bq, x.nq);
+        const auto rd = buf_rsrc(x.bd, x.nd);
         char* qt_lds = reinterpret_cast<char*>(qtile(bufi));
         char* dt_lds = reinterpret_cast<char*>(dotile(bufi));
 #pragma unroll
@@ -247,12 +264,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                 buf_load16_to_lds(rd, dt_lds + j * 1024, offd[i]);
             }
         }
-        if (wave < 2) {
-            const float* src = (wave == 0 ? p.lse2 : p.delta) + row_off + r0;
-            const auto rr = buf_rsrc(src, (uint32_t)(N - r0) * 4u);
-            buf_load4_to_lds(rr, wave == 0 ? lsetile(bufi) : deltile(bufi), (uint32_t)lane * 4u);
-        }
+        if (wave < 2)
+            buf_load4_to_lds(buf_rsrc(x.br, x.nr), wave == 0 ? lsetile(bufi) : deltile(bufi), (uint32_t)lane * 4u);
     };
+    auto issue_step = [&](const Step& st, int bufi) { issue_loads(issue_params(st), bufi); };
 
     TileIO<D, BQ, T> qio, doio;
     // Row terms of the step: threads 0 .. BQ-1 fetch log2-domain LSE, BQ ..
@@ -308,16 +323,33 @@ void bwd_dkdv_kernel(BwdParams p) {
     // the next step, whose loads it issues. The last step reloads its own
     // tiles into the idle buffer (never read), which keeps the body free of
     // branches.
+    Issue cx = issue_params(first);  // the step whose tiles are in LDS
     auto run_step = [&](int it, Step& cur, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int bufi = it & 1;
         const int g = cur.g;
         const int q0 = cur.qb * BQ;
-        cur = next_step(cur, it + 1);
-        if constexpr (DIRECT)
-            issue_step(cur, bufi ^ 1);
-        else
+        if constexpr (DIRECT) {
+            // Unmasked steps move on to the next query block of the same head
+            // (a few scalar adds); the others go through the general cursor.
+            if (!MASKED && cur.qb + 1 < qu_end) {
+                const int sqb = BQ * (int)p.sq.n, sdb = BQ * (int)p.sdo.n;
+                cx.bq += sqb;
+                cx.bd += sdb;
+                cx.br += BQ;
+                cx.nq -= (uint32_t)sqb * 2u;
+                cx.nd -= (uint32_t)sdb * 2u;
+                cx.nr -= BQ * 4u;
+                cur.qb += 1;
+            } else {
+                cur = next_step(cur, it + 1);
+                cx = issue_params(cur);
+            }
+            issue_loads(cx, bufi ^ 1);
+        } else {
+            cur = next_step(cur, it + 1);
             load_step(cur);
+        }
 
         // Every step runs for every wave (no data-dependent branch in the
         // loop body): a wave whose keys all lie after this query block just
@@ -401,6 +433,9 @@ void bwd_dkdv_kernel(BwdParams p) {
                 }
                 pp[u][e2] = cvt2<DT>(pv[0], pv[1]);
                 dd[u][e2] = cvt2<DT>(dv[0], dv[1]);
+                // keep the conversions in this chunk (the compiler would sink
+                // them all to the pack, outside the products' shadow)
+                asm volatile("" : "+v"(pp[u][e2]), "+v"(dd[u][e2]));
             };
             auto pack = [&](int u) {
                 pb[u] = cat8(pp[u][0], pp[u][1], pp[u][2], pp[u][3]);
@@ -441,6 +476,14 @@ void bwd_dkdv_kernel(BwdParams p) {
                     dp[qt] = mfma32<DT>(ra_d[idx % 3], vf[ks], dp[qt]);
                 };
                 e16x8 opA_d[NDT], opA_q[NDT], opB_d[NDT], opB_q[NDT];
+                auto tr_read_d = [&](int u, int dt, e16x8* ado) {
+                    const int ob = u * 16 * QP + dt * 32;
+                    ado[dt] = join8(lds_read_tr4(dOs + qtr0 + ob), lds_read_tr4(dOs + qtr1 + ob));
+                };
+                auto tr_read_q = [&](int u, int dt, e16x8* aq) {
+                    const int ob = u * 16 * QP + dt * 32;
+                    aq[dt] = join8(lds_read_tr4(Qs + qtr0 + ob), lds_read_tr4(Qs + qtr1 + ob));
+                };
                 auto tr_read = [&](int u, int dt, e16x8* ado, e16x8* aq) {
                     const int ob = u * 16 * QP + dt * 32;
                     ado[dt] = join8(lds_read_tr4(dOs + qtr0 + ob), lds_read_tr4(dOs + qtr1 + ob));
@@ -486,14 +529,22 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int k = 0; k < 2 * NDT; ++k) {
                     const int u = k / NDT, dt = k % NDT;
+                    // dV half: its product, then the dO^T reads of the next step
                     if (u == 0) {
                         mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opA_d[dt], pb[0]);
-                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opA_q[dt], dsb[0]);
-                        tr_read(1, dt, opB_d, opB_q);
+                        tr_read_d(1, dt, opB_d);
                     } else {
                         mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opB_d[dt], pb[1]);
+                        tr_read_d(2, dt, opA_d);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // dK half: its product, the Q^T reads and a share of the softmax
+                    if (u == 0) {
+                        mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opA_q[dt], dsb[0]);
+                        tr_read_q(1, dt, opB_q);
+                    } else {
                         mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opB_q[dt], dsb[1]);
-                        tr_read(2, dt, opA_d, opA_q);
+                        tr_read_q(2, dt, opA_q);
                     }
 #pragma unroll
                     for (int j = 0; j < (8 + 2 * NDT - 1) / (2 * NDT); ++j) {
@@ -510,8 +561,10 @@ void bwd_dkdv_kernel(BwdParams p) {
                     const int u = 2 + k / NDT, dt = k % NDT;
                     if (u == 2) {
                         mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opA_d[dt], pb[2]);
+                        tr_read_d(3, dt, opB_d);
+                        __builtin_amdgcn_sched_barrier(0);
                         mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opA_q[dt], dsb[2]);
-                        tr_read(3, dt, opB_d, opB_q);
+                        tr_read_q(3, dt, opB_q);
                     } else {
                         mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opB_d[dt], pb[3]);
                         mfma32_agpr<DT, ACC_GAP>(dkacc[dt], opB_q[dt], dsb[3]);
