@@ -321,8 +321,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     // Step it works on `cur` (whose tiles are in LDS) and moves `cur` on to
     // the next step, whose loads it issues. The last step reloads its own
-    // tiles into the idle buffer (never read), which keeps the body free of
-    // branches.
+    // tiles into the idle buffer (never read), so no step tests for being
+    // the last one.
     Issue cx = issue_params(first);  // the step whose tiles are in LDS
     auto run_step = [&](int it, Step& cur, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -529,7 +529,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int k = 0; k < 2 * NDT; ++k) {
                     const int u = k / NDT, dt = k % NDT;
-                    // dV half: its product, then the dO^T reads of the next step
+                    // dV half: its product, then the dO^T reads of the next
+                    // contraction step
                     if (u == 0) {
                         mfma32_agpr<DT, ACC_GAP>(dvacc[dt], opA_d[dt], pb[0]);
                         tr_read_d(1, dt, opB_d);
