@@ -26,6 +26,7 @@ CASES = [
     (2, 12, 4, 1, 333, 96, 64, "full", "fp16"),
     (64, 8, 8, 1, 256, 128, "causal", "ragged", "bf16"),  # many groups: one split
     (1, 32, 8, 1, 20000, 128, "causal", "full", "bf16"),  # long cache: many splits
+    (1, 8, 1, 2, (1 << 20) + 77, 128, "causal", "full", "bf16"),  # 2^20 keys: 2048 splits
 ]
 
 
