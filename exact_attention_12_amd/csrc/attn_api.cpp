@@ -157,7 +157,7 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     if (!aligned16(lse)) return ATTN_ERR_ALIGN;
 
     attn::FwdPlan plan;
-    attn::fwd_plan(pr->B, pr->Hq, pr->N, pr->d, &plan);
+    attn::fwd_plan(pr->B, pr->Hq, pr->N, pr->d, mask != attn::kMaskNone, &plan);
     attn::FwdParams p;
     p.q = q->data;
     p.k = k->data;
@@ -517,12 +517,11 @@ const char* attn_status_string(attn_status status) {
 const char* attn_last_hip_error(void) { return g_last_hip_error; }
 
 attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn_plan* plan) {
-    (void)causal;
     if (!plan) return ATTN_ERR_NULL;
     const attn_status st = check_shape(B, Hq, Hkv, N, d);
     if (st != ATTN_OK) return st;
     attn::FwdPlan fp;
-    attn::fwd_plan(B, Hq, N, d, &fp);
+    attn::fwd_plan(B, Hq, N, d, causal != 0, &fp);
     plan->rows_per_wave = fp.rows_per_wave;
     plan->block_q = fp.block_q;
     plan->block_kv = fp.block_kv;

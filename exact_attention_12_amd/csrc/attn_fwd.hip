@@ -84,7 +84,7 @@ void fwd_kernel(FwdParams p) {
     // latest (heaviest) query blocks come first.
     const int bid = blockIdx.x;
     const int bh = xcd_head(bid % p.BH, p.BH);
-    const int qb = CAUSAL ? (p.nqb - 1 - bid / p.BH) : (bid / p.BH);
+    const int qb = causal_block(bid / p.BH, p.nqb, NW == 4 && gridDim.x <= 512, CAUSAL);
     const int b = bh / p.Hq;
     const int hq = bh - b * p.Hq;
     const int hkv = hq / p.G;
@@ -477,9 +477,9 @@ static hipError_t launch_fwd_t(const FwdParams& p, int d, int mask, const FwdPla
 // gives every CU a workgroup. Shorter sequences use 4 waves (twice the
 // workgroups); d > 128 always uses 4.
 template <int D>
-static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
+static void plan_d(int B, int Hq, int N, bool causal, FwdPlan* plan) {
     const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
-    const int waves = (D <= 128 && wg256 >= 256) ? 8 : 4;
+    const int waves = (D <= 128 && wg256 >= (causal ? 512 : 256)) ? 8 : 4;
     const int BQ = waves * 32;
     const int BC = FwdTile<D>::BLOCK_KV;
     plan->rows_per_wave = 32;
@@ -491,10 +491,10 @@ static void plan_d(int B, int Hq, int N, FwdPlan* plan) {
     plan->lds_bytes = 2 * BC * (k_pitch(D) + v_pitch(D)) * 2;
 }
 
-bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan) {
+bool fwd_plan(int B, int Hq, int N, int d, bool causal, FwdPlan* plan) {
     switch (d) {
 #define ATTN_PLAN_CASE(D_) \
-        case D_: plan_d<D_>(B, Hq, N, plan); return true;
+        case D_: plan_d<D_>(B, Hq, N, causal, plan); return true;
         ATTN_FOR_EACH_HEAD_DIM(ATTN_PLAN_CASE)
 #undef ATTN_PLAN_CASE
         default: return false;

@@ -153,7 +153,20 @@ struct FwdPlan {
     int lds_bytes;
 };
 
-bool fwd_plan(int B, int Hq, int N, int d, FwdPlan* plan);
+bool fwd_plan(int B, int Hq, int N, int d, bool causal, FwdPlan* plan);
+// Query block of rank t (0 = first dispatched) among nqb blocks of a head.
+// Under a causal mask late blocks carry the most work. When a CU holds two
+// workgroups at once and the whole grid is resident (`paired`), the second
+// half of the ranks runs light blocks first, so that the CU that takes rank t
+// in the first pass and rank t + half in the second gets a heavy and a light
+// block; otherwise the heaviest blocks go first.
+__device__ __forceinline__ int causal_block(int t, int nqb, bool paired, bool causal) {
+    if (!causal) return t;
+    if (!paired) return nqb - 1 - t;
+    const int half = (nqb + 1) / 2;
+    return t < half ? nqb - 1 - t : t - half;
+}
+
 
 // Decoding against a key/value cache: Nq new queries per sequence, at
 // positions L_b - Nq .. L_b - 1 of a cache holding L_b valid rows (of Nk).

@@ -314,8 +314,10 @@ const char* attn_last_hip_error(void);
 /*
  * Tile plan of the forward kernel for a shape: query rows per wave, rows
  * of Q per workgroup, keys per inner step, threads per workgroup,
- * number of workgroups and bytes of LDS per workgroup. Host-only arithmetic
- * (no device call). Returns ATTN_OK or the validation error for that shape.
+ * number of workgroups and bytes of LDS per workgroup. `causal` is nonzero
+ * for the causal and sliding-window masks (their workgroups differ in work,
+ * which changes the plan for short sequences). Host-only arithmetic (no
+ * device call). Returns ATTN_OK or the validation error for that shape.
  */
 typedef struct attn_plan {
     int rows_per_wave;
