@@ -319,6 +319,34 @@ def time_loop(fn, steps, stream):
     return start.elapsed_time(end) / steps  # ms
 
 
+def unfused_baseline(w, g, o_fused, steps, stream, fused_ms):
+    """Standard attention as the pages write it ([CANN-FA] standard attention
+    code; [FA-seqlen] times it against FlashAttention by sequence length), in
+    torch eager bf16 on the same GPU: S = Q K^T * scale, P = softmax(S),
+    O = P V, with S and P materialised in HBM (B*H*N^2 16-bit values each).
+    Timed over the same number of steps as the fused forward; only for
+    unmasked multi-head forward workloads. The right operand of each batched
+    product is contiguous."""
+    import torch
+    q, k, v = g["q"], g["k"], g["v"]
+    kt = k.transpose(-1, -2).contiguous()
+
+    def run():
+        s = torch.matmul(q, kt) * w.scale
+        return torch.matmul(torch.softmax(s, dim=-1), v), s
+
+    o_ref, s = run()
+    torch.cuda.synchronize()
+    sp = si.score_matrix_bytes(w.B, w.Hq, w.N, 2)
+    assert s.numel() * s.element_size() == sp, "S is not B*H*N^2 16-bit values"
+    del s
+    o_err = float((o_ref.float() - o_fused.float()).abs().max())
+    ms = time_loop(lambda: run(), steps, stream)
+    return {"ms": round(ms, 4), "tflops": round(w.fwd_flops() / ms / 1e9, 2),
+            "s_and_p_bytes": 2 * sp, "fused_speedup": round(ms / fused_ms, 3),
+            "o_max_abs_diff_vs_fused": round(o_err, 5)}
+
+
 def cpu_baseline(w, inputs, budget_s):
     """Time the fp64 oracle on whole heads of the same workload (rank 0 only).
 
@@ -601,6 +629,12 @@ def main():
     par = parity_sample(w, inputs, o.transpose(1, 2) if w.layout == "bshd" else o, lse)
     print(f"[bench] parity sample: {par}", file=sys.stderr, flush=True)
 
+    unfused = None
+    if (not w.backward and not w.causal and w.window is None and w.Nq is None and w.dropout is None
+            and w.Hq == w.Hkv and w.layout == "bhsd"):
+        unfused = unfused_baseline(w, g, o, args.steps, stream, kernels[names[0]]["ms"])
+        print(f"[bench] unfused torch baseline: {unfused}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inputs, args.cpu_seconds)
@@ -631,6 +665,8 @@ def main():
         "cpu_baseline": cpu,
         "parity_sample": par,
     }
+    if unfused is not None:
+        line["unfused_baseline"] = unfused
     print(json.dumps(line), flush=True)
 
 
