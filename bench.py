@@ -319,6 +319,26 @@ def time_loop(fn, steps, stream):
     return start.elapsed_time(end) / steps  # ms
 
 
+def cold_time(fn, steps, stream, scratch_mib=512):
+    """Average time of fn when the caches start cold: before each call a
+    scratch buffer larger than L2 and the 256 MB MALL is overwritten (not
+    timed); each call is bracketed by its own events."""
+    import torch
+    scratch = torch.empty(scratch_mib * (1 << 18), dtype=torch.float32, device="cuda")
+    total = 0.0
+    for _ in range(steps):
+        scratch.fill_(1.0)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        total += start.elapsed_time(end)
+    del scratch
+    return total / steps  # ms
+
+
 def unfused_baseline(w, g, o_fused, steps, stream, fused_ms):
     """Standard attention as the pages write it ([CANN-FA] standard attention
     code; [FA-seqlen] times it against FlashAttention by sequence length), in
@@ -629,6 +649,11 @@ def main():
     par = parity_sample(w, inputs, o.transpose(1, 2) if w.layout == "bshd" else o, lse)
     print(f"[bench] parity sample: {par}", file=sys.stderr, flush=True)
 
+    cold = None
+    if not w.backward and w.Nq is None and w.N <= 1024:
+        cold = {"fwd_ms": round(cold_time(run_fwd, args.steps, stream), 4), "scratch_mib": 512}
+        print(f"[bench] cold-cache forward: {cold}", file=sys.stderr, flush=True)
+
     unfused = None
     if (not w.backward and not w.causal and w.window is None and w.Nq is None and w.dropout is None
             and w.Hq == w.Hkv and w.layout == "bhsd"):
@@ -665,6 +690,8 @@ def main():
         "cpu_baseline": cpu,
         "parity_sample": par,
     }
+    if cold is not None:
+        line["cold_cache"] = cold
     if unfused is not None:
         line["unfused_baseline"] = unfused
     print(json.dumps(line), flush=True)
