@@ -58,6 +58,9 @@ def parse():
                     help="turn two rocprofv3 --pmc runs of this script (GRBM_GUI_ACTIVE, then "
                          "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES) into a clock and matrix-core "
                          "busy summary and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "OUT"),
+                    help="tabulate the per-dispatch averages of every counter of a rocprofv3 "
+                         "--pmc run of this script for the attention kernels and exit")
     ap.add_argument("--summarize-waves", nargs=2, metavar=("PMC_DIR", "OUT"),
                     help="turn a rocprofv3 --pmc run of this script with the SQ wave-state "
                          "counters into a per-kernel breakdown of wave time and exit")
@@ -265,6 +268,37 @@ def summarize_busy(grbm_dir, mfma_dir, out, workload):
 WAVE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
                  "SQ_VALU_MFMA_COEXEC_CYCLES")
+
+
+def summarize_counters(pmc_dir, out, workload):
+    """Per-dispatch averages of every counter a rocprofv3 --pmc run collected,
+    for the attention kernels, with the command that collects them."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "attn::" in r["Kernel_Name"]:
+                acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    names = sorted({c for v in acc.values() for c in v})
+    with open(out, "w") as f:
+        f.write(f"# Counters of the attention kernels on {workload}, per dispatch (rocprofv3).\n")
+        f.write("# Commands (run from the repository root on the MI355X box):\n")
+        f.write(f"#   rocprofv3 --pmc {' '.join(names)} -f csv -d <pmc_dir> -- python bench.py "
+                f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+        f.write(f"#   python bench.py --workload {workload} --summarize-counters <pmc_dir> <this file>\n")
+        f.write("# Values are summed over the chip by rocprofv3; SQ_INSTS_* count instructions,\n"
+                "# SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE count LDS cycles.\n")
+        f.write("kernel | " + " | ".join(names) + "\n")
+        for name, c in sorted(acc.items()):
+            f.write(name.split("(")[0] + " | " + " | ".join(
+                f"{sum(c[n]) / len(c[n]):.4g}" if n in c else "-" for n in names) + "\n")
+    print(out)
 
 
 def summarize_waves(pmc_dir, out, workload):
@@ -497,6 +531,9 @@ def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.workload)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.workload)
         return
     if args.summarize_waves:
         summarize_waves(*args.summarize_waves, args.workload)

@@ -107,3 +107,16 @@ def test_wave_summary_shares_add_up(tmp_path):
     cols = [float(c) for c in line.split("|")[1:]]
     assert cols[:4] == pytest.approx([0.4, 0.35, 0.25, 1.0])
     assert cols[4:] == pytest.approx([0.2, 0.05])
+
+
+def test_counter_summary_lists_every_counter(tmp_path):
+    dk = "void attn::bwd_dkdv_kernel<0, 128, 1, false>(attn::BwdParams)"
+    other = "void at::native::vectorized_elementwise_kernel<neg_kernel>"
+    _write_counters(tmp_path / "c", [(dk, "SQ_INSTS_VALU", 10, 0, 1), (dk, "SQ_INSTS_VALU", 30, 0, 1),
+                                     (dk, "SQ_LDS_BANK_CONFLICT", 0, 0, 1), (other, "SQ_INSTS_VALU", 5, 0, 1)])
+    out = tmp_path / "c.txt"
+    bench.summarize_counters(str(tmp_path / "c"), str(out), "c5_bwd_d128")
+    text = out.read_text()
+    assert "--pmc SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT " in text
+    rows = [x for x in text.splitlines() if x.startswith("void ")]
+    assert rows == ["void attn::bwd_dkdv_kernel<0, 128, 1, false> | 20 | 0"]
