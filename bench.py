@@ -173,8 +173,13 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload, mib):
     written = []
     for kernel in ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel",
                    "decode_split_kernel", "decode_merge_kernel"):
+        # the dK/dV pass runs the 64-keys-per-wave kernel on large d = 128 grids
+        prefixes = [f"{kernel}<"] + (["bwd_dkdv_wide_kernel<"] if kernel == "bwd_dkdv_kernel" else [])
+        hits = [(pf, k) for pf in prefixes for k in fetch if pf in k]
+        if not hits:
+            continue
         try:
-            kf, kw = find(fetch, f"{kernel}<"), find(write, f"{kernel}<")
+            kf, kw = hits[0][1], find(write, hits[0][0])
         except SystemExit:
             continue
         fb = fetch[kf] * sf * 1024.0

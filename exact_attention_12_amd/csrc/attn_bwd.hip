@@ -629,7 +629,411 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------- dK, dV (64 keys per wave)
+
+// The same pass for d = 128 without dropout, with 64 keys per wave (256 per
+// workgroup): every Q and dO row read and every transposed read feeds two
+// products, one per 32-key half, so a wave issues about a third fewer LDS
+// reads per product than with 32 keys. K stays in VGPRs as the B operand of
+// S; V moves to LDS and is read row-wise as the B operand of dP; dK^T and
+// dV^T of the 64 keys fill the 256 AGPRs. Steps of 32 query rows, in five
+// regions pinned by scheduling barriers:
+//   S:  the S products of both halves, with the row reads;
+//   dP: the dP products, with P of the first 16 rows in their shadow;
+//   V0: dV products of rows 0..15, with P of rows 16..31;
+//   V1: dV products of rows 16..31, with dS of rows 0..15;
+//   K0, K1: dK products, with dS of rows 16..31 and the Q^T reads.
+template <int DT, int MASK>
+__global__ __launch_bounds__(256, 1)
+void bwd_dkdv_wide_kernel(BwdParams p) {
+    constexpr int D = 128;
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
+    constexpr int NW = 4;
+    constexpr int BK = NW * 64;   // keys per workgroup
+    constexpr int BQ = 32;        // query rows per step
+    constexpr int KS = D / 16;
+    constexpr int NDT = D / 32;
+    constexpr int QP = sw_pitch(D);  // Q, dO tiles: row reads and transposing reads
+    constexpr int VP = D + 8;        // V rows: row reads only
+    constexpr int TILE = BQ * QP;
+    constexpr int RT = 64;           // row-term slots per buffer (one 64-lane load)
+    constexpr int BUF = 2 * TILE * 2 + 2 * RT * 4;
+    constexpr int VBYTES = BK * VP * 2;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[VBYTES + 2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int N = p.N;
+
+    const int BHk = p.B * p.Hkv;
+    const int bid = blockIdx.x;
+    const int kb = bid / BHk;  // ascending key blocks: heaviest first when causal
+    const int bhk = bid - kb * BHk;
+    const int b = bhk / p.Hkv;
+    const int hkv = bhk - b * p.Hkv;
+    const int k0 = kb * BK;
+    const int kw0 = k0 + wave * 64;
+
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
+
+    e16* Vs = reinterpret_cast<e16*>(smem_raw);
+    auto qtile = [&](int bufi) { return reinterpret_cast<e16*>(smem_raw + VBYTES + bufi * BUF); };
+    auto dotile = [&](int bufi) { return qtile(bufi) + TILE; };
+    auto lsetile = [&](int bufi) { return reinterpret_cast<float*>(smem_raw + VBYTES + bufi * BUF + 4 * TILE); };
+    auto deltile = [&](int bufi) { return lsetile(bufi) + RT; };
+
+    // K of the wave's two 32-key halves as B operands (lane = key); the
+    // wave's 64 V rows into its own part of the V region (zeros past N).
+    e16x8 kf[2][KS];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int key = kw0 + 32 * j + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[j][ks] = key < N ? *reinterpret_cast<const e16x8*>(Kh + key * p.sk.n + ks * 16 + h * 8) : e16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < 64 * (D / 8) / 64; ++i) {
+        const int c = i * 64 + lane;
+        const int row = c / (D / 8), col = c - row * (D / 8);
+        const int key = kw0 + row;
+        const uint4 v = key < N ? *reinterpret_cast<const uint4*>(Vh + key * p.sv.n + col * 8) : zero4();
+        *reinterpret_cast<uint4*>(Vs + (wave * 64 + row) * VP + col * 8) = v;
+    }
+
+    const int nqb = (N + BQ - 1) / BQ;
+    const int qb_start = CAUSAL ? (k0 / BQ) : 0;
+    const int W = WINDOW ? p.window : 0;
+    const int qb_stop = WINDOW ? min(nqb, (k0 + BK - 1 + W - 1) / BQ + 1) : nqb;
+    const int nq_iter = qb_stop - qb_start;
+    const int total = p.G * nq_iter;
+    // Unmasked query blocks [qu_begin, qu_end), as in the 32-key kernel.
+    int qu_begin = qb_start, qu_end = qb_stop;
+    if (CAUSAL) qu_begin = min(qb_stop, max(qb_start, (k0 + BK - 1 + BQ - 1) / BQ));
+    if (WINDOW) {
+        const int t = k0 + W - BQ;
+        qu_end = max(qu_begin, min(qb_stop, t >= 0 ? t / BQ + 1 : 0));
+    }
+    const int nu = qu_end - qu_begin;
+    const int nmG = p.G * (nq_iter - nu);
+    struct Step {
+        int g, qb;
+        const e16* qh;
+        const e16* dh;
+        size_t rt;
+    };
+    const int hq0 = hkv * p.G;
+    const Step head0{0, 0, static_cast<const e16*>(p.q) + b * p.sq.b + hq0 * p.sq.h,
+                     static_cast<const e16*>(p.dout) + b * p.sdo.b + hq0 * p.sdo.h,
+                     ((size_t)b * p.Hq + hq0) * N};
+    const int qm_first = qb_start < qu_begin ? qb_start : qu_end;
+    auto next_head = [&](Step st, int qb) {
+        st.g += 1;
+        st.qb = qb;
+        st.qh += p.sq.h;
+        st.dh += p.sdo.h;
+        st.rt += N;
+        return st;
+    };
+    auto next_step = [&](Step st, int it_next) {
+        if (it_next >= total) return st;
+        const int qb = st.qb + 1;
+        if (it_next < nmG) {
+            const int qn = qb == qu_begin ? qu_end : qb;
+            if (qn == qb_stop) return next_head(st, qm_first);
+            st.qb = qn;
+            return st;
+        }
+        if (it_next == nmG) {
+            Step hh = head0;
+            hh.qb = qu_begin;
+            return hh;
+        }
+        if (qb == qu_end) return next_head(st, qu_begin);
+        st.qb = qb;
+        return st;
+    };
+    Step first = head0;
+    first.qb = nmG > 0 ? qm_first : qu_begin;
+
+    constexpr int CKQ = QP / 8;
+    constexpr int NLQ = BQ * CKQ / 64;
+    constexpr int LPWQ = (NLQ + NW - 1) / NW;
+    static_assert(BQ * CKQ % 64 == 0, "tile must be whole loads");
+    uint32_t offq[LPWQ], offd[LPWQ];
+    {
+        const uint32_t sq2 = (uint32_t)p.sq.n * 2u, sd2 = (uint32_t)p.sdo.n * 2u;
+#pragma unroll
+        for (int i = 0; i < LPWQ; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKQ;
+            const int lc = (chunk - row * CKQ) ^ sw_swizzle(row);
+            offq[i] = lc < D / 8 ? (uint32_t)row * sq2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+            offd[i] = lc < D / 8 ? (uint32_t)row * sd2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+        }
+    }
+    struct Issue {
+        const e16* bq;
+        const e16* bd;
+        const float* br;
+        uint32_t nq, nd, nr;
+    };
+    auto issue_params = [&](const Step& st) {
+        const int r0 = st.qb * BQ;
+        const uint32_t sq2 = (uint32_t)p.sq.n * 2u, sd2 = (uint32_t)p.sdo.n * 2u;
+        Issue x;
+        x.bq = st.qh + r0 * (int)p.sq.n;
+        x.bd = st.dh + r0 * (int)p.sdo.n;
+        x.nq = (uint32_t)(N - r0 - 1) * sq2 + D * 2;
+        x.nd = (uint32_t)(N - r0 - 1) * sd2 + D * 2;
+        x.br = (wave == 0 ? p.lse2 : p.delta) + st.rt + r0;
+        x.nr = (uint32_t)(N - r0) * 4u;
+        return x;
+    };
+    auto issue_loads = [&](const Issue& x, int bufi) {
+        const auto rq = buf_rsrc(x.bq, x.nq);
+        const auto rd = buf_rsrc(x.bd, x.nd);
+        char* qt_lds = reinterpret_cast<char*>(qtile(bufi));
+        char* dt_lds = reinterpret_cast<char*>(dotile(bufi));
+#pragma unroll
+        for (int i = 0; i < LPWQ; ++i) {
+            const int j = wave + i * NW;
+            if (NLQ % NW == 0 || j < NLQ) {
+                buf_load16_to_lds(rq, qt_lds + j * 1024, offq[i]);
+                buf_load16_to_lds(rd, dt_lds + j * 1024, offd[i]);
+            }
+        }
+        if (wave < 2)
+            buf_load4_to_lds(buf_rsrc(x.br, x.nr), wave == 0 ? lsetile(bufi) : deltile(bufi), (uint32_t)lane * 4u);
+    };
+
+    f32x16 dkacc[2][NDT], dvacc[2][NDT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) { dkacc[j][dt] = f32x16{}; dvacc[j][dt] = f32x16{}; }
+
+    const float c = p.c;
+    const int g16 = lane >> 4;
+    const int j16 = lane & 15;
+    const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
+    const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
+    const int qrd[2] = {sw_off(l32, h * 8, QP), sw_off(l32, 16 + h * 8, QP)};
+    const int qtr0 = sw_off(tr_row, tr_col, QP), qtr1 = sw_off(tr_row + 8, tr_col, QP);
+    const e16* Vl = Vs + (wave * 64 + l32) * VP + h * 8;  // this lane's V row (first half)
+
+    Issue cx{};
+    if (total > 0) {
+        cx = issue_params(first);
+        issue_loads(cx, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+
+    auto run_step = [&](int it, Step& cur, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int bufi = it & 1;
+        const int q0 = cur.qb * BQ;
+        if (!MASKED && cur.qb + 1 < qu_end) {
+            const int sqb = BQ * (int)p.sq.n, sdb = BQ * (int)p.sdo.n;
+            cx.bq += sqb;
+            cx.bd += sdb;
+            cx.br += BQ;
+            cx.nq -= (uint32_t)sqb * 2u;
+            cx.nd -= (uint32_t)sdb * 2u;
+            cx.nr -= BQ * 4u;
+            cur.qb += 1;
+        } else {
+            cur = next_step(cur, it + 1);
+            cx = issue_params(cur);
+        }
+        issue_loads(cx, bufi ^ 1);
+
+        const e16* Qs = qtile(bufi);
+        const e16* dOs = dotile(bufi);
+        const float* Ls = lsetile(bufi);
+        const float* Ds = deltile(bufi);
+        // register r of a product tile holds local query row qoff(r) + 4h
+        auto qoff = [](int r) { return (r >> 2) * 8 + (r & 3); };
+        f32x16 s[2], dp[2];
+        {
+            f32x16 a;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(Ds + 8 * k + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * k + e] = v[e];
+            }
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+            dp[0] = a;  // the dP sums start from -D_i
+            dp[1] = a;
+        }
+        const int kq0 = kw0 + l32 - q0 - 4 * h;  // key - query offset, first half
+        e16x2 pp[2][2][4], dd[2][2][4];
+        e16x8 pb[2][2], dsb[2][2];
+        // P of register pair (2e, 2e+1) of rows-half u, both key halves;
+        // the probability overwrites the score.
+        auto p_pair = [&](int u, int e) {
+            const int r = u * 8 + 2 * e;
+            const float2 l2 = *reinterpret_cast<const float2*>(Ls + qoff(r) + 4 * h);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float pe[2];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    pe[w] = fast_exp2(fmaf(s[j][r + w], c, -(w ? l2.y : l2.x)));
+                    const int kq = kq0 + 32 * j;
+                    if (MASKED && CAUSAL && kq > qoff(r + w)) pe[w] = 0.0f;
+                    if (MASKED && WINDOW && qoff(r + w) > kq + W - 1) pe[w] = 0.0f;
+                    s[j][r + w] = pe[w];
+                }
+                pp[j][u][e] = cvt2<DT>(pe[0], pe[1]);
+                asm volatile("" : "+v"(pp[j][u][e]));
+            }
+        };
+        auto ds_pair = [&](int u, int e) {
+            const int r = u * 8 + 2 * e;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                dd[j][u][e] = cvt2<DT>(s[j][r] * dp[j][r], s[j][r + 1] * dp[j][r + 1]);
+                asm volatile("" : "+v"(dd[j][u][e]));
+            }
+        };
+        // region S: row reads of Q two products ahead
+        e16x8 rq[3];
+        e16x8 rdo[2], rv[2][2];
+        auto rd_q = [&](int ks) { rq[ks % 3] = lds_read8(Qs + qrd[ks & 1] + (ks >> 1) * 32); };
+        auto rd_dv = [&](int ks) {
+            rdo[ks & 1] = lds_read8(dOs + qrd[ks & 1] + (ks >> 1) * 32);
+            rv[ks & 1][0] = lds_read8(Vl + ks * 16);
+            rv[ks & 1][1] = lds_read8(Vl + 32 * VP + ks * 16);
+        };
+        rd_q(0);
+        rd_q(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS) rd_q(ks + 2);
+            if (ks == KS - 1) rd_dv(0);
+            s[0] = mfma32<DT>(rq[ks % 3], kf[0][ks], s[0]);
+            s[1] = mfma32<DT>(rq[ks % 3], kf[1][ks], s[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // region dP, with P of rows-half 0 (4 pairs x 2 halves)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) rd_dv(ks + 1);
+            dp[0] = mfma32<DT>(rdo[ks & 1], rv[ks & 1][0], dp[0]);
+            dp[1] = mfma32<DT>(rdo[ks & 1], rv[ks & 1][1], dp[1]);
+            if (ks >= 2 && ks < 6) p_pair(0, ks - 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) pb[j][0] = cat8(pp[j][0][0], pp[j][0][1], pp[j][0][2], pp[j][0][3]);
+        valu_mfma_gap();
+        // dV^T += dO^T P: transposed dO reads one product ahead
+        e16x8 od[2];
+        auto tr_d = [&](int u, int dt, int slot) {
+            const int ob = u * 16 * QP + dt * 32;
+            od[slot] = join8(lds_read_tr4(dOs + qtr0 + ob), lds_read_tr4(dOs + qtr1 + ob));
+        };
+        tr_d(0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {  // region V0, with P of rows-half 1
+            tr_d(dt + 1 < NDT ? 0 : 1, (dt + 1) % NDT, (dt + 1) & 1);
+            mfma32_agpr<DT>(dvacc[0][dt], od[dt & 1], pb[0][0]);
+            mfma32_agpr<DT>(dvacc[1][dt], od[dt & 1], pb[1][0]);
+            p_pair(1, dt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) pb[j][1] = cat8(pp[j][1][0], pp[j][1][1], pp[j][1][2], pp[j][1][3]);
+        valu_mfma_gap();
+        e16x8 oq[2];
+        auto tr_q = [&](int u, int dt, int slot) {
+            const int ob = u * 16 * QP + dt * 32;
+            oq[slot] = join8(lds_read_tr4(Qs + qtr0 + ob), lds_read_tr4(Qs + qtr1 + ob));
+        };
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {  // region V1, with dS of rows-half 0
+            if (dt + 1 < NDT) tr_d(1, dt + 1, (dt + 1) & 1);
+            else tr_q(0, 0, 0);
+            mfma32_agpr<DT>(dvacc[0][dt], od[dt & 1], pb[0][1]);
+            mfma32_agpr<DT>(dvacc[1][dt], od[dt & 1], pb[1][1]);
+            ds_pair(0, dt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dsb[j][0] = cat8(dd[j][0][0], dd[j][0][1], dd[j][0][2], dd[j][0][3]);
+        valu_mfma_gap();
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {  // region K0, with dS of rows-half 1
+            tr_q(dt + 1 < NDT ? 0 : 1, (dt + 1) % NDT, (dt + 1) & 1);
+            mfma32_agpr<DT>(dkacc[0][dt], oq[dt & 1], dsb[0][0]);
+            mfma32_agpr<DT>(dkacc[1][dt], oq[dt & 1], dsb[1][0]);
+            ds_pair(1, dt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dsb[j][1] = cat8(dd[j][1][0], dd[j][1][1], dd[j][1][2], dd[j][1][3]);
+        valu_mfma_gap();
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {  // region K1
+            if (dt + 1 < NDT) tr_q(1, dt + 1, (dt + 1) & 1);
+            mfma32_agpr<DT>(dkacc[0][dt], oq[dt & 1], dsb[0][1]);
+            mfma32_agpr<DT>(dkacc[1][dt], oq[dt & 1], dsb[1][1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed in LDS
+        __syncthreads();
+    };
+    int it = 0;
+    Step cur = first;
+    for (; it < nmG; ++it) run_step(it, cur, std::true_type{});
+    for (; it < total; ++it) run_step(it, cur, std::false_type{});
+
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            agpr_acc_ready(dkacc[j][dt]);
+            agpr_acc_ready(dvacc[j][dt]);
+        }
+    const float sc = p.scale;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int key = kw0 + 32 * j + l32;
+        if (key < N) {
+            e16* dkrow = static_cast<e16*>(p.dk) + b * p.sdk.b + hkv * p.sdk.h + key * p.sdk.n;
+            e16* dvrow = static_cast<e16*>(p.dv) + b * p.sdv.b + hkv * p.sdv.h + key * p.sdv.n;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = dt * 32 + g4 * 8 + h * 4;
+                    store4<DT>(dkrow + d, dkacc[j][dt][g4 * 4 + 0] * sc, dkacc[j][dt][g4 * 4 + 1] * sc,
+                               dkacc[j][dt][g4 * 4 + 2] * sc, dkacc[j][dt][g4 * 4 + 3] * sc);
+                    store4<DT>(dvrow + d, dvacc[j][dt][g4 * 4 + 0], dvacc[j][dt][g4 * 4 + 1],
+                               dvacc[j][dt][g4 * 4 + 2], dvacc[j][dt][g4 * 4 + 3]);
+                }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launch
+
+// The 64-keys-per-wave dK/dV kernel runs one workgroup per CU at a time; with
+// fewer than two rounds of its 256-key blocks the unequal causal blocks leave
+// CUs idle, and the 32-key kernel (twice the blocks) is used instead.
+constexpr long long kWideDkDvMinGroups = 512;
 
 template <int DT, int D, int MASK>
 static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stream) {
@@ -639,6 +1043,18 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
                            stream, p, rows);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (passes & kBwdDkDv) {
+        if constexpr (D == 128) {
+            const long long nkw = (p.N + 255) / 256;
+            if (p.drop.thr == 0 && nkw * p.B * p.Hkv >= kWideDkDvMinGroups) {
+                hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK>), dim3((unsigned)(nkw * p.B * p.Hkv)),
+                                   dim3(256), 0, stream, p);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                passes &= ~kBwdDkDv;
+            }
+        }
     }
     if (passes & kBwdDkDv) {
         const long long nkb = (p.N + 127) / 128;

@@ -120,3 +120,13 @@ def test_counter_summary_lists_every_counter(tmp_path):
     assert "--pmc SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT " in text
     rows = [x for x in text.splitlines() if x.startswith("void ")]
     assert rows == ["void attn::bwd_dkdv_kernel<0, 128, 1, false> | 20 | 0"]
+
+
+def test_traffic_summary_finds_the_wide_dkdv_kernel(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "traffic_file", lambda k, wl: str(tmp_path / f"traffic_{k}_{wl}.txt"))
+    cal = "void at::native::vectorized_elementwise_kernel<neg_kernel>"
+    dk = "void attn::bwd_dkdv_wide_kernel<0, 1>(attn::BwdParams)"
+    _write_counters(tmp_path / "f", [(cal, "FETCH_SIZE", 2048.0, 0, 1), (dk, "FETCH_SIZE", 500.0, 0, 1)])
+    _write_counters(tmp_path / "w", [(cal, "WRITE_SIZE", 4096.0, 0, 1), (dk, "WRITE_SIZE", 100.0, 0, 1)])
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path), "c5_bwd_d128", 4)
+    assert bench.read_traffic("bwd_dkdv_kernel", "c5_bwd_d128") == pytest.approx((500.0 * 2 + 100.0) * 1024.0)

@@ -1,0 +1,64 @@
+"""The 64-keys-per-wave dK/dV kernel (d = 128, no dropout), which the backward
+uses once there are at least 512 blocks of 256 keys (B * Hkv * ceil(N / 256)).
+The other GPU tests reach it only at the large workload shapes, through sampled
+rows; these shapes are just above that size, ragged (N not a multiple of 256
+or 32), so every element of dQ, dK and dV is checked against the fp64 oracle.
+Together they cover causal, window and no mask, GQA, both element types and
+both layouts."""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_12_amd as ea
+import oracle
+import synthetic_inputs as si
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+# B, Hq, Hkv, N, mask, dtype, layout; each has >= 512 blocks of 256 keys
+CASES = [
+    (2, 52, 52, 1285, "causal", "bf16", "bhsd"),   # 6 blocks x 104
+    (1, 256, 128, 1037, 300, "bf16", "bhsd"),      # window, G = 2: 5 x 128
+    (4, 32, 32, 1031, "none", "fp16", "bshd"),     # 5 x 128
+]
+
+
+def ids(c):
+    return "B{}_Hq{}_Hkv{}_N{}_{}_{}_{}".format(*c)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ea.lib()
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=ids)
+def test_wide_dkdv(cfg):
+    B, Hq, Hkv, N, mask, dt, layout = cfg
+    d = 128
+    assert B * Hkv * ((N + 255) // 256) >= 512
+    parity.log(f"wide dK/dV: {ids(cfg)}")
+    if mask == "none":
+        kw, causal, window = dict(causal=False), False, None
+    elif mask == "causal":
+        kw, causal, window = dict(causal=True), True, None
+    else:
+        kw, causal, window = dict(window=mask), True, mask
+    inp = si.make_inputs(B, Hq, Hkv, N, d, seed=9100 + N, with_do=True, dtype=dt)
+    g = {key: si.in_layout(t.cuda(), layout) for key, t in inp.items()}
+    scale = ea.default_scale(d)
+    o, lse = ea.fwd(g["q"], g["k"], g["v"], scale=scale, layout=layout, **kw)
+    grads = ea.bwd(g["q"], g["k"], g["v"], o, lse, g["do"], scale=scale, layout=layout, **kw)
+    torch.cuda.synchronize()
+    if layout == "bshd":
+        grads = tuple(t.transpose(1, 2) for t in grads)
+    q, k, v, do = (si.to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    dQ, dK, dV = oracle.ref_bwd(q, k, v, do, scale, causal, window=window)
+    for name, gg, r in (("dQ", grads[0], dQ), ("dK", grads[1], dK), ("dV", grads[2], dV)):
+        e = parity.rel_l2(si.to_f64(gg), r)
+        parity.log(f"  {name} rel L2 {e:.3e}")
+        assert e <= parity.GRAD_TOL
