@@ -644,7 +644,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 //   V0: dV products of rows 0..15, with P of rows 16..31;
 //   V1: dV products of rows 16..31, with dS of rows 0..15;
 //   K0, K1: dK products, with dS of rows 16..31 and the Q^T reads.
-template <int DT, int MASK>
+template <int DT, int MASK, bool DROP>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_wide_kernel(BwdParams p) {
     constexpr int D = 128;
@@ -880,8 +880,19 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
             }
             s[0] = f32x16{};
             s[1] = f32x16{};
-            dp[0] = a;  // the dP sums start from -D_i
-            dp[1] = a;
+            // the dP sums start from -D_i; dropout scales dP alone, so there
+            // they start from zero and D_i is subtracted in dS
+            dp[0] = DROP ? f32x16{} : a;
+            dp[1] = DROP ? f32x16{} : a;
+        }
+        // Dropout keep bits of each half's key for the step's 32 queries (bit
+        // r for register r), as in the 32-key kernel.
+        uint32_t keep[2] = {0u, 0u};
+        if constexpr (DROP) {
+            const uint32_t bh = (uint32_t)(b * p.Hq + hkv * p.G + cur.g);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                keep[j] = keep_bits_key_lane(p.drop, (uint32_t)(kw0 + 32 * j + l32), (uint32_t)(q0 + 4 * h) >> 2, bh);
         }
         const int kq0 = kw0 + l32 - q0 - 4 * h;  // key - query offset, first half
         e16x2 pp[2][2][4], dd[2][2][4];
@@ -901,6 +912,8 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
                     if (MASKED && CAUSAL && kq > qoff(r + w)) pe[w] = 0.0f;
                     if (MASKED && WINDOW && qoff(r + w) > kq + W - 1) pe[w] = 0.0f;
                     s[j][r + w] = pe[w];
+                    // dV takes P * M / (1-p)
+                    if constexpr (DROP) pe[w] = ((keep[j] >> (r + w)) & 1u) ? pe[w] * p.drop.scale : 0.0f;
                 }
                 pp[j][u][e] = cvt2<DT>(pe[0], pe[1]);
                 asm volatile("" : "+v"(pp[j][u][e]));
@@ -908,6 +921,16 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
         };
         auto ds_pair = [&](int u, int e) {
             const int r = u * 8 + 2 * e;
+            if constexpr (DROP) {
+                // dS = P ((dP M / (1-p)) - D_i)
+                const float2 nd = *reinterpret_cast<const float2*>(Ds + qoff(r) + 4 * h);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int w = 0; w < 2; ++w)
+                        dp[j][r + w] = (((keep[j] >> (r + w)) & 1u) ? dp[j][r + w] * p.drop.scale : 0.0f) +
+                                       (w ? nd.y : nd.x);
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 dd[j][u][e] = cvt2<DT>(s[j][r] * dp[j][r], s[j][r + 1] * dp[j][r + 1]);
@@ -1054,9 +1077,13 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
     if (passes & kBwdDkDv) {
         if constexpr (D == 128) {
             const long long nkw = (p.N + 255) / 256;
-            if (p.drop.thr == 0 && nkw * p.B * p.Hkv >= kWideDkDvMinGroups) {
-                hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK>), dim3((unsigned)(nkw * p.B * p.Hkv)),
-                                   dim3(256), 0, stream, p);
+            if (nkw * p.B * p.Hkv >= kWideDkDvMinGroups) {
+                if (p.drop.thr != 0)
+                    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, true>), dim3((unsigned)(nkw * p.B * p.Hkv)),
+                                       dim3(256), 0, stream, p);
+                else
+                    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, false>), dim3((unsigned)(nkw * p.B * p.Hkv)),
+                                       dim3(256), 0, stream, p);
                 const hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
                 passes &= ~kBwdDkDv;
