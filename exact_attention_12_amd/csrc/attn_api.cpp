@@ -188,9 +188,15 @@ size_t row_terms_bytes(int B, int Hq, int N) {
     return (bytes + 255) & ~(size_t)255;
 }
 
+// fp32 partial dK and dV of the head-split dK/dV kernel, when a shape uses it.
+size_t partial_bytes(int B, int Hq, int Hkv, int N, int d) {
+    if (attn::dkdv_wide_split(B, Hq, Hkv, N, d) != 2) return 0;
+    return 2 * 2 * (size_t)B * Hkv * N * d * sizeof(float);
+}
+
 size_t workspace_bytes_for(int B, int Hq, int Hkv, int N, int d) {
     if (check_shape(B, Hq, Hkv, N, d) != ATTN_OK) return 0;
-    return 2 * row_terms_bytes(B, Hq, N);
+    return 2 * row_terms_bytes(B, Hq, N) + partial_bytes(B, Hq, Hkv, N, d);
 }
 
 // Shared validation and dispatch of every backward entry point. Only the
@@ -253,6 +259,10 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.delta = static_cast<float*>(const_cast<void*>(workspace));
     p.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
                                       row_terms_bytes(pr->B, pr->Hq, pr->N));
+    p.hsplit = attn::dkdv_wide_split(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d) == 2 ? 2 : 1;
+    p.part = p.hsplit == 2 ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                                      2 * row_terms_bytes(pr->B, pr->Hq, pr->N))
+                           : nullptr;
     p.sq = strides_of(or_none(q, main));
     p.sk = strides_of(or_none(k, main));
     p.sv = strides_of(or_none(v, main));

@@ -644,7 +644,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 //   V0: dV products of rows 0..15, with P of rows 16..31;
 //   V1: dV products of rows 16..31, with dS of rows 0..15;
 //   K0, K1: dK products, with dS of rows 16..31 and the Q^T reads.
-template <int DT, int MASK, bool DROP>
+template <int DT, int MASK, bool DROP, int SPLIT>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_wide_kernel(BwdParams p) {
     constexpr int D = 128;
@@ -671,12 +671,19 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
     const int h = lane >> 5;
     const int N = p.N;
 
+    // Workgroup index: key block (ascending: heaviest first when causal),
+    // then the part of the group's query heads (hsplit parts), then the KV
+    // head, fastest.
     const int BHk = p.B * p.Hkv;
+    constexpr int S = SPLIT;  // = p.hsplit
     const int bid = blockIdx.x;
-    const int kb = bid / BHk;  // ascending key blocks: heaviest first when causal
-    const int bhk = bid - kb * BHk;
+    const int kb = bid / (BHk * S);
+    const int rem = bid - kb * BHk * S;
+    const int part_i = rem / BHk;
+    const int bhk = rem - part_i * BHk;
     const int b = bhk / p.Hkv;
     const int hkv = bhk - b * p.Hkv;
+    const int Gs = p.G / S;  // query heads of this workgroup
     const int k0 = kb * BK;
     const int kw0 = k0 + wave * 64;
 
@@ -720,7 +727,7 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
     const int W = WINDOW ? p.window : 0;
     const int qb_stop = WINDOW ? min(nqb, (k0 + BK - 1 + W - 1) / BQ + 1) : nqb;
     const int nq_iter = qb_stop - qb_start;
-    const int total = p.G * nq_iter;
+    const int total = Gs * nq_iter;
     // Unmasked query blocks [qu_begin, qu_end), as in the 32-key kernel.
     int qu_begin = qb_start, qu_end = qb_stop;
     if (CAUSAL) qu_begin = min(qb_stop, max(qb_start, (k0 + BK - 1 + BQ - 1) / BQ));
@@ -729,14 +736,14 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
         qu_end = max(qu_begin, min(qb_stop, t >= 0 ? t / BQ + 1 : 0));
     }
     const int nu = qu_end - qu_begin;
-    const int nmG = p.G * (nq_iter - nu);
+    const int nmG = Gs * (nq_iter - nu);
     struct Step {
         int g, qb;
         const e16* qh;
         const e16* dh;
         size_t rt;
     };
-    const int hq0 = hkv * p.G;
+    const int hq0 = hkv * p.G + part_i * Gs;
     const Step head0{0, 0, static_cast<const e16*>(p.q) + b * p.sq.b + hq0 * p.sq.h,
                      static_cast<const e16*>(p.dout) + b * p.sdo.b + hq0 * p.sdo.h,
                      ((size_t)b * p.Hq + hq0) * N};
@@ -889,7 +896,7 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
         // r for register r), as in the 32-key kernel.
         uint32_t keep[2] = {0u, 0u};
         if constexpr (DROP) {
-            const uint32_t bh = (uint32_t)(b * p.Hq + hkv * p.G + cur.g);
+            const uint32_t bh = (uint32_t)(b * p.Hq + hq0 + cur.g);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 keep[j] = keep_bits_key_lane(p.drop, (uint32_t)(kw0 + 32 * j + l32), (uint32_t)(q0 + 4 * h) >> 2, bh);
@@ -1038,6 +1045,30 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
             agpr_acc_ready(dvacc[j][dt]);
         }
     const float sc = p.scale;
+    if constexpr (S > 1) {
+        // fp32 partial sums [2][S][B][Hkv][N][D]: dK (scaled), then dV
+        const size_t plane = (size_t)S * BHk * N * D;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int key = kw0 + 32 * j + l32;
+            if (key < N) {
+                float* pk = p.part + (((size_t)part_i * BHk + bhk) * N + key) * D;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int d = dt * 32 + g4 * 8 + h * 4;
+                        *reinterpret_cast<f32x4*>(pk + d) =
+                            f32x4{dkacc[j][dt][g4 * 4 + 0] * sc, dkacc[j][dt][g4 * 4 + 1] * sc,
+                                  dkacc[j][dt][g4 * 4 + 2] * sc, dkacc[j][dt][g4 * 4 + 3] * sc};
+                        *reinterpret_cast<f32x4*>(pk + plane + d) =
+                            f32x4{dvacc[j][dt][g4 * 4 + 0], dvacc[j][dt][g4 * 4 + 1], dvacc[j][dt][g4 * 4 + 2],
+                                  dvacc[j][dt][g4 * 4 + 3]};
+                    }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int key = kw0 + 32 * j + l32;
@@ -1058,12 +1089,33 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
     }
 }
 
-// ---------------------------------------------------------------- launch
+// Sum of the two partial dK, dV of the head-split dK/dV kernel (in part
+// order, so the result is deterministic), converted to the element type.
+// One thread per 4 elements of a row.
+template <int DT>
+__global__ __launch_bounds__(256)
+void bwd_dkdv_sum_kernel(BwdParams p, long long quads) {
+    constexpr int D = 128;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= quads) return;
+    const long long row = i / (D / 4);
+    const int d = (int)(i - row * (D / 4)) * 4;
+    const long long rows = (long long)p.B * p.Hkv * p.N;  // rows of one part
+    const int n = (int)(row % p.N);
+    const long long bh = row / p.N;
+    const int b = (int)(bh / p.Hkv), hkv = (int)(bh - (long long)b * p.Hkv);
+    const float* pk = p.part + row * D + d;
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(pk);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(pk + rows * D);
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(pk + 2 * rows * D);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(pk + 3 * rows * D);
+    e16* dkrow = static_cast<e16*>(p.dk) + b * p.sdk.b + hkv * p.sdk.h + n * p.sdk.n;
+    e16* dvrow = static_cast<e16*>(p.dv) + b * p.sdv.b + hkv * p.sdv.h + n * p.sdv.n;
+    store4<DT>(dkrow + d, k0[0] + k1[0], k0[1] + k1[1], k0[2] + k1[2], k0[3] + k1[3]);
+    store4<DT>(dvrow + d, v0[0] + v1[0], v0[1] + v1[1], v0[2] + v1[2], v0[3] + v1[3]);
+}
 
-// The 64-keys-per-wave dK/dV kernel runs one workgroup per CU at a time; with
-// fewer than two rounds of its 256-key blocks the unequal causal blocks leave
-// CUs idle, and the 32-key kernel (twice the blocks) is used instead.
-constexpr long long kWideDkDvMinGroups = 512;
+// ---------------------------------------------------------------- launch
 
 template <int DT, int D, int MASK>
 static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stream) {
@@ -1076,16 +1128,29 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
     }
     if (passes & kBwdDkDv) {
         if constexpr (D == 128) {
-            const long long nkw = (p.N + 255) / 256;
-            if (nkw * p.B * p.Hkv >= kWideDkDvMinGroups) {
-                if (p.drop.thr != 0)
-                    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, true>), dim3((unsigned)(nkw * p.B * p.Hkv)),
-                                       dim3(256), 0, stream, p);
-                else
-                    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, false>), dim3((unsigned)(nkw * p.B * p.Hkv)),
-                                       dim3(256), 0, stream, p);
-                const hipError_t e = hipGetLastError();
+            const int split = dkdv_wide_split(p.B, p.Hq, p.Hkv, p.N, D);
+            if (split > 0) {
+                const dim3 grid((unsigned)((p.N + 255) / 256 * p.B * p.Hkv * p.hsplit));
+                if (p.hsplit == 2) {
+                    if (p.drop.thr != 0)
+                        hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, true, 2>), grid, dim3(256), 0, stream, p);
+                    else
+                        hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, false, 2>), grid, dim3(256), 0, stream, p);
+                } else {
+                    if (p.drop.thr != 0)
+                        hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, true, 1>), grid, dim3(256), 0, stream, p);
+                    else
+                        hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DT, MASK, false, 1>), grid, dim3(256), 0, stream, p);
+                }
+                hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
+                if (p.hsplit == 2) {
+                    const long long quads = (long long)p.B * p.Hkv * p.N * (D / 4);
+                    hipLaunchKernelGGL((bwd_dkdv_sum_kernel<DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256),
+                                       0, stream, p, quads);
+                    e = hipGetLastError();
+                    if (e != hipSuccess) return e;
+                }
                 passes &= ~kBwdDkDv;
             }
         }

@@ -131,6 +131,8 @@ struct BwdParams {
     void* dv;
     float* delta;  // [B, Hq, N] workspace: -D_i = -<dO_i, O_i>
     float* lse2;   // [B, Hq, N] workspace: LSE_i * log2(e), written with D_i
+    float* part;   // [2, hsplit, B, Hkv, N, 128] workspace: partial dK, dV (hsplit 2 only)
+    int hsplit;    // workgroups per 256-key block of the 64-key dK/dV kernel (1 or 2)
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     int N;
     int Hq;
@@ -142,6 +144,20 @@ struct BwdParams {
     float c;       // scale * log2(e)
     DropParams drop;
 };
+
+// dK/dV kernel for a shape: 0 = 32 keys per wave; 1 = 64 keys per wave (d =
+// 128, at least 512 blocks of 256 keys: two rounds of one workgroup per CU);
+// 2 = 64 keys per wave with the query heads of each group split over two
+// workgroups, which write fp32 partial sums that a second kernel adds (256 to
+// 511 blocks and an even group size: one round would leave the CUs with the
+// light causal blocks idle).
+inline int dkdv_wide_split(int B, int Hq, int Hkv, int N, int d) {
+    if (d != 128 || Hkv <= 0) return 0;
+    const long long n4 = (long long)((N + 255) / 256) * B * Hkv;
+    if (n4 >= 512) return 1;
+    if ((Hq / Hkv) % 2 == 0 && 2 * n4 >= 512) return 2;
+    return 0;
+}
 
 struct FwdPlan {
     int rows_per_wave;  // query rows per wave (32)

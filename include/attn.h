@@ -118,7 +118,11 @@ attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o
 /*
  * Bytes of device workspace attn_bwd needs: two float32 per query row, the
  * row term D_i = <dO_i, O_i> (stored negated) and the LSE in base 2, each
- * array rounded up to 256 bytes. Returns 0 if the shape is invalid.
+ * array rounded up to 256 bytes. For d = 128 when B * Hkv * ceil(N / 256) is
+ * between 256 and 511 and Hq / Hkv is even, the dK/dV pass splits the query
+ * heads of each group over two workgroups and also keeps their float32
+ * partial dK and dV: 2 * 2 * B * Hkv * N * 128 * 4 more bytes. Returns 0 if
+ * the shape is invalid.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

@@ -112,6 +112,11 @@ def test_workspace_bytes(L):
     assert L.attn_bwd_workspace_bytes(1, 16, 16, 16384, 128) == 2 * 16 * 16384 * 4
     assert L.attn_bwd_workspace_bytes(1, 1, 1, 1, 64) == 512
     assert L.attn_bwd_workspace_bytes(2, 3, 1, 100, 80) == 2 * 2560  # 2400 rounded up to 256, twice
+    # d = 128 with 256 .. 511 blocks of 256 keys and an even group size: the
+    # dK/dV pass also keeps fp32 partial dK and dV of two head halves
+    assert L.attn_bwd_workspace_bytes(1, 64, 8, 8192, 128) == 2 * 64 * 8192 * 4 + 2 * 2 * 8 * 8192 * 128 * 4
+    assert L.attn_bwd_workspace_bytes(1, 64, 8, 8192, 64) == 2 * 64 * 8192 * 4
+    assert L.attn_bwd_workspace_bytes(1, 8, 8, 8192, 128) == 2 * 8 * 8192 * 4  # G = 1: no split
     assert L.attn_bwd_workspace_bytes(1, 3, 2, 100, 80) == 0
     assert L.attn_bwd_workspace_bytes(1, 2, 2, 100, 112) == 0
 

@@ -1,5 +1,7 @@
 """The 64-keys-per-wave dK/dV kernel (d = 128), which the backward
-uses once there are at least 512 blocks of 256 keys (B * Hkv * ceil(N / 256)).
+uses once there are at least 512 blocks of 256 keys (B * Hkv * ceil(N / 256)),
+or at least 256 of them with an even group size, splitting each group's
+query heads over two workgroups.
 The other GPU tests reach it only at the large workload shapes, through sampled
 rows; these shapes are just above that size, ragged (N not a multiple of 256
 or 32), so every element of dQ, dK and dV is checked against the fp64 oracle.
@@ -24,6 +26,10 @@ CASES = [
     (4, 32, 32, 1031, "none", "fp16", "bshd", 0.0),     # 5 x 128
     (1, 104, 104, 1285, "causal", "bf16", "bhsd", 0.2),  # 6 x 104
     (1, 128, 128, 1030, 300, "fp16", "bshd", 0.1),      # 5 x 128
+    # 256 .. 511 blocks, G even: the query heads of a group split over two
+    # workgroups, partial sums added by a second kernel
+    (1, 256, 128, 520, "causal", "bf16", "bhsd", 0.0),  # 3 x 128
+    (1, 128, 64, 1030, 300, "fp16", "bshd", 0.1),       # 5 x 64, window, dropout
 ]
 
 
@@ -42,7 +48,8 @@ def _gpu():
 def test_wide_dkdv(cfg):
     B, Hq, Hkv, N, mask, dt, layout, p = cfg
     d = 128
-    assert B * Hkv * ((N + 255) // 256) >= 512
+    n4 = B * Hkv * ((N + 255) // 256)
+    assert n4 >= 512 or (2 * n4 >= 512 and (Hq // Hkv) % 2 == 0)
     parity.log(f"wide dK/dV: {ids(cfg)}")
     if mask == "none":
         kw, causal, window = dict(causal=False), False, None
