@@ -35,13 +35,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 attn_status check_shape(int B, int Hq, int Hkv, int N, int d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return ATTN_ERR_SHAPE;
     if (N > ATTN_MAX_SEQ_LEN) return ATTN_ERR_SHAPE;
-    // Element counts must fit comfortably in 64-bit offsets, and the
-    // workgroup counts of every kernel in a 32-bit grid dimension.
+    // Element counts must fit comfortably in 64-bit offsets. A HIP grid
+    // holds fewer than 2^32 work-items per dimension; the forward, dQ and
+    // dK/dV kernels launch at most two work-items per query (or key) row,
+    // rows padded to 256, and the row-term pass loops over its rows, so
+    // B * Hq * round_up(N, 256) < 2^31 keeps every launch inside the limit.
     const long double elems = (long double)B * Hq * N * 256.0L;
     if (elems > 4.0e18L) return ATTN_ERR_SHAPE;
-    const long long rows = (long long)B * Hq * ((N + 127) / 128);
-    if (rows > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    if ((long long)B * Hq * N / 16 + 1 > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    const long double padded_rows = (long double)B * Hq * (long double)(((long long)N + 255) / 256 * 256);
+    if (padded_rows >= 2147483648.0L) return ATTN_ERR_SHAPE;
     if (Hq % Hkv != 0) return ATTN_ERR_GQA;
     if (!head_dim_ok(d)) return ATTN_ERR_HEAD_DIM;
     return ATTN_OK;
@@ -135,7 +137,7 @@ attn_status check_layout(const attn_tensor* const* ts, int n, int rows = 0, int 
 }
 
 attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_tensor* k,
-                     const attn_tensor* v, const attn_tensor* o, float* lse, void* stream) {
+                     const attn_tensor* v, const attn_tensor* o, float* lse, hipStream_t stream) {
     if (!pr) return ATTN_ERR_NULL;
     const attn_tensor* ts[] = {q, k, v, o};
     attn_status st = check_null(ts, 4);
@@ -178,7 +180,7 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.c = pr->scale * kLog2eHost;
     p.drop = drop;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_fwd(p, pr->dtype, pr->d, mask, plan, static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_fwd(p, pr->dtype, pr->d, mask, plan, stream));
 }
 
 // Two float32 per query row, each array 256-byte aligned: D_i, then
@@ -206,7 +208,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
                      const attn_tensor* v, const attn_tensor* o, const float* lse,
                      const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
                      const attn_tensor* dv, const void* workspace, size_t workspace_bytes,
-                     unsigned passes, void* stream) {
+                     unsigned passes, hipStream_t stream) {
     if (!pr) return ATTN_ERR_NULL;
     if (passes == 0 || (passes & ~(unsigned)attn::kBwdAll)) return ATTN_ERR_PASSES;
     const bool pre = passes & attn::kBwdPre, kv = passes & attn::kBwdDkDv, qq = passes & attn::kBwdDq;
@@ -282,7 +284,7 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.drop = drop;
     g_last_hip_error[0] = '\0';
     return hip_status(attn::launch_bwd(p, pr->dtype, pr->d, mask, (int)passes,
-                                       static_cast<hipStream_t>(stream)));
+                                       stream));
 }
 
 attn_problem plain_problem(int B, int Hq, int Hkv, int N, int d, float scale, int causal,
@@ -309,7 +311,7 @@ attn_status bwd_plain(const void* q, const void* k, const void* v, const void* o
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       const void* workspace, size_t workspace_bytes,
                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
-                      void* stream, unsigned passes) {
+                      hipStream_t stream, unsigned passes) {
     if (window < 0 || (window > 0 && causal == 0)) {
         if (passes & (attn::kBwdDkDv | attn::kBwdDq)) return ATTN_ERR_WINDOW;
         window = 0;
@@ -366,7 +368,7 @@ size_t attn_decode_workspace_bytes(const attn_decode_problem* problem) {
 attn_status attn_decode_fwd(const attn_decode_problem* problem, const attn_tensor* q,
                             const attn_tensor* k_cache, const attn_tensor* v_cache,
                             const int* kv_lens, const attn_tensor* o, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!problem) return ATTN_ERR_NULL;
     const attn_tensor* ts[] = {q, k_cache, v_cache, o};
     attn_status st = check_null(ts, 4);
@@ -415,12 +417,12 @@ attn_status attn_decode_fwd(const attn_decode_problem* problem, const attn_tenso
     p.window = window;
     p.c = pr.scale * kLog2eHost;
     g_last_hip_error[0] = '\0';
-    return hip_status(attn::launch_decode(p, pr.dtype, pr.d, mask, static_cast<hipStream_t>(stream)));
+    return hip_status(attn::launch_decode(p, pr.dtype, pr.d, mask, stream));
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream) {
+                     hipStream_t stream) {
     const attn_problem pr = plain_problem(B, Hq, Hkv, N, d, scale, causal, 0);
     const attn_tensor tq = bhsd(q, Hq, N, d), tk = bhsd(k, Hkv, N, d), tv = bhsd(v, Hkv, N, d),
                       to = bhsd(o, Hq, N, d);
@@ -429,7 +431,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int N, int d, float scale, int window,
-                            void* stream) {
+                            hipStream_t stream) {
     if (window < 1) return ATTN_ERR_WINDOW;
     const attn_problem pr = plain_problem(B, Hq, Hkv, N, d, scale, 1, window);
     const attn_tensor tq = bhsd(q, Hq, N, d), tk = bhsd(k, Hkv, N, d), tv = bhsd(v, Hkv, N, d),
@@ -438,7 +440,7 @@ attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o
 }
 
 attn_status attn_fwd_ex(const attn_problem* problem, const attn_tensor* q, const attn_tensor* k,
-                        const attn_tensor* v, const attn_tensor* o, float* lse, void* stream) {
+                        const attn_tensor* v, const attn_tensor* o, float* lse, hipStream_t stream) {
     return fwd_impl(problem, q, k, v, o, lse, stream);
 }
 
@@ -451,7 +453,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream) {
+                     hipStream_t stream) {
     return bwd_plain(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
                      scale, causal, 0, stream, attn::kBwdAll);
 }
@@ -461,7 +463,7 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
                             void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes,
                             int B, int Hq, int Hkv, int N, int d, float scale, int window,
-                            void* stream) {
+                            hipStream_t stream) {
     if (window < 1) return ATTN_ERR_WINDOW;
     return bwd_plain(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
                      scale, 1, window, stream, attn::kBwdAll);
@@ -469,7 +471,7 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
 
 attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
-                                void* stream) {
+                                hipStream_t stream) {
     return bwd_plain(nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr, nullptr, workspace,
                      workspace_bytes, B, Hq, Hkv, N, d, 1.0f, 0, 0, stream, attn::kBwdPre);
 }
@@ -478,7 +480,7 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const flo
                           const void* dout, void* dk, void* dv,
                           const void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                          int window, void* stream) {
+                          int window, hipStream_t stream) {
     return bwd_plain(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes, B, Hq,
                      Hkv, N, d, scale, causal, window, stream, attn::kBwdDkDv);
 }
@@ -487,7 +489,7 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float
                         const void* dout, void* dq,
                         const void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                        int window, void* stream) {
+                        int window, hipStream_t stream) {
     return bwd_plain(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes, B,
                      Hq, Hkv, N, d, scale, causal, window, stream, attn::kBwdDq);
 }
@@ -496,7 +498,7 @@ attn_status attn_bwd_ex(const attn_problem* problem, const attn_tensor* q, const
                         const attn_tensor* v, const attn_tensor* o, const float* lse,
                         const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
                         const attn_tensor* dv, void* workspace, size_t workspace_bytes,
-                        unsigned passes, void* stream) {
+                        unsigned passes, hipStream_t stream) {
     return bwd_impl(problem, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, passes,
                     stream);
 }

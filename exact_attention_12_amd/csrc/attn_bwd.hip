@@ -37,35 +37,41 @@ namespace attn {
 // ---------------------------------------------------------------- D_i
 
 // One 16-lane group per query row; rows are numbered (b * Hq + h) * N + n,
-// the layout of the D_i workspace.
+// the layout of the D_i workspace. The grid is capped (kPreMaxBlocks) and
+// each group steps through the rows by the grid's row count, so a launch
+// stays far below the 2^32 work-items of a grid dimension at any size.
+constexpr long long kPreMaxBlocks = 1 << 20;
+
 template <int DT, int D>
 __global__ __launch_bounds__(256)
 void bwd_pre_kernel(BwdParams p, long long rows) {
     constexpr int CPR = D / 8;
-    const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int j = threadIdx.x & 15;
-    float acc = 0.0f;
-    if (row < rows) {
+    // All 16 lanes of a group share their row, so the loop exit and the
+    // shuffles (inside the group) see the group whole.
+    for (long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4); row < rows;
+         row += (long long)gridDim.x * 16) {
         const long long bh = row / p.N;
         const int n = (int)(row - bh * p.N);
         const int b = (int)(bh / p.Hq);
         const int hq = (int)(bh - (long long)b * p.Hq);
         const e16* op = static_cast<const e16*>(p.o) + b * p.so.b + hq * p.so.h + n * p.so.n;
         const e16* dp = static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h + n * p.sdo.n;
+        float acc = 0.0f;
         for (int c = j; c < CPR; c += 16) {
             const e16x8 a = *reinterpret_cast<const e16x8*>(op + c * 8);
             const e16x8 g = *reinterpret_cast<const e16x8*>(dp + c * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = fmaf(widen<DT>(a[e]), widen<DT>(g[e]), acc);
         }
-    }
-    acc += __shfl_xor(acc, 8);
-    acc += __shfl_xor(acc, 4);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 1);
-    if (row < rows && j == 0) {
-        p.delta[row] = -acc;  // -D_i: the dK/dV pass starts its dP sums from it
-        p.lse2[row] = p.lse[row] * kLog2e;  // the dK/dV pass's log2-domain LSE
+        acc += __shfl_xor(acc, 8);
+        acc += __shfl_xor(acc, 4);
+        acc += __shfl_xor(acc, 2);
+        acc += __shfl_xor(acc, 1);
+        if (j == 0) {
+            p.delta[row] = -acc;  // -D_i: the dK/dV pass starts its dP sums from it
+            p.lse2[row] = p.lse[row] * kLog2e;  // the dK/dV pass's log2-domain LSE
+        }
     }
 }
 
@@ -1121,8 +1127,8 @@ template <int DT, int D, int MASK>
 static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stream) {
     if (passes & kBwdPre) {
         const long long rows = (long long)p.B * p.Hq * p.N;
-        hipLaunchKernelGGL((bwd_pre_kernel<DT, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                           stream, p, rows);
+        const long long blocks = (rows + 15) / 16 < kPreMaxBlocks ? (rows + 15) / 16 : kPreMaxBlocks;
+        hipLaunchKernelGGL((bwd_pre_kernel<DT, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p, rows);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -63,6 +63,8 @@
 
 #include <stddef.h>
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -70,7 +72,9 @@ extern "C" {
 typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,       /* a required pointer is NULL */
-    ATTN_ERR_SHAPE = 2,      /* B, Hq, Hkv or N < 1, or a size overflows */
+    ATTN_ERR_SHAPE = 2,      /* B, Hq, Hkv or N < 1, N > ATTN_MAX_SEQ_LEN, or
+                                B * Hq * round_up(N, 256) >= 2^31 rows (a kernel grid
+                                would pass 2^32 work-items) */
     ATTN_ERR_GQA = 3,        /* Hq is not a multiple of Hkv */
     ATTN_ERR_HEAD_DIM = 4,   /* d is not one of 32, 64, 80, 96, 128, 192, 256 */
     ATTN_ERR_SCALE = 5,      /* scale is not finite or not > 0 */
@@ -104,7 +108,7 @@ typedef enum attn_status {
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream);
+                     hipStream_t stream);
 
 /*
  * Forward pass under the sliding-window mask of W = window keys (query i
@@ -113,7 +117,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  */
 attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int N, int d, float scale, int window,
-                            void* stream);
+                            hipStream_t stream);
 
 /*
  * Bytes of device workspace attn_bwd needs: two float32 per query row, the
@@ -142,7 +146,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream);
+                     hipStream_t stream);
 
 /*
  * Backward pass of attn_fwd_window: the gradients of the banded attention,
@@ -154,7 +158,7 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
                             void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes,
                             int B, int Hq, int Hkv, int N, int d, float scale, int window,
-                            void* stream);
+                            hipStream_t stream);
 
 /*
  * The three passes attn_bwd runs, in order, for callers that schedule them
@@ -172,17 +176,17 @@ attn_status attn_bwd_window(const void* q, const void* k, const void* v, const v
  */
 attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                                 size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
-                                void* stream);
+                                hipStream_t stream);
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dk, void* dv,
                           const void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                          int window, void* stream);
+                          int window, hipStream_t stream);
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                         const void* dout, void* dq,
                         const void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                        int window, void* stream);
+                        int window, hipStream_t stream);
 
 /*
  * Strided, typed interface. The entry points above are the special case
@@ -247,7 +251,7 @@ typedef struct attn_problem {
  * [B, Hq, N] float32. Returns ATTN_OK or an error code with nothing enqueued.
  */
 attn_status attn_fwd_ex(const attn_problem* problem, const attn_tensor* q, const attn_tensor* k,
-                        const attn_tensor* v, const attn_tensor* o, float* lse, void* stream);
+                        const attn_tensor* v, const attn_tensor* o, float* lse, hipStream_t stream);
 
 /*
  * Backward pass of `problem`: the passes selected by the bits of `passes`
@@ -264,7 +268,7 @@ attn_status attn_bwd_ex(const attn_problem* problem, const attn_tensor* q, const
                         const attn_tensor* v, const attn_tensor* o, const float* lse,
                         const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
                         const attn_tensor* dv, void* workspace, size_t workspace_bytes,
-                        unsigned passes, void* stream);
+                        unsigned passes, hipStream_t stream);
 
 /*
  * Decoding: Nq new queries per sequence against a key/value cache.
@@ -304,7 +308,7 @@ size_t attn_decode_workspace_bytes(const attn_decode_problem* problem);
 attn_status attn_decode_fwd(const attn_decode_problem* problem, const attn_tensor* q,
                             const attn_tensor* k_cache, const attn_tensor* v_cache,
                             const int* kv_lens, const attn_tensor* o, float* lse,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);

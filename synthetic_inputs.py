@@ -168,6 +168,31 @@ def make_inputs(B, Hq, Hkv, N, d, seed, with_do=False, dtype="bf16"):
     return out
 
 
+def make_rising_inputs(B, Hq, Hkv, N, d, seed, growth=64.0, v_scale=0.25, with_do=False,
+                       dtype="bf16"):
+    """Inputs whose key norms grow along the sequence: drawn as make_inputs
+    does (float32 normals in the order Q, K, V, dO), then key row j is
+    multiplied by 1 + j / growth before the rounding to 16 bits. The spread
+    of the scores then widens with the key index, so a row's later key blocks
+    reach far larger maxima than its first ones: the recipe that makes a
+    running maximum move again and again along a row. V is multiplied by
+    v_scale (a power of two, so exactly): with scores this spread a row's
+    weights sit on a few keys and O is close to single V rows."""
+    t = TORCH_DTYPES[dtype]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    ramp = 1.0 + torch.arange(N, dtype=torch.float32) / float(growth)
+    k = k * ramp[None, None, :, None]
+    v = v * float(v_scale)
+    out = {"q": q.to(t), "k": k.to(t), "v": v.to(t)}
+    if with_do:
+        out["do"] = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32).to(t)
+    return out
+
+
 def workload_inputs(w: Workload):
     """Q, K, V (and dO) of a workload; for decoding, K and V are the cache
     [B, Hkv, N, d] and Q the Nq new queries, drawn after them."""

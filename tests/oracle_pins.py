@@ -531,6 +531,43 @@ def check_philox_against_numpy(philox):
             assert [int(x) for x in want] == [int(x) for x in got[4 * blk:4 * blk + 4]]
 
 
+def check_philox_weyl_constants(constants):
+    """The Weyl constants by which Philox advances its key are the golden
+    ratio and sqrt(3), less one, as binary fractions of the word size
+    (Salmon et al., SC'11, section 3.3): W0 = floor(2^W (phi - 1)) and
+    W1 = floor(2^W (sqrt(3) - 1)). Integer square roots make both exact; the
+    32-bit constants are the top halves of the 64-bit ones (which the numpy
+    pin covers)."""
+    for w in (32, 64):
+        one = 1 << w
+        phi_m1 = (math.isqrt(5 << (2 * w)) - one) // 2   # floor(2^w (sqrt(5) - 1) / 2)
+        sqrt3_m1 = math.isqrt(3 << (2 * w)) - one         # floor(2^w (sqrt(3) - 1))
+        assert constants[w]["W0"] == phi_m1, w
+        assert constants[w]["W1"] == sqrt3_m1, w
+    assert constants[32]["W0"] == constants[64]["W0"] >> 32
+    assert constants[32]["W1"] == constants[64]["W1"] >> 32
+
+
+def check_philox32_against_rocrand(philox4x32, run_rocrand):
+    """Philox-4x32-10 equals rocRAND's philox4x32_10_engine (an independent
+    library implementation) on random 128-bit counters and 64-bit keys:
+    this pins the two 32-bit multipliers, which have no closed form.
+    `run_rocrand` maps lines "seed counter_lo64 counter_hi64" to the four
+    words of each block."""
+    r = np.random.default_rng(9)
+    cases = [(0, 0, 0), (2**64 - 1, 2**62 - 1, 2**64 - 1)]
+    for _ in range(40):
+        seed = int(r.integers(0, 2**63, dtype=np.uint64)) * 2 + int(r.integers(0, 2))
+        lo = int(r.integers(0, 2**62, dtype=np.uint64))
+        hi = int(r.integers(0, 2**63, dtype=np.uint64)) * 2 + int(r.integers(0, 2))
+        cases.append((seed, lo, hi))
+    got = run_rocrand(cases)
+    for (seed, lo, hi), words in zip(cases, got):
+        m = 0xFFFFFFFF
+        want = philox4x32((lo & m, lo >> 32, hi & m, hi >> 32), (seed & m, seed >> 32), rounds=10)
+        assert [int(x) for x in want] == words, (seed, lo, hi)
+
+
 def check_philox32_stream(philox, philox4x32):
     """The vectorised 32-bit path equals the generic one, and its words look
     uniform: mean, per-bit frequencies and lag-1 correlation within 5 sigma."""

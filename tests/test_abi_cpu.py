@@ -61,9 +61,19 @@ def test_fwd_null_pointer(L, which):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0), dict(Hkv=0), dict(N=0), dict(N=-5),
-                                dict(N=(1 << 24) + 1), dict(B=1 << 30, Hq=1 << 30)])
+                                dict(N=(1 << 24) + 1), dict(B=1 << 30, Hq=1 << 30),
+                                dict(Hq=1 << 15, Hkv=1, N=1 << 16),
+                                dict(B=2, Hq=1 << 14, Hkv=1, N=(1 << 16) - 100)])
 def test_fwd_bad_shape(L, kw):
     assert fwd(L, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(Hq=1 << 15, Hkv=1, N=1 << 16),
+                                dict(B=1 << 10, Hq=1 << 5, Hkv=1, N=(1 << 16) - 255)])
+def test_bwd_rows_past_the_grid_limit(L, kw):
+    # B * Hq * round_up(N, 256) >= 2^31 rows: two work-items per row would
+    # pass the 2^32 work-items of one grid dimension
+    assert bwd(L, **kw) == 2
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(3, 2), (8, 3), (1, 2)])

@@ -108,6 +108,10 @@ PHILOX_MUTANTS = {
     "both_keys_same_half": ("(16 * (j % 2))", "(16 * (j % 1))"),
     "row_word_from_key": ("np.choose((i % 4) * np.ones_like(j), words)", "np.choose((j % 4) * np.ones_like(i), words)"),
     "threshold_32_bit": ("np.float64(p) * 65536.0)), 65535)", "np.float64(p) * 4294967296.0)), 4294967295)"),
+    "multiplier_bit_flip": ("32: dict(M0=0xD2511F53,", "32: dict(M0=0xD2511F57,"),
+    "weyl_constant_off_by_one": ("W0=0x9E3779B9, W1=0xBB67AE85", "W0=0x9E3779B9, W1=0xBB67AE86"),
+    "hi_lo_swapped": ("c = [(p1 >> s32) ^ c[1] ^ k0, p1 & m32, (p0 >> s32) ^ c[3] ^ k1, p0 & m32]",
+                      "c = [(p1 & m32) ^ c[1] ^ k0, p1 >> s32, (p0 >> s32) ^ c[3] ^ k1, p0 & m32]"),
 }
 
 
@@ -121,6 +125,19 @@ def load_philox_mutant(old, new):
 
 def run_stream_pins(mod):
     pins.check_keep_mask(mod.dropout_keep, mod.keep_threshold)
+    pins.check_philox_weyl_constants(mod.CONSTANTS)
+    pins.check_philox32_against_rocrand(mod.philox4x32, _rocrand_cases)
+
+
+_ROCRAND_CACHE = {}
+
+
+def _rocrand_cases(cases):
+    key = tuple(cases)
+    if key not in _ROCRAND_CACHE:
+        from tests.test_oracle_pins import _run_rocrand
+        _ROCRAND_CACHE[key] = _run_rocrand(cases)
+    return _ROCRAND_CACHE[key]
 
 
 def test_unmutated_philox_passes():

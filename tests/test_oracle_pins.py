@@ -1,6 +1,8 @@
 """The fp64 oracle against brute force, hand-worked cases, closed forms,
 invariants and finite differences (CPU only)."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -183,6 +185,32 @@ def bwd_d(q, k, v, do, scale, causal, drop):
 
 def test_philox_matches_numpy_philox4x64():
     pins.check_philox_against_numpy(ph.philox)
+
+
+def test_philox_weyl_constants():
+    pins.check_philox_weyl_constants(ph.CONSTANTS)
+
+
+def _run_rocrand(cases):
+    """Builds tests/rocrand_philox.cpp (rocRAND's Philox engine, host code)
+    and runs it on the cases."""
+    import shutil
+    import subprocess
+    import tempfile
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"):
+        pytest.skip("no ROCm toolchain with rocRAND headers")
+    src = os.path.join(os.path.dirname(__file__), "rocrand_philox.cpp")
+    with tempfile.TemporaryDirectory() as tmp:
+        exe = os.path.join(tmp, "rocrand_philox")
+        subprocess.run([hipcc, "-O1", src, "-o", exe], check=True, capture_output=True)
+        inp = "".join(f"{a} {b} {c}\n" for a, b, c in cases)
+        out = subprocess.run([exe], input=inp, check=True, capture_output=True, text=True).stdout
+    return [[int(w, 16) for w in line.split()] for line in out.splitlines()]
+
+
+def test_philox32_matches_rocrand():
+    pins.check_philox32_against_rocrand(ph.philox4x32, _run_rocrand)
 
 
 def test_philox32_stream():
