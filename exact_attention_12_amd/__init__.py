@@ -47,6 +47,7 @@ STATUS = {
     11: "ATTN_ERR_DTYPE",
     12: "ATTN_ERR_PASSES",
     13: "ATTN_ERR_DROPOUT",
+    14: "ATTN_ERR_SCRATCH",
 }
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW = 0, 1, 2
@@ -134,6 +135,9 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     L.attn_bwd_ex.argtypes = [pp, tp, tp, tp, tp, vp, tp, tp, tp, tp, vp, sz, u, vp]
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_noalloc_max_rows.argtypes = []
+    L.attn_bwd_noalloc_max_rows.restype = sz
     L.attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, vp]
     L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
@@ -142,7 +146,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_fwd.argtypes = [dp, tp, tp, tp, vp, tp, vp, vp, sz, vp]
     for name in ("attn_decode_fwd", "attn_fwd", "attn_fwd_window", "attn_fwd_ex", "attn_bwd", "attn_bwd_window",
-                 "attn_bwd_ex", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"):
+                 "attn_bwd_ex", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
+                 "attn_bwd_noalloc"):
         getattr(L, name).restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
@@ -338,6 +343,33 @@ def bwd(q, k, v, o, lse, do, *, scale=None, causal=False, window=None, layout="b
     return bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, scale=scale, causal=causal,
                       window=window, layout=layout, passes=("pre", "dkdv", "dq"), use_ex=use_ex,
                       fused=True, dropout_p=dropout_p, seed=seed, offset=offset)
+
+
+def bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, *, scale=None, causal=False):
+    """attn_bwd_noalloc: the backward with the library's fixed scratch in
+    place of a workspace (contiguous bf16 BHSD tensors; dq, dk, dv are the
+    caller's outputs, written in place). Nothing is allocated on the device,
+    by torch or by the library."""
+    import torch
+    qv, kv_, vv = (_as_bhsd(t, n, "bhsd") for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    B, Hq, Hkv, N, d = _shapes(qv, kv_, vv)
+    for name, t, ref in (("o", o, qv), ("do", do, qv), ("dq", dq, qv), ("dk", dk, kv_), ("dv", dv, vv)):
+        _same(_as_bhsd(t, name, "bhsd"), name, ref)
+    _rows(lse, "lse", B, Hq, N, q.device)
+    ts = (qv, kv_, vv, o, do, dq, dk, dv)
+    if qv.dtype != torch.bfloat16 or not _plain(ts):
+        raise ValueError("bwd_noalloc takes contiguous bfloat16 [B, H, N, d] tensors")
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().attn_bwd_noalloc(qv.data_ptr(), kv_.data_ptr(), vv.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                                  _stream_ptr(q.device)))
+    return dq, dk, dv
+
+
+def bwd_noalloc_max_rows() -> int:
+    return int(lib().attn_bwd_noalloc_max_rows())
 
 
 def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal=False,

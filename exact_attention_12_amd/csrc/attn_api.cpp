@@ -5,12 +5,23 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "attn_kernels.h"
+
+// Device scratch of the backward entry point that allocates nothing
+// (attn_bwd_noalloc): its row terms live in this fixed array, which every GPU
+// the library runs on holds from the module's load until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -183,6 +194,30 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     return hip_status(attn::launch_fwd(p, pr->dtype, pr->d, mask, plan, stream));
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+attn_status scratch_of_current_device(const void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_status(e);
+            if (!ptr || !aligned16(ptr)) return hip_status(hipErrorInvalidSymbol);
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return ATTN_OK;
+}
+
 // Two float32 per query row, each array 256-byte aligned: D_i, then
 // LSE_i * log2(e).
 size_t row_terms_bytes(int B, int Hq, int N) {
@@ -204,11 +239,13 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int N, int d) {
 // Shared validation and dispatch of every backward entry point. Only the
 // tensors the selected passes read or write are checked; the others may be
 // NULL and are never dereferenced.
+// no_alloc: the workspace arguments are ignored and the row terms go to the
+// library's fixed scratch array instead (see attn_bwd_noalloc).
 attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_tensor* k,
                      const attn_tensor* v, const attn_tensor* o, const float* lse,
                      const attn_tensor* dout, const attn_tensor* dq, const attn_tensor* dk,
                      const attn_tensor* dv, const void* workspace, size_t workspace_bytes,
-                     unsigned passes, hipStream_t stream) {
+                     unsigned passes, hipStream_t stream, bool no_alloc = false) {
     if (!pr) return ATTN_ERR_NULL;
     if (passes == 0 || (passes & ~(unsigned)attn::kBwdAll)) return ATTN_ERR_PASSES;
     const bool pre = passes & attn::kBwdPre, kv = passes & attn::kBwdDkDv, qq = passes & attn::kBwdDq;
@@ -238,11 +275,18 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
         st = make_drop(*pr, &drop);
         if (st != ATTN_OK) return st;
     }
-    if (!workspace || workspace_bytes < workspace_bytes_for(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d))
+    if (no_alloc) {
+        if (2 * row_terms_bytes(pr->B, pr->Hq, pr->N) > kScratchBytes) return ATTN_ERR_SCRATCH;
+    } else if (!workspace || workspace_bytes < workspace_bytes_for(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d)) {
         return ATTN_ERR_WORKSPACE;
+    }
     st = check_layout(ts, n, pr->N, pr->d);
     if (st != ATTN_OK) return st;
-    if (!aligned16(lse) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
+    if (!aligned16(lse) || (!no_alloc && !aligned16(workspace))) return ATTN_ERR_ALIGN;
+    if (no_alloc) {
+        st = scratch_of_current_device(&workspace);
+        if (st != ATTN_OK) return st;
+    }
 
     const attn_tensor none = {nullptr, 0, 0, 0};
     auto or_none = [&](const attn_tensor* t, bool used) -> const attn_tensor& {
@@ -261,7 +305,12 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.delta = static_cast<float*>(const_cast<void*>(workspace));
     p.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
                                       row_terms_bytes(pr->B, pr->Hq, pr->N));
-    p.hsplit = attn::dkdv_wide_split(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d) == 2 ? 2 : 1;
+    // The head-split dK/dV kernel needs fp32 partials in the workspace; the
+    // fixed scratch has no room for them, so there the 32-key kernel (the
+    // faster of the two others on such grids) takes its place.
+    p.dkdv = attn::dkdv_wide_split(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d);
+    if (no_alloc && p.dkdv == 2) p.dkdv = 0;
+    p.hsplit = p.dkdv == 2 ? 2 : 1;
     p.part = p.hsplit == 2 ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
                                                       2 * row_terms_bytes(pr->B, pr->Hq, pr->N))
                            : nullptr;
@@ -458,6 +507,20 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      scale, causal, 0, stream, attn::kBwdAll);
 }
 
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                             hipStream_t stream) {
+    const attn_problem pr = plain_problem(B, Hq, Hkv, N, d, scale, causal, 0);
+    const attn_tensor tq = bhsd(q, Hq, N, d), tk = bhsd(k, Hkv, N, d), tv = bhsd(v, Hkv, N, d),
+                      to = bhsd(o, Hq, N, d), tdo = bhsd(dout, Hq, N, d), tdq = bhsd(dq, Hq, N, d),
+                      tdk = bhsd(dk, Hkv, N, d), tdv = bhsd(dv, Hkv, N, d);
+    return bwd_impl(&pr, &tq, &tk, &tv, &to, lse, &tdo, &tdq, &tdk, &tdv, nullptr, 0, attn::kBwdAll,
+                    stream, true);
+}
+
+size_t attn_bwd_noalloc_max_rows(void) { return kScratchBytes / (2 * sizeof(float)); }
+
 attn_status attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
                             const float* lse, const void* dout,
                             void* dq, void* dk, void* dv,
@@ -522,6 +585,9 @@ const char* attn_status_string(attn_status status) {
         case ATTN_ERR_DTYPE: return "unknown element type (supported: bf16, fp16)";
         case ATTN_ERR_PASSES: return "passes must be a nonzero subset of ATTN_BWD_ALL";
         case ATTN_ERR_DROPOUT: return "dropout_p must be in [0, 1)";
+        case ATTN_ERR_SCRATCH:
+            return "the problem needs more scratch than the fixed buffer of attn_bwd_noalloc holds "
+                   "(more than attn_bwd_noalloc_max_rows() query rows)";
     }
     return "unknown status";
 }

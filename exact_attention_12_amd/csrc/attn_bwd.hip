@@ -1134,8 +1134,7 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
     }
     if (passes & kBwdDkDv) {
         if constexpr (D == 128) {
-            const int split = dkdv_wide_split(p.B, p.Hq, p.Hkv, p.N, D);
-            if (split > 0) {
+            if (p.dkdv > 0) {
                 const dim3 grid((unsigned)((p.N + 255) / 256 * p.B * p.Hkv * p.hsplit));
                 if (p.hsplit == 2) {
                     if (p.drop.thr != 0)

@@ -132,7 +132,8 @@ struct BwdParams {
     float* delta;  // [B, Hq, N] workspace: -D_i = -<dO_i, O_i>
     float* lse2;   // [B, Hq, N] workspace: LSE_i * log2(e), written with D_i
     float* part;   // [2, hsplit, B, Hkv, N, 128] workspace: partial dK, dV (hsplit 2 only)
-    int hsplit;    // workgroups per 256-key block of the 64-key dK/dV kernel (1 or 2)
+    int dkdv;      // dK/dV kernel (dkdv_wide_split's numbering; 1 and 2 only at d = 128)
+    int hsplit;    // workgroups per 256-key block of the 64-key dK/dV kernel (2 iff dkdv == 2)
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     int N;
     int Hq;

@@ -89,7 +89,9 @@ typedef enum attn_status {
                                 byte offsets) */
     ATTN_ERR_DTYPE = 11,     /* unknown element type */
     ATTN_ERR_PASSES = 12,    /* passes is 0 or has bits other than ATTN_BWD_ALL */
-    ATTN_ERR_DROPOUT = 13    /* dropout_p is not in [0, 1) */
+    ATTN_ERR_DROPOUT = 13,   /* dropout_p is not in [0, 1) */
+    ATTN_ERR_SCRATCH = 14    /* attn_bwd_noalloc: B * Hq * N exceeds
+                                attn_bwd_noalloc_max_rows() */
 } attn_status;
 
 /* Head dimensions with a specialised kernel: 32, 64, 80, 96, 128, 192, 256. */
@@ -147,6 +149,34 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                      hipStream_t stream);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc). Arguments, layouts, results and errors are those
+ * of attn_bwd; the row terms attn_bwd keeps in the caller's workspace go to
+ * a scratch array of fixed size inside the library instead (16 MiB: at most
+ * attn_bwd_noalloc_max_rows() = 2^21 query rows B * Hq * N, else
+ * ATTN_ERR_SCRATCH with nothing enqueued). Each GPU the library runs on
+ * holds its own copy of that array from the library's load until the
+ * process ends. The call allocates and frees nothing. Its first call on a
+ * device looks up that device's copy (hipGetSymbolAddress), with the device
+ * current on the calling thread, which must be the stream's device. The
+ * kernels write every scratch entry before reading it, so nothing carries
+ * over from a previous call. Calls that overlap on one GPU (concurrent
+ * streams, or threads) share the one array and race: serialise them.
+ * Shapes for which attn_bwd sums two fp32 halves of dK/dV in its workspace
+ * use a single-pass dK/dV kernel here, so dK and dV may differ from
+ * attn_bwd's in the last bits; everything else is bitwise identical.
+ */
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv,
+                             int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                             hipStream_t stream);
+
+/* Largest B * Hq * N that attn_bwd_noalloc accepts. */
+size_t attn_bwd_noalloc_max_rows(void);
 
 /*
  * Backward pass of attn_fwd_window: the gradients of the banded attention,

@@ -46,7 +46,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for code in range(14):
+    for code in range(15):
         s = ea.status_string(code)
         assert s and s != "unknown status"
     assert ea.status_string(99) == "unknown status"
@@ -353,3 +353,27 @@ def test_decode_workspace_formula(L):
     rows = 32 * 8 * 8
     want = -(-(rows * S * 128 * 4) // 256) * 256 + -(-(rows * S * 4) // 256) * 256
     assert L.attn_decode_workspace_bytes(ctypes.byref(pr)) == want
+
+
+def noalloc(L, ptrs=None, B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125, causal=1):
+    p = ptrs or [P] * 9
+    return L.attn_bwd_noalloc(*p, B, Hq, Hkv, N, d, scale, causal, None)
+
+
+def test_noalloc_validates_like_bwd(L):
+    assert L.attn_bwd_noalloc_max_rows() == 1 << 21
+    for which in range(9):
+        ptrs = [P] * 9
+        ptrs[which] = None
+        assert noalloc(L, ptrs) == 1
+    assert noalloc(L, N=0) == 2
+    assert noalloc(L, Hq=3, Hkv=2) == 3
+    assert noalloc(L, d=72) == 4
+    assert noalloc(L, scale=0.0) == 5
+    assert noalloc(L, ptrs=[P + 8] + [P] * 8) == 6
+
+
+@pytest.mark.parametrize("B,Hq,N", [(1, 32, 65537), (4, 8, 65536 + 256), (1, 1, (1 << 21) + 1)])
+def test_noalloc_rejects_problems_past_its_scratch(L, B, Hq, N):
+    # more than 2^21 query rows: the fixed 16 MiB scratch cannot hold their row terms
+    assert noalloc(L, B=B, Hq=Hq, Hkv=1, N=N) == 14
