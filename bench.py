@@ -345,6 +345,24 @@ def summarize_waves(pmc_dir, out, workload):
     print(out)
 
 
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def cpu_model():
+    """The host CPU's model name (Linux), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def time_loop(fn, steps, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -449,6 +467,8 @@ def cpu_baseline(w, inputs, budget_s):
         "value": round(value, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
+        "host_usable_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"{heads} of {w.B * w.Hq} heads of the same workload "
                    f"({'Nq=' + str(w.Nq) + ' against a cache of ' if w.Nq else ''}N={w.N}, d={w.d}, "
@@ -519,14 +539,32 @@ def summarize_trace(trace_dir, bench_json, out_md, workload):
             short = short[:60]
         out.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    out += ["", "HIP-event timings of the same build (bench run):", "",
-            "| kernel | avg ms | credited TFLOP/s | % of 2.5 PFLOP/s |", "|---|---|---|---|"]
+    out += ["", f"HIP-event timings of the same build (bench run, {b['steps']} timed steps):", "",
+            "| kernel | avg ms | median ms | min ms | credited TFLOP/s | % of 2.5 PFLOP/s | GB/s (algorithmic bytes) |",
+            "|---|---|---|---|---|---|---|"]
     for name, v in b["kernels"].items():
-        out.append(f"| {name} | {v['ms']} | {v['tflops']} | {v['pct_of_bf16_peak']} |")
-    out += ["", f"Step: {b['ms_per_step']} ms = {b['value']} TFLOP/s algorithmic "
+        gbs = f"{v['bytes'] / v['ms'] / 1e6:.0f}" if v.get("bytes") else "-"
+        out.append(f"| {name} | {v['ms']} | {v.get('ms_median', '-')} | {v.get('ms_min', '-')} | "
+                   f"{v['tflops']} | {v['pct_of_bf16_peak']} | {gbs} |")
+    out += ["", f"Step: {b['ms_per_step']} ms mean (median {b.get('ms_per_step_median', '-')}, min "
+                f"{b.get('ms_per_step_min', '-')}) = {b['value']} TFLOP/s algorithmic "
                 f"({b['pct_of_bf16_peak']}% of the bf16 peak); roofline kernel "
                 f"{b['roofline']['kernel']} at {b['roofline']['achieved']} {b['roofline']['unit']} "
                 f"(frac {b['roofline']['frac']})."]
+    if b.get("cold_cache"):
+        c = b["cold_cache"]
+        out += ["", f"Cold caches ({c['scratch_mib']} MiB scratch overwritten before each call, each "
+                    f"call bracketed by its own events): forward {c['fwd_ms']} ms."]
+    if b.get("unfused_baseline"):
+        u = b["unfused_baseline"]
+        out += ["", f"Unfused torch eager baseline (S = Q K^T * scale, softmax, P V; S and P "
+                    f"materialised, {u['s_and_p_bytes'] / 2**20:.0f} MiB): {u['ms']} ms = {u['tflops']} "
+                    f"TFLOP/s; the fused forward is {u['fused_speedup']}x faster; outputs differ by at "
+                    f"most {u['o_max_abs_diff_vs_fused']}."]
+    if b.get("cpu_baseline"):
+        c = b["cpu_baseline"]
+        out += ["", f"CPU oracle: {c['value']} TFLOP/s on {c['cores']} threads ({c.get('cpu_model', '?')}); "
+                    f"sample: {c['sample']}."]
     with open(out_md, "w") as f:
         f.write("\n".join(out) + "\n")
     print(out_md)
@@ -627,6 +665,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev[0][0].elapsed_time(ev[-1][-1]) / args.steps
+    step_ms = sorted(s_ev[0].elapsed_time(s_ev[-1]) for s_ev in ev)
     print(f"[bench] {args.steps} steps of {w.name}: {ms_step:.3f} ms/step (wall {wall:.2f} s)",
           file=sys.stderr, flush=True)
 
@@ -639,9 +678,11 @@ def main():
             "bwd_dq_kernel": (credit["bwd_dq"], None)}
     kernels = {}
     for i, name in enumerate(names):
-        ms = sum(s_ev[i].elapsed_time(s_ev[i + 1]) for s_ev in ev) / args.steps
+        per_step = sorted(s_ev[i].elapsed_time(s_ev[i + 1]) for s_ev in ev)
+        ms = sum(per_step) / args.steps
         flops, nbytes = work[name]
-        kernels[name] = {"ms": ms, "flops": flops}
+        kernels[name] = {"ms": ms, "flops": flops, "ms_median": round(median(per_step), 4),
+                         "ms_min": round(per_step[0], 4)}
         if nbytes is not None:
             kernels[name]["bytes"] = nbytes
     for k in kernels.values():
@@ -715,6 +756,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(median(step_ms), 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
