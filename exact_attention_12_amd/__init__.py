@@ -70,6 +70,7 @@ class AttnPlan(ctypes.Structure):
         ("threads", ctypes.c_int),
         ("workgroups", ctypes.c_longlong),
         ("lds_bytes", ctypes.c_int),
+        ("key_splits", ctypes.c_int),
     ]
 
 

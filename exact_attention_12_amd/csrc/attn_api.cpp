@@ -170,7 +170,7 @@ attn_status fwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     if (!aligned16(lse)) return ATTN_ERR_ALIGN;
 
     attn::FwdPlan plan;
-    attn::fwd_plan(pr->B, pr->Hq, pr->N, pr->d, mask != attn::kMaskNone, &plan);
+    attn::fwd_plan(pr->B, pr->Hq, pr->N, pr->d, mask != attn::kMaskNone, drop.thr != 0, &plan);
     attn::FwdParams p;
     p.q = q->data;
     p.k = k->data;
@@ -599,13 +599,14 @@ attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn
     const attn_status st = check_shape(B, Hq, Hkv, N, d);
     if (st != ATTN_OK) return st;
     attn::FwdPlan fp;
-    attn::fwd_plan(B, Hq, N, d, causal != 0, &fp);
+    attn::fwd_plan(B, Hq, N, d, causal != 0, false, &fp);
     plan->rows_per_wave = fp.rows_per_wave;
     plan->block_q = fp.block_q;
     plan->block_kv = fp.block_kv;
     plan->threads = fp.threads;
     plan->workgroups = fp.workgroups;
     plan->lds_bytes = fp.lds_bytes;
+    plan->key_splits = fp.key_splits;
     return ATTN_OK;
 }
 

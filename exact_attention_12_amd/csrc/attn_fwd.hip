@@ -431,6 +431,240 @@ void fwd_kernel(FwdParams p) {
     }
 }
 
+// Short sequences (at most kSplitMaxKeys keys, small grids): the keys of one
+// 32-row query tile are split over the workgroup's waves, one 64-key tile
+// each. Every wave issues all of its loads at once (its K tile straight into
+// MFMA operand registers, its V tile into its own LDS region), computes its
+// tile's probabilities against its own row maximum m_w with sum l_w and
+// unnormalised output O_w, and the waves then combine through LDS with the
+// same identity the online softmax applies block by block (CANN
+// ops-transformer FlashAttention page, section on online softmax):
+//   M = max_w m_w,  L = sum_w 2^(m_w - M) l_w,  O = sum_w 2^(m_w - M) O_w / L,
+// all in the log2 domain. A workgroup thus waits on memory once instead of
+// once per key step, and the grid has a workgroup per 32 rows: the regime
+// where the step loop above is bound by latency rather than throughput.
+template <int D> struct SplitTile {
+    static constexpr int NDT = (D + 31) / 32;
+    static constexpr int VBYTES = 64 * v_pitch(D) * 2;       // one wave's V tile
+    static constexpr int OP = 40;                             // floats per partial-O row
+    static constexpr int OBYTES = NDT * 32 * OP * 4;          // one wave's O_w^T
+    static constexpr int AREA = VBYTES > OBYTES ? VBYTES : OBYTES;
+    static constexpr int lds_bytes(int nw) { return nw * AREA + nw * 32 * 8; }
+};
+
+template <int DT, int D, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64, 1)
+void fwd_split_kernel(FwdParams p) {
+    constexpr int T = NW * 64;
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
+    constexpr int BC = 64;
+    constexpr int KS = D / 16;
+    constexpr int NKT = BC / 32;
+    constexpr int PVS = BC / 16;
+    constexpr int NDT = SplitTile<D>::NDT;
+    constexpr int VP = v_pitch(D);
+    constexpr int CPR = D / 8;
+    constexpr int CKV = VP / 8;
+    constexpr int NLV = BC * CKV / 64;
+    constexpr int OP = SplitTile<D>::OP;
+    constexpr int AREA = SplitTile<D>::AREA;
+    static_assert(BC * CKV % 64 == 0, "V tile must be whole loads");
+    static_assert(4 * OP % 64 == 32, "the two lane halves of a partial-O store hit disjoint banks");
+
+    __shared__ __attribute__((aligned(16))) char smem[SplitTile<D>::lds_bytes(NW)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int N = p.N;
+
+    const int bid = blockIdx.x;
+    const int bh = xcd_head(bid % p.BH, p.BH);
+    const int q0 = (bid / p.BH) * 32;
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hkv = hq / p.G;
+    const int qrow = q0 + l32;
+    const int W = WINDOW ? p.window : 0;
+
+    const e16* Qh = static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h;
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
+    const long long sqn = p.sq.n, skn = p.sk.n, svn = p.sv.n;
+
+    // This wave's keys kv0 .. kv0 + 63; it has work if any of them is
+    // allowed for some row of the tile.
+    const int kv0 = wave * BC;
+    const bool active = kv0 < N && (!CAUSAL || kv0 <= q0 + 31) && (!WINDOW || kv0 + BC - 1 >= q0 - W + 1);
+
+    e16x8 qf[KS];
+    e16x8 kf[NKT][KS];
+    char* vlds = smem + wave * AREA;
+    if (active) {
+        // Q operand (B of S^T = K Q^T): query qrow, dims 16*ks + 8*h .. +7.
+        if (qrow < N) {
+            const e16* qp = Qh + qrow * sqn + h * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const e16x8*>(qp + ks * 16);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[ks] = e16x8{};
+        }
+        // K operand (A): key kv0 + 32*kt + l32, dims 16*ks + 8*h .. +7; keys
+        // at or past N read as zeros (buffer range).
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 x = buf_load16(rk, (uint32_t)(kt * 32 + l32) * sk2 + (uint32_t)(h * 8 + ks * 16) * 2u);
+                kf[kt][ks] = __builtin_bit_cast(e16x8, x);
+            }
+        // V tile into this wave's LDS region (row-major, pitch VP): load i
+        // fills chunks 64i .. 64i + 63; padding chunks and rows past N are
+        // given offsets outside the buffer and arrive as zeros.
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
+#pragma unroll
+        for (int i = 0; i < NLV; ++i) {
+            const int chunk = i * 64 + lane;
+            const int row = chunk / CKV, ch = chunk - row * CKV;
+            const uint32_t off = ch < CPR ? (uint32_t)row * sv2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+            buf_load16_to_lds(rv, vlds + i * 1024, off);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's K operands and V tile have landed
+
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+    float m = -__builtin_huge_valf();  // row maximum of c*s over this wave's keys
+    float l = 0.0f;                    // this lane's half of the row sum
+    const float c = p.c;
+    if (active) {
+        f32x16 s[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            s[kt] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s[kt] = mfma32<DT>(kf[kt][ks], qf[ks], s[kt]);
+        }
+        // keys outside [lo, hi] (relative to kv0 + 4h): past N, after the
+        // row (causal), before its band (window)
+        const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0) || (kv0 + BC > N) || (WINDOW && kv0 < q0 + 32 - W);
+        if (need_mask) {
+            const int hi = (CAUSAL ? min(qrow, N - 1) : N - 1) - kv0 - 4 * h;
+            const int lo = (WINDOW ? qrow - W + 1 : 0) - kv0 - 4 * h;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int koff = kt * 32 + (r >> 2) * 8 + (r & 3);
+                    s[kt][r] = (koff > hi || koff < lo) ? -__builtin_huge_valf() : s[kt][r];
+                }
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+        m = max_across_halves(mx) * c;
+        const float mref = (m == -__builtin_huge_valf()) ? 0.0f : m;
+        const int g16 = lane >> 4, j16 = lane & 15;
+        const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
+        const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
+        const e16* Vs = reinterpret_cast<const e16*>(vlds);
+#pragma unroll
+        for (int u = 0; u < PVS; ++u) {
+            const int kt = u >> 1;
+            e16x2 pr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = (u & 1) * 8 + 2 * e;
+                const float a0 = fast_exp2(fmaf(s[kt][r], c, -mref));
+                const float a1 = fast_exp2(fmaf(s[kt][r + 1], c, -mref));
+                l += a0 + a1;
+                pr[e] = cvt2<DT>(a0, a1);
+            }
+            const e16x8 pb = cat8(pr[0], pr[1], pr[2], pr[3]);
+            const e16* vp = Vs + (u * 16 + tr_row) * VP + tr_col;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                oacc[dt] = mfma32<DT>(join8(lds_read_tr4(vp + dt * 32), lds_read_tr4(vp + 8 * VP + dt * 32)),
+                                      pb, oacc[dt]);
+        }
+        l = sum_across_halves(l);
+    }
+
+    // Partial results to LDS: O_w^T as [dim][query] rows of OP floats (the
+    // V tiles are dead once every wave is past this barrier), m_w and l_w per
+    // query.
+    __syncthreads();
+    float* ow = reinterpret_cast<float*>(smem + wave * AREA);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ow[(dt * 32 + (r >> 2) * 8 + 4 * h + (r & 3)) * OP + l32] = oacc[dt][r];
+    float* mw = reinterpret_cast<float*>(smem + NW * AREA);
+    float* lw = mw + NW * 32;
+    if (h == 0) {
+        mw[wave * 32 + l32] = m;
+        lw[wave * 32 + l32] = l;
+    }
+    __syncthreads();
+
+    // Combine: thread (query q, dim group g) produces dims g*DPT .. +DPT-1.
+    constexpr int GROUPS = T / 32;
+    constexpr int DPT = (D + GROUPS - 1) / GROUPS;
+    const int q = tid & 31, g = tid >> 5;
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w * 32 + q]);
+    float a[NW];
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float mv = mw[w * 32 + q];
+        a[w] = mv == -__builtin_huge_valf() ? 0.0f : fast_exp2(mv - M);
+        L += a[w] * lw[w * 32 + q];
+    }
+    const int row = q0 + q;
+    if (row < N) {
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        e16* orow = static_cast<e16*>(p.o) + b * p.so.b + hq * p.so.h + row * p.so.n;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            const int dim = g * DPT + j;
+            if (dim < D) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w)
+                    acc = fmaf(a[w], reinterpret_cast<const float*>(smem + w * AREA)[dim * OP + q], acc);
+                orow[dim] = cvt2<DT>(acc * inv, 0.0f)[0];
+            }
+        }
+        if (g == 0) p.lse[(size_t)bh * N + row] = L > 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_huge_valf();
+    }
+}
+
+template <int DT, int D, int MASK>
+static hipError_t launch_fwd_split(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
+    const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
+    if constexpr (D <= kSplitMaxD) {
+        switch (plan.key_splits) {
+            case 2: hipLaunchKernelGGL((fwd_split_kernel<DT, D, MASK, 2>), grid, block, 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((fwd_split_kernel<DT, D, MASK, 4>), grid, block, 0, stream, p); break;
+            case 8: hipLaunchKernelGGL((fwd_split_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int DT, int D, int MASK, bool DROP>
 static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
     const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
@@ -446,6 +680,10 @@ static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStr
 
 template <int DT, int D, int MASK>
 static hipError_t launch_fwd_dm(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
+    if (plan.key_splits > 1) {
+        if (p.drop.thr != 0) return hipErrorInvalidValue;  // the plan never pairs them
+        return launch_fwd_split<DT, D, MASK>(p, plan, stream);
+    }
     return p.drop.thr != 0 ? launch_fwd_dmd<DT, D, MASK, true>(p, plan, stream)
                            : launch_fwd_dmd<DT, D, MASK, false>(p, plan, stream);
 }
@@ -477,8 +715,25 @@ static hipError_t launch_fwd_t(const FwdParams& p, int d, int mask, const FwdPla
 // gives every CU a workgroup. Shorter sequences use 4 waves (twice the
 // workgroups); d > 128 always uses 4.
 template <int D>
-static void plan_d(int B, int Hq, int N, bool causal, FwdPlan* plan) {
+static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* plan) {
     const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
+    const long long wg128 = (long long)((N + 127) / 128) * B * Hq;
+    plan->key_splits = 1;
+    // Short sequences whose grid of 128-row workgroups would leave CUs idle:
+    // the key-split kernel (one workgroup per 32 rows, waves over the keys).
+    if (D <= kSplitMaxD && !dropout && N <= kSplitMaxKeys && wg128 < kSplitMaxGrid) {
+        const int nkb = (N + 63) / 64;
+        const int nw = nkb <= 2 ? 2 : nkb <= 4 ? 4 : 8;
+        plan->rows_per_wave = 32;
+        plan->waves = nw;
+        plan->key_splits = nw;
+        plan->block_q = 32;
+        plan->block_kv = 64;
+        plan->threads = nw * 64;
+        plan->workgroups = (long long)((N + 31) / 32) * B * Hq;
+        plan->lds_bytes = SplitTile<D <= kSplitMaxD ? D : 32>::lds_bytes(nw);
+        return;
+    }
     const int waves = (D <= 128 && wg256 >= (causal ? 512 : 256)) ? 8 : 4;
     const int BQ = waves * 32;
     const int BC = FwdTile<D>::BLOCK_KV;
@@ -491,10 +746,10 @@ static void plan_d(int B, int Hq, int N, bool causal, FwdPlan* plan) {
     plan->lds_bytes = 2 * BC * (k_pitch(D) + v_pitch(D)) * 2;
 }
 
-bool fwd_plan(int B, int Hq, int N, int d, bool causal, FwdPlan* plan) {
+bool fwd_plan(int B, int Hq, int N, int d, bool causal, bool dropout, FwdPlan* plan) {
     switch (d) {
 #define ATTN_PLAN_CASE(D_) \
-        case D_: plan_d<D_>(B, Hq, N, causal, plan); return true;
+        case D_: plan_d<D_>(B, Hq, N, causal, dropout, plan); return true;
         ATTN_FOR_EACH_HEAD_DIM(ATTN_PLAN_CASE)
 #undef ATTN_PLAN_CASE
         default: return false;

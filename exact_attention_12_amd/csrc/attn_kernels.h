@@ -168,9 +168,17 @@ struct FwdPlan {
     int threads;
     long long workgroups;
     int lds_bytes;
+    int key_splits;     // > 1: the key-split kernel, its waves each take 64 keys of one 32-row tile
 };
 
-bool fwd_plan(int B, int Hq, int N, int d, bool causal, FwdPlan* plan);
+// Key-split forward for short sequences: head dims up to kSplitMaxD, at most
+// kSplitMaxKeys keys (one 64-key tile per wave, 8 waves), used when the
+// 128-row grid would have fewer than kSplitMaxGrid workgroups.
+constexpr int kSplitMaxD = 96;
+constexpr int kSplitMaxKeys = 512;
+constexpr long long kSplitMaxGrid = 256;
+
+bool fwd_plan(int B, int Hq, int N, int d, bool causal, bool dropout, FwdPlan* plan);
 // Query block of rank t (0 = first dispatched) among nqb blocks of a head.
 // Under a causal mask late blocks carry the most work. When a CU holds two
 // workgroups at once and the whole grid is resident (`paired`), the second

@@ -364,6 +364,9 @@ typedef struct attn_plan {
     int threads;
     long long workgroups;
     int lds_bytes;
+    int key_splits;  /* > 1: short-sequence plan, each 32-row query tile's keys
+                        split over this many waves of one workgroup (64 keys
+                        each) and combined in LDS; 1: the step-loop kernel */
 } attn_plan;
 
 attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn_plan* plan);

@@ -132,10 +132,18 @@ def test_workspace_bytes(L):
 
 
 def test_fwd_plan(L):
+    # the 20x20-map shape: its 32 workgroups of 128 rows would idle most CUs,
+    # so each 32-row query tile gets a workgroup whose 8 waves split the keys
     p = ea.fwd_plan(1, 8, 8, 400, 64)
-    assert p["block_q"] == 128 and p["threads"] == 256
-    assert p["workgroups"] == math.ceil(400 / 128) * 8
+    assert p["block_q"] == 32 and p["key_splits"] == 8 and p["threads"] == 512
+    assert p["workgroups"] == math.ceil(400 / 32) * 8
     assert p["lds_bytes"] <= 160 * 1024
+    # past 512 keys, 128 or more workgroups of 128 rows, or d = 128: the step loop
+    for shape in [(1, 8, 8, 513, 64), (4, 16, 16, 512, 64), (1, 8, 8, 400, 128)]:
+        p = ea.fwd_plan(*shape)
+        assert p["key_splits"] == 1 and p["block_q"] == 128 and p["threads"] == 256, shape
+    for N, nw in [(1, 2), (64, 2), (128, 2), (129, 4), (256, 4), (257, 8), (512, 8)]:
+        assert ea.fwd_plan(1, 2, 1, N, 80, True)["key_splits"] == nw, N
     for d in ea.SUPPORTED_HEAD_DIMS:
         q = ea.fwd_plan(2, 32, 32, 4096, d, True)
         assert q["workgroups"] == 2 * 32 * 4096 // q["block_q"]

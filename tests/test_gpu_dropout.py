@@ -117,7 +117,11 @@ def test_dropout_streams_and_determinism():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert not torch.equal(o1, o3) and not torch.equal(o1, o4)
-    assert torch.equal(l1, l3) and torch.equal(l1, l0)  # dropout leaves the LSE alone
+    # dropout leaves the LSE alone: bit for bit between dropout streams (one
+    # kernel), and to fp32 rounding against the plain forward, which takes
+    # the key-split plan at this length and so sums in another order
+    assert torch.equal(l1, l3)
+    assert float((l1 - l0).abs().max()) <= 1e-5
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
     assert torch.equal(o0, oz) and torch.equal(l0, lz)

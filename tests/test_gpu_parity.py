@@ -38,6 +38,11 @@ SMALL = [
     (1, 2, 2, 130, 96, False),
     (1, 2, 1, 260, 192, True),
     (1, 2, 2, 70, 192, False),
+    # past 512 keys: the step-loop forward at the head dims whose short
+    # shapes take the key-split forward
+    (1, 2, 1, 777, 32, True),
+    (1, 2, 1, 700, 96, False),
+    (1, 2, 2, 600, 64, False),
 ]
 
 
