@@ -567,7 +567,11 @@ attn_status attn_bwd_ex(const attn_problem* problem, const attn_tensor* q, const
 }
 
 const char* attn_status_string(attn_status status) {
-    switch (status) {
+    // C callers may pass any int; reading an out-of-range value through the
+    // enum type is undefined in C++, so the code is copied out as an int.
+    int code;
+    std::memcpy(&code, &status, sizeof code);
+    switch (code) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL: return "a required pointer is NULL";
         case ATTN_ERR_SHAPE: return "B, Hq, Hkv and N must be >= 1 and the sizes must fit the grid";
