@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "OUT"),
                     help="tabulate the per-dispatch averages of every counter of a rocprofv3 "
                          "--pmc run of this script for the attention kernels and exit")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="time the matrix-core rate probe on N(0,1) bf16 operands (and on zeros) "
+                         "and print one JSON line instead of the attention bench")
     ap.add_argument("--summarize-waves", nargs=2, metavar=("PMC_DIR", "OUT"),
                     help="turn a rocprofv3 --pmc run of this script with the SQ wave-state "
                          "counters into a per-kernel breakdown of wave time and exit")
@@ -245,18 +248,23 @@ def summarize_busy(grbm_dir, mfma_dir, out, workload):
     with open(out, "w") as f:
         f.write(f"# Clock and matrix-core busy fraction on {workload}, from rocprofv3 counters.\n")
         f.write("# Commands (run from the repository root on the MI355X box):\n")
-        f.write(f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE -f csv -d <grbm_dir> -- python bench.py "
-                f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
-        f.write(f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d <mfma_dir> -- "
-                f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
-        f.write(f"#   python bench.py --workload {workload} --summarize-busy <grbm_dir> <mfma_dir> <this file>\n")
+        if os.path.abspath(grbm_dir) == os.path.abspath(mfma_dir):
+            f.write(f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d <dir> -- "
+                    f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+            f.write(f"#   python bench.py --workload {workload} --summarize-busy <dir> <dir> <this file>\n")
+        else:
+            f.write(f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE -f csv -d <grbm_dir> -- python bench.py "
+                    f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+            f.write(f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d <mfma_dir> -- "
+                    f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+            f.write(f"#   python bench.py --workload {workload} --summarize-busy <grbm_dir> <mfma_dir> <this file>\n")
         f.write(f"# cycles = GRBM_GUI_ACTIVE / {XCDS} XCDs; clock = cycles / dispatch duration;\n")
         f.write(f"# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / {SIMDS} SIMDs, as a share of the cycles.\n")
         f.write("# The counter window is a little longer than the dispatch, so kernels shorter than\n"
                 "# about 0.1 ms read a clock above the real one; the long kernels are not affected.\n")
         f.write("kernel | dispatches | avg us | clock GHz (min-max) | cycles | MFMA busy cycles per SIMD | busy share\n")
         for name, v in sorted(grbm.items(), key=lambda kv: -sum(d for _, d in kv[1])):
-            if "attn::" not in name:
+            if "attn::" not in name and "mfma_rate_kernel" not in name:
                 continue
             dur = sum(d for _, d in v) / len(v)
             cyc = sum(c for c, _ in v) / len(v) / XCDS
@@ -361,6 +369,35 @@ def cpu_model():
     except OSError:
         pass
     return platform.processor() or "unknown"
+
+
+def mfma_ceiling(steps):
+    """TFLOP/s of attn_probe_mfma_rate (independent v_mfma_f32_32x32x16_bf16
+    products, two waves per SIMD, no other work) on operands drawn like the
+    workloads' inputs (N(0,1) rounded to bf16) and on all-zero operands: the
+    matrix-core rate the chip sustains under its power management for each
+    operand pattern, which bounds every attention kernel's MFMA throughput."""
+    import torch
+
+    import exact_attention_12_amd as ea
+    blocks, iters = 1024, 1024
+    n = ea.probe_mfma_src_elems(blocks)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(4242)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, src in (("random", torch.randn(n, generator=g).to(torch.bfloat16).cuda()),
+                      ("zeros", torch.zeros(n, dtype=torch.bfloat16, device="cuda"))):
+        dst = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+        for chains in (1, 2, 4, 8):
+            flops = ea.probe_mfma_rate(src, dst, blocks, iters, chains)  # warm-up
+            ms = time_loop(lambda: ea.probe_mfma_rate(src, dst, blocks, iters, chains), steps, stream)
+            out[f"{name}_chains{chains}"] = {
+                "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                "pct_of_bf16_peak": round(100.0 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    line = {"probe": "mfma_ceiling", "op": "v_mfma_f32_32x32x16_bf16", "waves_per_simd": 2,
+            "flops_per_call": blocks * 8 * 8 * iters * 32768.0, "steps": steps, **out}
+    print(json.dumps(line), flush=True)
 
 
 def time_loop(fn, steps, stream):
@@ -603,6 +640,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.mfma_ceiling:
+        mfma_ceiling(args.steps)
+        return
 
     w = si.WORKLOADS[args.workload]
     inputs = si.workload_inputs(w)

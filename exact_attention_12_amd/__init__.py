@@ -158,13 +158,18 @@ def lib() -> ctypes.CDLL:
     L.attn_last_hip_error.restype = ctypes.c_char_p
     L.attn_fwd_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(AttnPlan)]
     L.attn_fwd_plan.restype = i
+    L.attn_probe_mfma_src_elems.argtypes = [i]
+    L.attn_probe_mfma_src_elems.restype = sz
+    L.attn_probe_mfma_rate.argtypes = [vp, vp, i, i, i, vp]
+    L.attn_probe_mfma_rate.restype = i
     _lib = L
     return L
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/attn.h declares."""
-    text = open(HEADER_PATH).read()
+    """Names of the functions the headers under include/ declare."""
+    inc = os.path.dirname(HEADER_PATH)
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(attn_\w+)\s*\(", text, re.M)))
 
 
@@ -505,3 +510,21 @@ def fwd_plan(B, Hq, Hkv, N, d, causal=False) -> dict:
     plan = AttnPlan()
     _check(lib().attn_fwd_plan(B, Hq, Hkv, N, d, int(bool(causal)), ctypes.byref(plan)))
     return {name: getattr(plan, name) for name, _ in AttnPlan._fields_}
+
+
+def probe_mfma_rate(src, dst, blocks, iters, chains=8):
+    """attn_probe_mfma_rate (include/attn_probe.h): enqueue the matrix-core
+    rate probe on the current stream; src holds probe_mfma_src_elems(blocks)
+    bf16 values, dst blocks * 512 floats. Returns the flops it enqueues."""
+    import torch
+    if src.dtype != torch.bfloat16 or src.numel() < lib().attn_probe_mfma_src_elems(blocks):
+        raise ValueError("src must hold probe_mfma_src_elems(blocks) bf16 values")
+    if dst.dtype != torch.float32 or dst.numel() < blocks * 512:
+        raise ValueError("dst must hold blocks * 512 floats")
+    _check(lib().attn_probe_mfma_rate(src.data_ptr(), dst.data_ptr(), blocks, iters, chains,
+                                      _stream_ptr(src.device)))
+    return blocks * 8 * 8 * iters * 32768.0
+
+
+def probe_mfma_src_elems(blocks) -> int:
+    return int(lib().attn_probe_mfma_src_elems(blocks))

@@ -28,6 +28,7 @@ SOURCES = {
     "attn_bwd.hip": [],
     "attn_bwd_dq.hip": [],
     "attn_decode.hip": [],
+    "mfma_probe.hip": [],
 }
 
 # Packed fp32 VALU forms are turned off for all device code. MFMA results

@@ -385,3 +385,13 @@ def test_noalloc_validates_like_bwd(L):
 def test_noalloc_rejects_problems_past_its_scratch(L, B, Hq, N):
     # more than 2^21 query rows: the fixed 16 MiB scratch cannot hold their row terms
     assert noalloc(L, B=B, Hq=Hq, Hkv=1, N=N) == 14
+
+
+def test_mfma_probe_validates(L):
+    assert L.attn_probe_mfma_src_elems(3) == 3 * 512 * 16
+    assert L.attn_probe_mfma_rate(None, P, 4, 8, 8, None) == 1
+    assert L.attn_probe_mfma_rate(P, None, 4, 8, 8, None) == 1
+    assert L.attn_probe_mfma_rate(P, P, 0, 8, 8, None) == 2
+    assert L.attn_probe_mfma_rate(P, P, 4, 0, 8, None) == 2
+    assert L.attn_probe_mfma_rate(P, P, (1 << 20) + 1, 8, 8, None) == 2
+    assert L.attn_probe_mfma_rate(P, P, 4, 8, 3, None) == 2
