@@ -45,6 +45,9 @@
 //    wave skips the math of blocks after its own last query; the diagonal
 //    blocks are masked per element. Heavy (late) query blocks are launched
 //    first.
+//  * Short sequences take fwd_split_kernel instead (further down): the keys
+//    of one 32-row tile are split over the workgroup's waves, which load
+//    everything at once and merge in LDS.
 #include <type_traits>
 
 #include "attn_device.h"
