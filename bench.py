@@ -176,8 +176,10 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload, mib):
     written = []
     for kernel in ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel",
                    "decode_split_kernel", "decode_merge_kernel"):
-        # the dK/dV pass runs the 64-keys-per-wave kernel on large d = 128 grids
-        prefixes = [f"{kernel}<"] + (["bwd_dkdv_wide_kernel<"] if kernel == "bwd_dkdv_kernel" else [])
+        # the dK/dV pass runs the 64-keys-per-wave kernel on large d = 128 grids,
+        # the forward the key-split kernel on short sequences
+        prefixes = [f"{kernel}<"] + (["bwd_dkdv_wide_kernel<"] if kernel == "bwd_dkdv_kernel" else []) + \
+            (["fwd_split_kernel<"] if kernel == "fwd_kernel" else [])
         hits = [(pf, k) for pf in prefixes for k in fetch if pf in k]
         if not hits:
             continue
