@@ -861,6 +861,7 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int bufi = it & 1;
         const int q0 = cur.qb * BQ;
+        const int g = cur.g;  // this step's head (cur moves on to the next step below)
         if (!MASKED && cur.qb + 1 < qu_end) {
             const int sqb = BQ * (int)p.sq.n, sdb = BQ * (int)p.sdo.n;
             cx.bq += sqb;
@@ -902,7 +903,7 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
         // r for register r), as in the 32-key kernel.
         uint32_t keep[2] = {0u, 0u};
         if constexpr (DROP) {
-            const uint32_t bh = (uint32_t)(b * p.Hq + hq0 + cur.g);
+            const uint32_t bh = (uint32_t)(b * p.Hq + hq0 + g);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 keep[j] = keep_bits_key_lane(p.drop, (uint32_t)(kw0 + 32 * j + l32), (uint32_t)(q0 + 4 * h) >> 2, bh);

@@ -30,6 +30,10 @@ CASES = [
     # workgroups, partial sums added by a second kernel
     (1, 256, 128, 520, "causal", "bf16", "bhsd", 0.0),  # 3 x 128
     (1, 128, 64, 1030, 300, "fp16", "bshd", 0.1),       # 5 x 64, window, dropout
+    # dropout with two query heads per workgroup: each step's keep bits must
+    # come from that step's head (G = 2 unsplit; G = 4 split in two)
+    (1, 256, 128, 1037, "causal", "bf16", "bhsd", 0.1),  # 5 x 128
+    (1, 128, 32, 1800, "causal", "fp16", "bshd", 0.1),   # 8 x 32, split
 ]
 
 
