@@ -34,13 +34,21 @@ METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at 1 MI355X vs CPU o
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DEFAULT_WORKLOAD = "c5_bwd_d128"
+# Default warm-up: the chip raises its clock over the first few tens of
+# milliseconds of load; five steps of a 0.3 ms workload left it measurably
+# slower (C3's forward 0.347 ms against 0.272 ms after 100 steps).
+WARMUP_MIN_STEPS = 5
+WARMUP_SECONDS = 0.3
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps; by default at least %d, and as many as %.1f s of "
+                         "steps take, so that the chip's clocks have settled before the timed "
+                         "steps (short steps otherwise run at a lower clock)" % (WARMUP_MIN_STEPS, WARMUP_SECONDS))
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
@@ -252,13 +260,13 @@ def summarize_busy(grbm_dir, mfma_dir, out, workload):
         f.write("# Commands (run from the repository root on the MI355X box):\n")
         if os.path.abspath(grbm_dir) == os.path.abspath(mfma_dir):
             f.write(f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d <dir> -- "
-                    f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+                    f"python bench.py --workload {workload} --steps 2 --no-cpu-baseline\n")
             f.write(f"#   python bench.py --workload {workload} --summarize-busy <dir> <dir> <this file>\n")
         else:
             f.write(f"#   rocprofv3 --pmc GRBM_GUI_ACTIVE -f csv -d <grbm_dir> -- python bench.py "
-                    f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+                    f"--workload {workload} --steps 2 --no-cpu-baseline\n")
             f.write(f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d <mfma_dir> -- "
-                    f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline\n")
+                    f"python bench.py --workload {workload} --steps 2 --no-cpu-baseline\n")
             f.write(f"#   python bench.py --workload {workload} --summarize-busy <grbm_dir> <mfma_dir> <this file>\n")
         f.write(f"# cycles = GRBM_GUI_ACTIVE / {XCDS} XCDs; clock = cycles / dispatch duration;\n")
         f.write(f"# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / {SIMDS} SIMDs, as a share of the cycles.\n")
@@ -400,6 +408,27 @@ def mfma_ceiling(steps):
     line = {"probe": "mfma_ceiling", "op": "v_mfma_f32_32x32x16_bf16", "waves_per_simd": 2,
             "flops_per_call": blocks * 8 * 8 * iters * 32768.0, "steps": steps, **out}
     print(json.dumps(line), flush=True)
+
+
+def warm_up(launches, steps):
+    """Run the step's launches untimed: `steps` times if given, else at least
+    WARMUP_MIN_STEPS times and until WARMUP_SECONDS have passed. Returns the
+    number of warm-up steps run."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        if steps is not None and n >= steps:
+            break
+        for f in launches:
+            f()
+        n += 1
+        if steps is None and n >= WARMUP_MIN_STEPS and n % WARMUP_MIN_STEPS == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARMUP_SECONDS:
+                break
+    torch.cuda.synchronize()
+    return n
 
 
 def time_loop(fn, steps, stream):
@@ -565,7 +594,7 @@ def summarize_trace(trace_dir, bench_json, out_md, workload):
            f"{w.mask}, {'fwd+bwd' if w.backward else 'fwd'})", "",
            "Commands (repository root on the MI355X box):", "",
            f"    cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d <trace_dir> -o trace -- "
-           f"python <repo>/bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+           f"python <repo>/bench.py --workload {workload} --steps 20 --no-cpu-baseline",
            f"    python bench.py --workload {workload} > <bench_json>",
            f"    python bench.py --workload {workload} --summarize-trace <trace_dir> <bench_json> <this file>",
            "", "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
@@ -692,10 +721,7 @@ def main():
         names += ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
         launches += [bwd_pass("pre"), bwd_pass("dkdv"), bwd_pass("dq")]
 
-    for _ in range(args.warmup):
-        for f in launches:
-            f()
-    torch.cuda.synchronize()
+    warmup = warm_up(launches, args.warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
           for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -796,7 +822,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_median": round(median(step_ms), 4),
         "ms_per_step_min": round(step_ms[0], 4),
