@@ -71,6 +71,7 @@ class AttnPlan(ctypes.Structure):
         ("workgroups", ctypes.c_longlong),
         ("lds_bytes", ctypes.c_int),
         ("key_splits", ctypes.c_int),
+        ("key_groups", ctypes.c_int),
     ]
 
 

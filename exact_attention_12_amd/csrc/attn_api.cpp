@@ -611,6 +611,7 @@ attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn
     plan->workgroups = fp.workgroups;
     plan->lds_bytes = fp.lds_bytes;
     plan->key_splits = fp.key_splits;
+    plan->key_groups = fp.key_groups;
     return ATTN_OK;
 }
 

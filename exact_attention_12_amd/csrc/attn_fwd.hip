@@ -48,6 +48,15 @@
 //  * Short sequences take fwd_split_kernel instead (further down): the keys
 //    of one 32-row tile are split over the workgroup's waves, which load
 //    everything at once and merge in LDS.
+//  * Key groups (KG = 2): when the grid is so small that the longest query
+//    block's key loop decides the time, the 4 waves form two groups of 2
+//    over the same 64 rows (one wave per SIMD, one workgroup per CU); group
+//    0 walks the first half of the block's key tiles and group 1 the rest,
+//    each with its own double-buffered tiles, and group 1 hands its (m, l,
+//    O) to group 0 through LDS at the end. The two partial softmax states
+//    combine exactly: M = max(m0, m1), l = sum_g 2^(m_g - M) l_g,
+//    O = sum_g 2^(m_g - M) O_g. (Two groups of 4 waves over 128 rows, two
+//    waves per SIMD, gained nothing: the groups then share each SIMD.)
 #include <type_traits>
 
 #include "attn_device.h"
@@ -55,11 +64,14 @@
 
 namespace attn {
 
-template <int DT, int D, int MASK, int NW, bool DROP>
-__global__ __launch_bounds__(NW * 64, (D <= 128 ? 2 : 1))
+// Two waves per SIMD, except d > 128 and the 4-wave key-group kernel, whose
+// tile buffers leave room for one workgroup (one wave per SIMD) per CU.
+template <int DT, int D, int MASK, int NW, bool DROP, int KG>
+__global__ __launch_bounds__(NW * 64, (D <= 128 && !(KG == 2 && NW == 4) ? 2 : 1))
 void fwd_kernel(FwdParams p) {
     constexpr int T = NW * 64;
-    constexpr int BQ = NW * 32;
+    constexpr int WG = NW / KG;          // waves per key group
+    constexpr int BQ = WG * 32;          // query rows of the workgroup
     constexpr bool CAUSAL = MASK != kMaskNone;
     constexpr bool WINDOW = MASK == kMaskWindow;
     constexpr int BC = FwdTile<D>::BLOCK_KV;
@@ -73,12 +85,15 @@ void fwd_kernel(FwdParams p) {
     constexpr int CHUNKS = BC * CPR;
     constexpr int NCH = (CHUNKS + T - 1) / T;
     constexpr int BUF = BC * (KP + VP);
+    static_assert(KG == 1 || (KG == 2 && BC == 64 && !DROP), "key groups: d <= 128, no dropout");
 
-    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF * KG];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer resources
+    const int grp = KG == 1 ? 0 : wave / WG;  // key group
+    const int gw = wave - grp * WG;           // wave within the group = its 32-row tile
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int N = p.N;
@@ -87,7 +102,7 @@ void fwd_kernel(FwdParams p) {
     // latest (heaviest) query blocks come first.
     const int bid = blockIdx.x;
     const int bh = xcd_head(bid % p.BH, p.BH);
-    const int qb = causal_block(bid / p.BH, p.nqb, NW == 4 && gridDim.x <= 512, CAUSAL);
+    const int qb = causal_block(bid / p.BH, p.nqb, NW == 4 && KG == 1 && gridDim.x <= 512, CAUSAL);
     const int b = bh / p.Hq;
     const int hq = bh - b * p.Hq;
     const int hkv = hq / p.G;
@@ -98,14 +113,14 @@ void fwd_kernel(FwdParams p) {
     const long long sqn = p.sq.n, skn = p.sk.n, svn = p.sv.n;
 
     const int q0 = qb * BQ;
-    const int qw0 = q0 + wave * 32;
+    const int qw0 = q0 + gw * 32;
     const int qrow = qw0 + l32;
 
     // Columns d .. padded width of the V tiles are read by the last O^T tile
     // and must be zero; the loaders never write them.
     if constexpr (NDT * 32 > D) {
         constexpr int PADC = NDT * 32 - D;
-        for (int i = tid; i < 2 * BC * PADC; i += T) {
+        for (int i = tid; i < 2 * KG * BC * PADC; i += T) {
             const int row = i / PADC;
             const int col = D + i % PADC;
             const int bufi = row / BC;
@@ -173,44 +188,54 @@ void fwd_kernel(FwdParams p) {
     constexpr bool DIRECT = BC == 64;
     constexpr int CKK = KP / 8, CKV = VP / 8;           // chunks per padded row
     constexpr int NLK = BC * CKK / 64, NLV = BC * CKV / 64;  // loads per tile
-    constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
+    // A group's tiles are loaded by its own WG waves.
+    constexpr int LPWK = (NLK + WG - 1) / WG, LPWV = (NLV + WG - 1) / WG;
     static_assert(!DIRECT || (BC * CKK % 64 == 0 && BC * CKV % 64 == 0), "tile must be whole loads");
     uint32_t offk[DIRECT ? LPWK : 1], offv[DIRECT ? LPWV : 1];
     if constexpr (DIRECT) {
         const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
-            const int chunk = (wave + i * NW) * 64 + lane;
+            const int chunk = (gw + i * WG) * 64 + lane;
             const int row = chunk / CKK, ch = chunk - row * CKK;
             offk[i] = ch < CPR ? (uint32_t)row * sk2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
         }
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
-            const int chunk = (wave + i * NW) * 64 + lane;
+            const int chunk = (gw + i * WG) * 64 + lane;
             const int row = chunk / CKV, ch = chunk - row * CKV;
             offv[i] = ch < CPR ? (uint32_t)row * sv2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
         }
     }
+    e16* const gsm = smem + grp * 2 * BUF;  // this group's two tile buffers
     auto issue_tile = [&](int kv0, int bufi) {
         const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
         const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
         const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
-        char* kb_lds = reinterpret_cast<char*>(smem + bufi * BUF);
+        char* kb_lds = reinterpret_cast<char*>(gsm + bufi * BUF);
         char* vb_lds = kb_lds + BC * KP * 2;
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
-            const int j = wave + i * NW;
-            if (NLK % NW == 0 || j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
+            const int j = gw + i * WG;
+            if (NLK % WG == 0 || j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
         }
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
-            const int j = wave + i * NW;
-            if (NLV % NW == 0 || j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
+            const int j = gw + i * WG;
+            if (NLV % WG == 0 || j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
         }
     };
 
+    // Key tiles of this group: [gs, ge). With one group that is the whole
+    // range; with two, group 0 takes the first ceil(n/2) tiles.
+    const int kmid = kb_begin + (kb_end - kb_begin + 1) / 2;
+    const int gs = KG == 1 ? kb_begin : (grp == 0 ? kb_begin : kmid);
+    const int ge = KG == 1 ? kb_end : (grp == 0 ? kmid : kb_end);
     if constexpr (DIRECT) {
-        issue_tile(kb_begin * BC, kb_begin & 1);
+        if (KG == 1)
+            issue_tile(kb_begin * BC, kb_begin & 1);
+        else if (gs < ge)
+            issue_tile(gs * BC, 0);
         __builtin_amdgcn_s_waitcnt(0);
     } else {
         load_tile(kb_begin * BC);
@@ -231,20 +256,24 @@ void fwd_kernel(FwdParams p) {
     const int tr_row = (g16 >> 1) * 4 + (j16 >> 2);
     const int tr_col = (g16 & 1) * 16 + (j16 & 3) * 4;
 
-    auto run_step = [&](int kb, auto masked_tag) {
+    // One step: tile kb in buffer bufi, the next tile (kb + 1, at most
+    // kb_last) loaded into the other buffer. `has` is false only for the
+    // idle last step of a key group with fewer tiles, which just keeps the
+    // barrier count.
+    auto run_step = [&](int kb, int bufi, int kb_last, bool has, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int bufi = kb & 1;
         // The last step reloads its own tile into the idle buffer (never
         // read again), so the loads and stores need no branch.
-        if constexpr (DIRECT)
-            issue_tile(min(kb + 1, kb_end - 1) * BC, bufi ^ 1);
-        else
-            load_tile(min(kb + 1, kb_end - 1) * BC);
+        if constexpr (DIRECT) {
+            if (has) issue_tile(min(kb + 1, kb_last) * BC, bufi ^ 1);
+        } else {
+            load_tile(min(kb + 1, kb_last) * BC);
+        }
 
         const int kv0 = kb * BC;
-        const e16* Ks = smem + bufi * BUF;
+        const e16* Ks = gsm + bufi * BUF;
         const e16* Vs = Ks + BC * KP;
-        const bool active = !MASKED || !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
+        const bool active = has && (!MASKED || !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1)));
         if (active) {
             f32x16 s[NKT];
             if constexpr (D <= 128) {
@@ -411,13 +440,58 @@ void fwd_kernel(FwdParams p) {
         ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
     }
     ku_end = max(ku_end, ku_begin);
-    int kb = kb_begin;
-    for (; kb < ku_begin; ++kb) run_step(kb, std::true_type{});
-    for (; kb < ku_end; ++kb) run_step(kb, std::false_type{});
-    for (; kb < kb_end; ++kb) run_step(kb, std::true_type{});
+    float lt;
+    if constexpr (KG == 1) {
+        int kb = kb_begin;
+        for (; kb < ku_begin; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::true_type{});
+        for (; kb < ku_end; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::false_type{});
+        for (; kb < kb_end; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::true_type{});
+        lt = sum_across_halves(l);  // the two half-row sums
+    } else {
+        // Both groups step together (one barrier per step); group 0 has the
+        // same number of tiles as group 1 or one more.
+        const int nit = kmid - kb_begin;
+        for (int it = 0; it < nit; ++it) {
+            const int kb = gs + it;
+            const bool has = kb < ge;
+            if (has && (kb < ku_begin || kb >= ku_end))
+                run_step(kb, it & 1, ge - 1, true, std::true_type{});
+            else
+                run_step(kb, it & 1, ge - 1, has, std::false_type{});
+        }
+        // Group 1 hands (m, l, O^T) to the wave of group 0 with the same rows,
+        // through the tile buffers (every wave has finished with them: each
+        // waited for its own loads before the last barrier).
+        const float lg = sum_across_halves(l);
+        constexpr int OSZ = WG * NDT * 16 * 64;
+        static_assert((OSZ + 2 * WG * 64) * 4 <= 2 * KG * BUF * 2, "merge data must fit the tile buffers");
+        float* xs = reinterpret_cast<float*>(smem);
+        if (grp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xs[((gw * NDT + dt) * 16 + r) * 64 + lane] = oacc[dt][r];
+            xs[OSZ + gw * 64 + lane] = m;
+            xs[OSZ + (WG + gw) * 64 + lane] = lg;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = xs[OSZ + gw * 64 + lane];
+        const float l1 = xs[OSZ + (WG + gw) * 64 + lane];
+        const float mm = fmaxf(m, m1);
+        // a group that met no allowed key of the row has m = -inf and adds nothing
+        const float a0 = m == -__builtin_huge_valf() ? (m1 == -__builtin_huge_valf() ? 1.0f : 0.0f) : fast_exp2(m - mm);
+        const float a1 = m1 == -__builtin_huge_valf() ? 0.0f : fast_exp2(m1 - mm);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                oacc[dt][r] = a0 * oacc[dt][r] + a1 * xs[((gw * NDT + dt) * 16 + r) * 64 + lane];
+        lt = a0 * lg + a1 * l1;
+        m = mm;
+    }
 
-    // Epilogue: combine the two half-row sums, normalise, store O and LSE.
-    const float lt = sum_across_halves(l);
+    // Epilogue: normalise, store O and LSE.
     const float inv = (DROP ? p.drop.scale : 1.0f) / lt;
     if (qrow < N) {
         e16* orow = static_cast<e16*>(p.o) + b * p.so.b + hq * p.so.h + qrow * p.so.n;
@@ -672,12 +746,22 @@ template <int DT, int D, int MASK, bool DROP>
 static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
     const dim3 grid((unsigned)plan.workgroups), block((unsigned)plan.threads);
     if constexpr (D <= 128) {
+        if (plan.key_groups == 2) {
+            if constexpr (DROP) {
+                return hipErrorInvalidValue;  // the plan never pairs them
+            } else {
+                if (plan.waves != 4) return hipErrorInvalidValue;
+                hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 4, false, 2>), grid, block, 0, stream, p);
+                return hipGetLastError();
+            }
+        }
         if (plan.waves == 8) {
-            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP, 1>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 4, DROP>), grid, block, 0, stream, p);
+    if (plan.key_groups != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 4, DROP, 1>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
@@ -722,6 +806,7 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
     const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
     const long long wg128 = (long long)((N + 127) / 128) * B * Hq;
     plan->key_splits = 1;
+    plan->key_groups = 1;
     // Short sequences whose grid of 128-row workgroups would leave CUs idle:
     // the key-split kernel (one workgroup per 32 rows, waves over the keys).
     if (D <= kSplitMaxD && !dropout && N <= kSplitMaxKeys && wg128 < kSplitMaxGrid) {
@@ -737,9 +822,33 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
         plan->lds_bytes = SplitTile<D <= kSplitMaxD ? D : 32>::lds_bytes(nw);
         return;
     }
+    const int BC = FwdTile<D>::BLOCK_KV;
+    // Key groups: the longest query block walks nkb key tiles one after the
+    // other, while the average SIMD holds `load` wave steps (32-row tiles
+    // times their mean key tiles over the chip's 1024 SIMDs). When nkb is at
+    // least about twice the load, the longest blocks decide the kernel's
+    // time and splitting their keys over two groups of waves pays: measured
+    // 1.06-1.41x on grids of 256 to 1024 row tiles at ratios of 1.9 to 8,
+    // and 0.7-0.95x at ratios of 1 to 1.9.
+    if (D <= 128 && !dropout) {
+        const int nkb = (N + BC - 1) / BC;
+        const double tiles32 = (double)((N + 31) / 32) * B * Hq;
+        const double mean_kb = causal ? (nkb + 1) / 2.0 : (double)nkb;
+        const double load = tiles32 * mean_kb / kSimds;
+        if (nkb >= 4 && nkb >= 1.9 * load) {
+            plan->rows_per_wave = 32;
+            plan->waves = 4;
+            plan->key_groups = 2;
+            plan->block_q = 64;
+            plan->block_kv = BC;
+            plan->threads = 256;
+            plan->workgroups = (long long)((N + 63) / 64) * B * Hq;
+            plan->lds_bytes = 2 * 2 * BC * (k_pitch(D) + v_pitch(D)) * 2;
+            return;
+        }
+    }
     const int waves = (D <= 128 && wg256 >= (causal ? 512 : 256)) ? 8 : 4;
     const int BQ = waves * 32;
-    const int BC = FwdTile<D>::BLOCK_KV;
     plan->rows_per_wave = 32;
     plan->waves = waves;
     plan->block_q = BQ;

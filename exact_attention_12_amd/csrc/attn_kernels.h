@@ -169,7 +169,11 @@ struct FwdPlan {
     long long workgroups;
     int lds_bytes;
     int key_splits;     // > 1: the key-split kernel, its waves each take 64 keys of one 32-row tile
+    int key_groups;     // 2: the step-loop kernel with its 4 waves in two groups over one 64-row block's keys
 };
+
+// SIMDs of the part (256 compute units x 4), for the forward plan's load estimate.
+constexpr int kSimds = 1024;
 
 // Key-split forward for short sequences: head dims up to kSplitMaxD, at most
 // kSplitMaxKeys keys (one 64-key tile per wave, 8 waves), used when the

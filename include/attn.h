@@ -367,6 +367,11 @@ typedef struct attn_plan {
     int key_splits;  /* > 1: short-sequence plan, each 32-row query tile's keys
                         split over this many waves of one workgroup (64 keys
                         each) and combined in LDS; 1: the step-loop kernel */
+    int key_groups;  /* 2: the step-loop kernel with its 4 waves in two groups
+                        of 2 over one 64-row query block, each group walking
+                        half of the block's key tiles, the two softmax states
+                        combined in LDS (small grids, where the longest
+                        block's key loop would decide the time); else 1 */
 } attn_plan;
 
 attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn_plan* plan);

@@ -138,10 +138,25 @@ def test_fwd_plan(L):
     assert p["block_q"] == 32 and p["key_splits"] == 8 and p["threads"] == 512
     assert p["workgroups"] == math.ceil(400 / 32) * 8
     assert p["lds_bytes"] <= 160 * 1024
-    # past 512 keys, 128 or more workgroups of 128 rows, or d = 128: the step loop
-    for shape in [(1, 8, 8, 513, 64), (4, 16, 16, 512, 64), (1, 8, 8, 400, 128)]:
+    # past 512 keys, 128 or more workgroups of 128 rows, or d = 128: the step
+    # loop with one group of 4 waves
+    p = ea.fwd_plan(4, 16, 16, 512, 64)
+    assert p["key_splits"] == 1 and p["key_groups"] == 1 and p["block_q"] == 128 and p["threads"] == 256
+    # grids so small that the longest block's key tiles are about twice the
+    # average SIMD's wave steps or more: two groups of 2 waves over 64 rows,
+    # one workgroup per CU
+    for shape in [(1, 8, 8, 513, 64), (1, 8, 8, 400, 128), (1, 2, 2, 4096, 128, True), (1, 8, 8, 2048, 128, True)]:
         p = ea.fwd_plan(*shape)
-        assert p["key_splits"] == 1 and p["block_q"] == 128 and p["threads"] == 256, shape
+        assert p["key_splits"] == 1 and p["key_groups"] == 2, shape
+        assert p["block_q"] == 64 and p["threads"] == 256, shape
+        assert p["workgroups"] == math.ceil(shape[3] / 64) * shape[0] * shape[1], shape
+        assert p["lds_bytes"] <= 160 * 1024, shape
+    assert ea.fwd_plan(1, 8, 8, 2048, 80, True)["lds_bytes"] == 2 * 2 * 64 * (88 + 96) * 2
+    # larger grids (the d = 80 training shape among them), head dims past 128: one group
+    for shape in [(2, 32, 32, 4096, 128, True), (1, 16, 16, 16384, 128, True), (1, 64, 8, 8192, 128, True),
+                  (4, 16, 16, 2048, 64, False), (1, 16, 16, 4096, 80, True), (1, 16, 16, 4096, 128, True),
+                  (1, 2, 2, 4096, 192, True), (1, 2, 2, 4096, 256, False)]:
+        assert ea.fwd_plan(*shape)["key_groups"] == 1, shape
     for N, nw in [(1, 2), (64, 2), (128, 2), (129, 4), (256, 4), (257, 8), (512, 8)]:
         assert ea.fwd_plan(1, 2, 1, N, 80, True)["key_splits"] == nw, N
     for d in ea.SUPPORTED_HEAD_DIMS:
@@ -297,7 +312,10 @@ def test_bwd_ex_validation(L):
 def test_head_dims_have_plans(L):
     for d in ea.SUPPORTED_HEAD_DIMS:
         p = ea.fwd_plan(1, 4, 4, 1000, d)
-        assert p["lds_bytes"] <= 160 * 1024 // (2 if d <= 128 else 1)
+        # two workgroups per CU, except one for d > 128 and for the
+        # key-group plan (8 waves in two groups, twice the tile buffers)
+        one_per_cu = d > 128 or p["key_groups"] == 2
+        assert p["lds_bytes"] <= 160 * 1024 // (1 if one_per_cu else 2)
         assert p["block_kv"] == (64 if d <= 128 else 32)
 
 

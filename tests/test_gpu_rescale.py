@@ -22,8 +22,10 @@ wrong rescale errs by the order of |O| itself (0.1 to 1 here). Every case first 
 scores, that the lazy rule fires on the rows it checks; the outputs are then
 compared with the oracle element by element (O, LSE) and per tensor (dQ, dK,
 dV), at d = 64 and 128, with no mask, causal and sliding-window masks, in
-bf16 and fp16, on the 4-wave and the 8-wave forward plans (the latter above
-512 causal / 256 unmasked blocks of 256 rows).
+bf16 and fp16, on the three plans of the step-loop forward: two key groups
+of 4 waves over a 128-row block (small grids, where each group keeps its own
+reference maximum and the two are combined at the end), and one group of 4
+or of 8 waves (larger grids).
 """
 
 import numpy as np
@@ -42,22 +44,25 @@ BLOCK_KV = 64  # keys per forward step at d <= 128
 LAZY = 8.0     # the reference maximum moves when a block beats it by more than this (log2 units)
 
 CASES = [
-    # B, Hq, Hkv, N, d, mask, dtype, plan (the forward plan the shape selects)
-    (1, 4, 2, 1000, 64, "causal", "bf16", 4),
-    (1, 4, 2, 1000, 128, "causal", "bf16", 4),
-    (1, 2, 1, 777, 128, "none", "bf16", 4),
-    (1, 2, 2, 901, 64, "none", "fp16", 4),
-    (1, 4, 1, 1000, 128, 300, "bf16", 4),
-    (1, 2, 2, 600, 64, 129, "fp16", 4),
-    (1, 4, 4, 999, 128, "causal", "fp16", 4),
-    (2, 64, 8, 1024, 128, "causal", "bf16", 8),
-    (1, 64, 8, 1024, 64, "none", "bf16", 8),
-    (2, 64, 16, 1024, 128, 200, "bf16", 8),
+    # B, Hq, Hkv, N, d, mask, dtype, plan the shape selects (kg2: two key
+    # groups of 4 waves; w4, w8: one group of 4 or 8 waves)
+    (1, 4, 2, 1000, 64, "causal", "bf16", "kg2"),
+    (1, 4, 2, 1000, 128, "causal", "bf16", "kg2"),
+    (1, 2, 1, 777, 128, "none", "bf16", "kg2"),
+    (1, 2, 2, 901, 64, "none", "fp16", "kg2"),
+    (1, 4, 1, 1000, 128, 300, "bf16", "kg2"),
+    (1, 2, 2, 600, 64, 129, "fp16", "kg2"),
+    (1, 4, 4, 999, 128, "causal", "fp16", "kg2"),
+    (1, 124, 31, 1000, 128, "causal", "bf16", "w4"),
+    (1, 124, 4, 1000, 64, 200, "fp16", "w4"),
+    (2, 64, 8, 1024, 128, "causal", "bf16", "w8"),
+    (1, 64, 8, 1024, 64, "none", "bf16", "w8"),
+    (2, 64, 16, 1024, 128, 200, "bf16", "w8"),
 ]
 
 
 def ids(c):
-    return "B{}_Hq{}_Hkv{}_N{}_d{}_{}_{}_w{}".format(*c)
+    return "B{}_Hq{}_Hkv{}_N{}_d{}_{}_{}_{}".format(*c)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -100,8 +105,8 @@ def test_rescale_fwd_bwd(cfg):
     else:
         kw, causal, window = dict(window=mask), True, mask
     fp = ea.fwd_plan(B, Hq, Hkv, N, d, causal)
-    waves = fp["threads"] // 64
-    assert waves == plan, f"shape selects the {waves}-wave forward plan"
+    got = "kg2" if fp["key_groups"] == 2 else "w{}".format(fp["threads"] // 64)
+    assert fp["key_splits"] == 1 and got == plan, f"shape selects the {got} forward plan"
 
     # a band holds fewer keys, so the norms grow faster there
     growth = 16.0 if window else 64.0
