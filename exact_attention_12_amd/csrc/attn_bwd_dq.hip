@@ -3,7 +3,10 @@
 // One workgroup per (batch, query head, 128-row query block), in the
 // forward's orientation: S^T = K Q^T and dP^T = V dO^T put one query per
 // lane, so LSE_i and D_i are per-lane scalars; dQ^T += K^T dS^T with K^T read
-// from the (chunk-swizzled) K tile by the transposing LDS read. It is a
+// from the (chunk-swizzled) K tile by the transposing LDS read. On grids too
+// small to hide the longest block's key loop, one workgroup per 64-row block
+// instead, whose two pairs of waves each take half of the block's key tiles
+// and add their partial dQ through LDS at the end. It is a
 // separate translation unit because it is scheduled for occupancy (two waves
 // per SIMD), while the dK/dV pass, one wave per SIMD, is scheduled for ILP.
 // The formulas are the chain rule written out in attn_bwd.hip.
@@ -15,14 +18,14 @@ namespace attn {
 
 // ---------------------------------------------------------------- dQ
 
-template <int DT, int D, int MASK, bool DROP>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1))
+template <int DT, int D, int MASK, bool DROP, int KG>
+__global__ __launch_bounds__(256, (D <= 128 && KG == 1 ? 2 : 1))
 void bwd_dq_kernel(BwdParams p) {
     constexpr bool CAUSAL = MASK != kMaskNone;
     constexpr bool WINDOW = MASK == kMaskWindow;
     constexpr int NW = 4;
-    constexpr int T = NW * 64;
-    constexpr int BQ = NW * 32;
+    constexpr int WG = NW / KG;  // waves per key group
+    constexpr int BQ = WG * 32;
     // Keys per step: 64 halves the per-step overhead while two waves per SIMD
     // still fit without spills; dropout (its keep bits) and d > 128 take 32.
     constexpr int BC = (D <= 128 && !DROP) ? 64 : 32;
@@ -33,12 +36,15 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int KP = sw_pitch(D);    // K tile: row reads and transposing reads
     constexpr int VP = k_pitch(D);     // V tile: row reads only
     constexpr int BUF = BC * (KP + VP);
+    static_assert(KG == 1 || (KG == 2 && BC == 64), "key groups: d <= 128, no dropout");
 
-    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF * KG];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches and buffer resources
+    const int grp = KG == 1 ? 0 : wave / WG;  // key group
+    const int gw = wave - grp * WG;           // wave within the group = its 32-row tile
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int N = p.N;
@@ -56,7 +62,7 @@ void bwd_dq_kernel(BwdParams p) {
     const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
 
     const int q0 = qb * BQ;
-    const int qw0 = q0 + wave * 32;
+    const int qw0 = q0 + gw * 32;
     const int qrow = qw0 + l32;
 
 
@@ -104,45 +110,55 @@ void bwd_dq_kernel(BwdParams p) {
     // the end of a tile whose chunk count is not a multiple of 64 are idle.
     constexpr int CKK = KP / 8, CKV = VP / 8;
     constexpr int NLK = (BC * CKK + 63) / 64, NLV = (BC * CKV + 63) / 64;
-    constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
+    // A group's tiles are loaded by its own WG waves.
+    constexpr int LPWK = (NLK + WG - 1) / WG, LPWV = (NLV + WG - 1) / WG;
     uint32_t offk[LPWK], offv[LPWV];
     {
         const uint32_t sk2 = (uint32_t)p.sk.n * 2u, sv2 = (uint32_t)p.sv.n * 2u;
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
-            const int chunk = (wave + i * NW) * 64 + lane;
+            const int chunk = (gw + i * WG) * 64 + lane;
             const int row = chunk / CKK;
             const int lc = (chunk - row * CKK) ^ sw_swizzle(row);
             offk[i] = lc < D / 8 ? (uint32_t)row * sk2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
-            const int chunk = (wave + i * NW) * 64 + lane;
+            const int chunk = (gw + i * WG) * 64 + lane;
             const int row = chunk / CKV;
             const int lc = chunk - row * CKV;
             offv[i] = lc < D / 8 ? (uint32_t)row * sv2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
     }
+    e16* const gsm = smem + grp * 2 * BUF;  // this group's two tile buffers
     auto issue_tile = [&](int kv0, int bufi) {
         const uint32_t sk2 = (uint32_t)p.sk.n * 2u, sv2 = (uint32_t)p.sv.n * 2u;
         const auto rk = buf_rsrc(Kh + (long long)kv0 * p.sk.n, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
         const auto rv = buf_rsrc(Vh + (long long)kv0 * p.sv.n, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
-        char* k_lds = reinterpret_cast<char*>(smem + bufi * BUF);
+        char* k_lds = reinterpret_cast<char*>(gsm + bufi * BUF);
         char* v_lds = k_lds + BC * KP * 2;
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
-            const int j = wave + i * NW;
-            if ((NLK % NW == 0 || j < NLK) && (BC * CKK % 64 == 0 || j * 64 + lane < BC * CKK))
+            const int j = gw + i * WG;
+            if ((NLK % WG == 0 || j < NLK) && (BC * CKK % 64 == 0 || j * 64 + lane < BC * CKK))
                 buf_load16_to_lds(rk, k_lds + j * 1024, offk[i]);
         }
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
-            const int j = wave + i * NW;
-            if ((NLV % NW == 0 || j < NLV) && (BC * CKV % 64 == 0 || j * 64 + lane < BC * CKV))
+            const int j = gw + i * WG;
+            if ((NLV % WG == 0 || j < NLV) && (BC * CKV % 64 == 0 || j * 64 + lane < BC * CKV))
                 buf_load16_to_lds(rv, v_lds + j * 1024, offv[i]);
         }
     };
-    issue_tile(kb_begin * BC, kb_begin & 1);
+    // Key tiles of this group: [gs, ge); with two groups, group 0 takes the
+    // first ceil(n/2).
+    const int kmid = kb_begin + (kb_end - kb_begin + 1) / 2;
+    const int gs = KG == 1 ? kb_begin : (grp == 0 ? kb_begin : kmid);
+    const int ge = KG == 1 ? kb_end : (grp == 0 ? kmid : kb_end);
+    if (KG == 1)
+        issue_tile(kb_begin * BC, kb_begin & 1);
+    else if (gs < ge)
+        issue_tile(gs * BC, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -161,18 +177,20 @@ void bwd_dq_kernel(BwdParams p) {
     const int krd[2] = {sw_off(l32, h * 8, KP), sw_off(l32, 16 + h * 8, KP)};
     const int ktr0 = sw_off(tr_row, tr_col, KP), ktr1 = sw_off(tr_row + 8, tr_col, KP);
 
-    auto run_step = [&](int kb, auto masked_tag) {
+    // One step: tile kb in buffer bufi, the next tile (kb + 1, at most
+    // kb_last) loaded into the other buffer. `has` is false only for the
+    // idle last step of a key group with fewer tiles.
+    auto run_step = [&](int kb, int bufi, int kb_last, bool has, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int bufi = kb & 1;
         // The last step reloads its own tile into the idle buffer (never
         // read again), so the loads need no branch.
-        issue_tile(min(kb + 1, kb_end - 1) * BC, bufi ^ 1);
+        if (has) issue_tile(min(kb + 1, kb_last) * BC, bufi ^ 1);
         const int kv0 = kb * BC;
-        const e16* Ks = smem + bufi * BUF;
+        const e16* Ks = gsm + bufi * BUF;
         const e16* Vs = Ks + BC * KP;
         // Branch-free step: in the masked blocks, keys past a wave's last
         // query are masked to zero.
-        {
+        if (has) {
             f32x16 s[NKT], dp[NKT];
             // S^T = K Q^T and dP^T = V dO^T with the K and V row reads kept
             // two products ahead, pinned in order by scheduling barriers.
@@ -333,10 +351,42 @@ void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
         __syncthreads();
     };
-    int kb = kb_begin;
-    for (; kb < ku_begin; ++kb) run_step(kb, std::true_type{});
-    for (; kb < ku_end; ++kb) run_step(kb, std::false_type{});
-    for (; kb < kb_end; ++kb) run_step(kb, std::true_type{});
+    if constexpr (KG == 1) {
+        int kb = kb_begin;
+        for (; kb < ku_begin; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::true_type{});
+        for (; kb < ku_end; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::false_type{});
+        for (; kb < kb_end; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::true_type{});
+    } else {
+        // Both groups step together (one barrier per step); group 0 has the
+        // same number of tiles as group 1 or one more.
+        const int nit = kmid - kb_begin;
+        for (int it = 0; it < nit; ++it) {
+            const int kb = gs + it;
+            const bool has = kb < ge;
+            if (has && (kb < ku_begin || kb >= ku_end))
+                run_step(kb, it & 1, ge - 1, true, std::true_type{});
+            else
+                run_step(kb, it & 1, ge - 1, has, std::false_type{});
+        }
+        // Group 1 adds its partial dQ^T to the wave of group 0 with the same
+        // rows, through the tile buffers (every wave has finished with them:
+        // each waited for its own loads before the last barrier).
+        constexpr int OSZ = WG * NDT * 16 * 64;
+        static_assert(OSZ * 4 <= 2 * KG * BUF * 2, "partial dQ must fit the tile buffers");
+        float* xs = reinterpret_cast<float*>(smem);
+        if (grp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xs[((gw * NDT + dt) * 16 + r) * 64 + lane] = dqacc[dt][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dqacc[dt][r] += xs[((gw * NDT + dt) * 16 + r) * 64 + lane];
+    }
 
     if (qrow < N) {
         e16* dqrow = static_cast<e16*>(p.dq) + b * p.sdq.b + hq * p.sdq.h + qrow * p.sdq.n;
@@ -355,12 +405,19 @@ void bwd_dq_kernel(BwdParams p) {
 
 template <int DT, int D, int MASK>
 static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
-    const long long nqb = (p.N + 127) / 128;
-    const dim3 grid((unsigned)(nqb * p.B * p.Hq)), block(256);
-    if (p.drop.thr != 0)
-        hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, false>), grid, block, 0, stream, p);
+    const dim3 block(256);
+    if (p.drop.thr != 0) {
+        const dim3 grid((unsigned)((p.N + 127) / 128 * p.B * p.Hq));
+        hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, true, 1>), grid, block, 0, stream, p);
+    } else if (D <= 128 && key_groups_pay(p.B, p.Hq, p.N, MASK != kMaskNone)) {
+        if constexpr (D <= 128) {
+            const dim3 grid((unsigned)((p.N + 63) / 64 * p.B * p.Hq));
+            hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, false, 2>), grid, block, 0, stream, p);
+        }
+    } else {
+        const dim3 grid((unsigned)((p.N + 127) / 128 * p.B * p.Hq));
+        hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, false, 1>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

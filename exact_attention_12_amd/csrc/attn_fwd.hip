@@ -823,19 +823,10 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
         return;
     }
     const int BC = FwdTile<D>::BLOCK_KV;
-    // Key groups: the longest query block walks nkb key tiles one after the
-    // other, while the average SIMD holds `load` wave steps (32-row tiles
-    // times their mean key tiles over the chip's 1024 SIMDs). When nkb is at
-    // least about twice the load, the longest blocks decide the kernel's
-    // time and splitting their keys over two groups of waves pays: measured
-    // 1.06-1.41x on grids of 256 to 1024 row tiles at ratios of 1.9 to 8,
-    // and 0.7-0.95x at ratios of 1 to 1.9.
+    // Key groups on grids too small to hide the longest query block's key
+    // loop (key_groups_pay).
     if (D <= 128 && !dropout) {
-        const int nkb = (N + BC - 1) / BC;
-        const double tiles32 = (double)((N + 31) / 32) * B * Hq;
-        const double mean_kb = causal ? (nkb + 1) / 2.0 : (double)nkb;
-        const double load = tiles32 * mean_kb / kSimds;
-        if (nkb >= 4 && nkb >= 1.9 * load) {
+        if (key_groups_pay(B, Hq, N, causal)) {
             plan->rows_per_wave = 32;
             plan->waves = 4;
             plan->key_groups = 2;

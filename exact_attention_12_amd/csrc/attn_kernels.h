@@ -172,8 +172,22 @@ struct FwdPlan {
     int key_groups;     // 2: the step-loop kernel with its 4 waves in two groups over one 64-row block's keys
 };
 
-// SIMDs of the part (256 compute units x 4), for the forward plan's load estimate.
+// SIMDs of the part (256 compute units x 4), for the load estimate below.
 constexpr int kSimds = 1024;
+
+// Whether a pass that walks each query block's 64-key tiles one after the
+// other should split every block's tiles over two groups of waves (the
+// forward and the dQ pass): when the longest block has at least about twice
+// as many tiles (nkb) as the average SIMD has wave steps (32-row tiles times
+// their mean key tiles over the chip's SIMDs), the longest blocks decide the
+// time. Measured on the forward: 1.06-1.41x at ratios of 1.9 to 8, 0.7-0.95x
+// at ratios of 1 to 1.9.
+inline bool key_groups_pay(int B, int Hq, int N, bool causal) {
+    const int nkb = (N + 63) / 64;
+    const double tiles32 = (double)((N + 31) / 32) * B * Hq;
+    const double mean_kb = causal ? (nkb + 1) / 2.0 : (double)nkb;
+    return nkb >= 4 && nkb >= 1.9 * tiles32 * mean_kb / kSimds;
+}
 
 // Key-split forward for short sequences: head dims up to kSplitMaxD, at most
 // kSplitMaxKeys keys (one 64-key tile per wave, 8 waves), used when the
