@@ -225,9 +225,12 @@ size_t row_terms_bytes(int B, int Hq, int N) {
     return (bytes + 255) & ~(size_t)255;
 }
 
-// fp32 partial dK and dV of the head-split dK/dV kernel, when a shape uses it.
+// fp32 partial dK and dV of the head-split or the query-split dK/dV kernel,
+// when a shape can use one (the query split's causal threshold covers the
+// unmasked one too).
 size_t partial_bytes(int B, int Hq, int Hkv, int N, int d) {
-    if (attn::dkdv_wide_split(B, Hq, Hkv, N, d) != 2) return 0;
+    if (attn::dkdv_wide_split(B, Hq, Hkv, N, d) != 2 && attn::dkdv_query_split(B, Hq, Hkv, N, d, true) != 2)
+        return 0;
     return 2 * 2 * (size_t)B * Hkv * N * d * sizeof(float);
 }
 
@@ -311,9 +314,18 @@ attn_status bwd_impl(const attn_problem* pr, const attn_tensor* q, const attn_te
     p.dkdv = attn::dkdv_wide_split(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d);
     if (no_alloc && p.dkdv == 2) p.dkdv = 0;
     p.hsplit = p.dkdv == 2 ? 2 : 1;
-    p.part = p.hsplit == 2 ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
-                                                      2 * row_terms_bytes(pr->B, pr->Hq, pr->N))
-                           : nullptr;
+    // The query split of the 32-key kernel; in the fixed scratch only when
+    // its partials fit beside the row terms.
+    p.qsplit = 1;
+    if (p.dkdv == 0 && attn::dkdv_query_split(pr->B, pr->Hq, pr->Hkv, pr->N, pr->d, mask != attn::kMaskNone) == 2) {
+        const size_t need = 2 * row_terms_bytes(pr->B, pr->Hq, pr->N) +
+                            2 * 2 * (size_t)pr->B * pr->Hkv * pr->N * pr->d * sizeof(float);
+        if (!no_alloc || need <= kScratchBytes) p.qsplit = 2;
+    }
+    p.part = (p.hsplit == 2 || p.qsplit == 2)
+                 ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                            2 * row_terms_bytes(pr->B, pr->Hq, pr->N))
+                 : nullptr;
     p.sq = strides_of(or_none(q, main));
     p.sk = strides_of(or_none(k, main));
     p.sv = strides_of(or_none(v, main));

@@ -77,7 +77,7 @@ void bwd_pre_kernel(BwdParams p, long long rows) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int DT, int D, int MASK, bool DROP>
+template <int DT, int D, int MASK, bool DROP, int QS>
 __global__ __launch_bounds__(256, 1)
 void bwd_dkdv_kernel(BwdParams p) {
     constexpr bool CAUSAL = MASK != kMaskNone;
@@ -88,8 +88,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int BQ = (D <= 128) ? 64 : 32;  // queries per step
     constexpr int NQT = BQ / 32;
     // d = 32: the compiler sinks part of the P / dS packing past the region
-    // gaps, so every dV/dK product carries its own two wait states.
-    constexpr bool ACC_GAP = D <= 32;
+    // gaps, and in the query-split kernels it moves accumulator tiles between
+    // AGPRs right before their product: there every dV/dK product carries its
+    // own two wait states.
+    constexpr bool ACC_GAP = D <= 32 || QS == 2;
     constexpr int PVS = BQ / 16;
     constexpr int KS = D / 16;
     constexpr int NDT = (D + 31) / 32;
@@ -106,10 +108,14 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int h = lane >> 5;
     const int N = p.N;
 
+    // Workgroup index: key block (ascending: heaviest first when causal),
+    // then the part of its query range (QS parts), then the KV head, fastest.
     const int BHk = p.B * p.Hkv;
     const int bid = blockIdx.x;
-    const int kb = bid / BHk;           // ascending key blocks: heaviest first when causal
-    const int bhk = bid - kb * BHk;
+    const int kb = bid / (BHk * QS);
+    const int rem = bid - kb * BHk * QS;
+    const int part = QS == 1 ? 0 : rem / BHk;
+    const int bhk = rem - part * BHk;
     const int b = bhk / p.Hkv;
     const int hkv = bhk - b * p.Hkv;
     const int k0 = kb * BK;
@@ -143,12 +149,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 
     const int nqb = (N + BQ - 1) / BQ;
-    const int qb_start = CAUSAL ? (k0 / BQ) : 0;
+    int qb_start = CAUSAL ? (k0 / BQ) : 0;
     // Sliding window: only queries i <= (last key) + window - 1 see this block.
     const int W = WINDOW ? p.window : 0;
-    const int qb_stop = WINDOW ? min(nqb, (k0 + BK - 1 + W - 1) / BQ + 1) : nqb;
-    const int nq_iter = qb_stop - qb_start;
-    const int total = p.G * nq_iter;
+    int qb_stop = WINDOW ? min(nqb, (k0 + BK - 1 + W - 1) / BQ + 1) : nqb;
     // Query blocks that need no per-element mask form [qu_begin, qu_end):
     // every query is at or after every key of the workgroup (q0 >= k0 + BK
     // - 1) and, under a window, every key lies in every query's band
@@ -162,6 +166,18 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int t = k0 + W - BQ;
         qu_end = max(qu_begin, min(qb_stop, t >= 0 ? t / BQ + 1 : 0));
     }
+    if constexpr (QS == 2) {
+        // This workgroup's part of the query range: the first or the second
+        // half of its blocks (the masked ones keep their classification).
+        const int mid = qb_start + (qb_stop - qb_start + 1) / 2;
+        const int lo = part == 0 ? qb_start : mid, hi = part == 0 ? mid : qb_stop;
+        qb_start = lo;
+        qb_stop = hi;
+        qu_begin = min(max(qu_begin, lo), hi);
+        qu_end = min(max(qu_end, qu_begin), hi);
+    }
+    const int nq_iter = qb_stop - qb_start;
+    const int total = p.G * nq_iter;
     const int nu = qu_end - qu_begin;
     const int nmG = p.G * (nq_iter - nu);
     // Step cursor (head g of the group, query block qb), advanced with a few
@@ -615,6 +631,29 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int dt = 0; dt < NDT; ++dt) {
         agpr_acc_ready(dkacc[dt]);
         agpr_acc_ready(dvacc[dt]);
+    }
+    if constexpr (QS > 1) {
+        // fp32 partial sums [2][QS][B][Hkv][N][D]: dK (scaled), then dV
+        if (key < N) {
+            const float sc = p.scale;
+            const size_t plane = (size_t)QS * BHk * N * D;
+            float* pk = p.part + (((size_t)part * BHk + bhk) * N + key) * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = dt * 32 + g4 * 8 + h * 4;
+                    if (d < D) {
+                        *reinterpret_cast<f32x4*>(pk + d) =
+                            f32x4{dkacc[dt][g4 * 4 + 0] * sc, dkacc[dt][g4 * 4 + 1] * sc,
+                                  dkacc[dt][g4 * 4 + 2] * sc, dkacc[dt][g4 * 4 + 3] * sc};
+                        *reinterpret_cast<f32x4*>(pk + plane + d) =
+                            f32x4{dvacc[dt][g4 * 4 + 0], dvacc[dt][g4 * 4 + 1], dvacc[dt][g4 * 4 + 2],
+                                  dvacc[dt][g4 * 4 + 3]};
+                    }
+                }
+        }
+        return;
     }
     if (key < N) {
         e16* dkrow = static_cast<e16*>(p.dk) + b * p.sdk.b + hkv * p.sdk.h + key * p.sdk.n;
@@ -1096,13 +1135,13 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
     }
 }
 
-// Sum of the two partial dK, dV of the head-split dK/dV kernel (in part
-// order, so the result is deterministic), converted to the element type.
-// One thread per 4 elements of a row.
-template <int DT>
+// Sum of the two partial dK, dV of the head-split 64-key dK/dV kernel or of
+// the query-split 32-key one (in part order, so the result is
+// deterministic), converted to the element type. One thread per 4 elements
+// of a row.
+template <int DT, int D>
 __global__ __launch_bounds__(256)
 void bwd_dkdv_sum_kernel(BwdParams p, long long quads) {
-    constexpr int D = 128;
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= quads) return;
     const long long row = i / (D / 4);
@@ -1152,7 +1191,7 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
                 if (e != hipSuccess) return e;
                 if (p.hsplit == 2) {
                     const long long quads = (long long)p.B * p.Hkv * p.N * (D / 4);
-                    hipLaunchKernelGGL((bwd_dkdv_sum_kernel<DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256),
+                    hipLaunchKernelGGL((bwd_dkdv_sum_kernel<DT, D>), dim3((unsigned)((quads + 255) / 256)), dim3(256),
                                        0, stream, p, quads);
                     e = hipGetLastError();
                     if (e != hipSuccess) return e;
@@ -1163,13 +1202,33 @@ static hipError_t launch_bwd_dc(const BwdParams& p, int passes, hipStream_t stre
     }
     if (passes & kBwdDkDv) {
         const long long nkb = (p.N + 127) / 128;
-        const dim3 grid((unsigned)(nkb * p.B * p.Hkv)), block(256);
-        if (p.drop.thr != 0)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, false>), grid, block, 0, stream, p);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        const dim3 block(256);
+        if (p.qsplit == 2) {
+            if constexpr (D <= 128) {
+                const dim3 grid((unsigned)(nkb * p.B * p.Hkv * 2));
+                if (p.drop.thr != 0)
+                    hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, true, 2>), grid, block, 0, stream, p);
+                else
+                    hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, false, 2>), grid, block, 0, stream, p);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                const long long quads = (long long)p.B * p.Hkv * p.N * (D / 4);
+                hipLaunchKernelGGL((bwd_dkdv_sum_kernel<DT, D>), dim3((unsigned)((quads + 255) / 256)), block, 0,
+                                   stream, p, quads);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            } else {
+                return hipErrorInvalidValue;  // the split is planned for d <= 128 only
+            }
+        } else {
+            const dim3 grid((unsigned)(nkb * p.B * p.Hkv));
+            if (p.drop.thr != 0)
+                hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, true, 1>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, MASK, false, 1>), grid, block, 0, stream, p);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     if (passes & kBwdDq) {
         const hipError_t e = launch_bwd_dq(p, DT, D, MASK, stream);

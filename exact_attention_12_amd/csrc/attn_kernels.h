@@ -131,9 +131,10 @@ struct BwdParams {
     void* dv;
     float* delta;  // [B, Hq, N] workspace: -D_i = -<dO_i, O_i>
     float* lse2;   // [B, Hq, N] workspace: LSE_i * log2(e), written with D_i
-    float* part;   // [2, hsplit, B, Hkv, N, 128] workspace: partial dK, dV (hsplit 2 only)
+    float* part;   // [2, 2, B, Hkv, N, d] workspace: partial dK, dV (hsplit or qsplit 2 only)
     int dkdv;      // dK/dV kernel (dkdv_wide_split's numbering; 1 and 2 only at d = 128)
     int hsplit;    // workgroups per 256-key block of the 64-key dK/dV kernel (2 iff dkdv == 2)
+    int qsplit;    // workgroups per 128-key block of the 32-key dK/dV kernel, each over a part of its queries
     Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
     int N;
     int Hq;
@@ -158,6 +159,18 @@ inline int dkdv_wide_split(int B, int Hq, int Hkv, int N, int d) {
     if (n4 >= 512) return 1;
     if ((Hq / Hkv) % 2 == 0 && 2 * n4 >= 512) return 2;
     return 0;
+}
+
+// Query split of the 32-key dK/dV kernel (d <= 128, where neither 64-key
+// form is used): when its grid of 128-key blocks holds at most one workgroup
+// per CU (causal; half that unmasked, where every block has the same work),
+// the heaviest block's query loop decides the time. Two workgroups per block
+// then each take half of its query blocks and write fp32 partial dK, dV,
+// which a second kernel adds. 1 or 2.
+inline int dkdv_query_split(int B, int Hq, int Hkv, int N, int d, bool causal) {
+    if (d > 128 || Hkv <= 0 || N < 512 || dkdv_wide_split(B, Hq, Hkv, N, d) != 0) return 1;
+    const long long wgs = (long long)((N + 127) / 128) * B * Hkv;
+    return wgs <= (causal ? 256 : 128) ? 2 : 1;
 }
 
 struct FwdPlan {

@@ -124,11 +124,14 @@ attn_status attn_fwd_window(const void* q, const void* k, const void* v, void* o
 /*
  * Bytes of device workspace attn_bwd needs: two float32 per query row, the
  * row term D_i = <dO_i, O_i> (stored negated) and the LSE in base 2, each
- * array rounded up to 256 bytes. For d = 128 when B * Hkv * ceil(N / 256) is
- * between 256 and 511 and Hq / Hkv is even, the dK/dV pass splits the query
- * heads of each group over two workgroups and also keeps their float32
- * partial dK and dV: 2 * 2 * B * Hkv * N * 128 * 4 more bytes. Returns 0 if
- * the shape is invalid.
+ * array rounded up to 256 bytes. Two kinds of shapes also keep float32
+ * partial dK and dV of two workgroups per key block, 2 * 2 * B * Hkv * N * d
+ * * 4 more bytes: d = 128 when B * Hkv * ceil(N / 256) is between 256 and
+ * 511 and Hq / Hkv is even (the query heads of each group split over two
+ * workgroups), and, among the other shapes with d <= 128 and N >= 512, those
+ * with B * Hkv * ceil(N / 128) <= 256 (each key block's query range split
+ * over two workgroups; taken for the causal and window masks, and for no
+ * mask at <= 128). Returns 0 if the shape is invalid.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
@@ -166,7 +169,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * over from a previous call. Calls that overlap on one GPU (concurrent
  * streams, or threads) share the one array and race: serialise them.
  * Shapes for which attn_bwd sums two fp32 halves of dK/dV in its workspace
- * use a single-pass dK/dV kernel here, so dK and dV may differ from
+ * do the same here when the halves fit in the array beside the row terms,
+ * else use a single-pass dK/dV kernel, whose dK and dV may differ from
  * attn_bwd's in the last bits; everything else is bitwise identical.
  */
 attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,

@@ -128,6 +128,14 @@ def test_workspace_bytes(L):
     assert L.attn_bwd_workspace_bytes(1, 64, 8, 8192, 64) == 2 * 64 * 8192 * 4
     assert L.attn_bwd_workspace_bytes(1, 8, 8, 8192, 128) == 2 * 8 * 8192 * 4  # G = 1: no split
     assert L.attn_bwd_workspace_bytes(1, 3, 2, 100, 80) == 0
+    # small grids (B * Hkv * ceil(N / 128) <= 256, N >= 512, d <= 128, no
+    # 64-key form): two workgroups per 128-key block, fp32 partials
+    rt = lambda B, Hq, N: 2 * (-(-B * Hq * N * 4 // 256) * 256)
+    assert L.attn_bwd_workspace_bytes(1, 2, 2, 4096, 128) == rt(1, 2, 4096) + 2 * 2 * 2 * 4096 * 128 * 4
+    assert L.attn_bwd_workspace_bytes(1, 4, 4, 4096, 80) == rt(1, 4, 4096) + 2 * 2 * 4 * 4096 * 80 * 4
+    assert L.attn_bwd_workspace_bytes(1, 16, 16, 4096, 80) == rt(1, 16, 4096)   # 512 blocks: none
+    assert L.attn_bwd_workspace_bytes(1, 4, 4, 511, 64) == rt(1, 4, 511)        # N < 512: none
+    assert L.attn_bwd_workspace_bytes(1, 2, 2, 4096, 192) == rt(1, 2, 4096)     # d > 128: none
     assert L.attn_bwd_workspace_bytes(1, 2, 2, 100, 112) == 0
 
 
