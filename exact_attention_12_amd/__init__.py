@@ -10,6 +10,7 @@ If the library is missing or fails to load, every call raises.
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
     o, lse = fwd(q, k, v, window=256)               # sliding window i-256 < j <= i
     o, lse = fwd(q, k, v, layout="bshd")            # [B, N, H, d] tensors, read in place
+    o = attention(q, k, v, causal=True)             # differentiable: o.backward() runs bwd
 
 Tensors are bf16 or fp16 (all of one call alike), 4-D, innermost dim
 contiguous; `layout` says whether dims 1 and 2 are (H, N) ("bhsd", default) or
@@ -448,6 +449,55 @@ def bwd_passes(q, k, v, o, lse, do, dq, dk, dv, workspace, *, scale=None, causal
     if layout == "bshd":
         return tuple(t.transpose(1, 2) for t in outs)
     return dqv, dkv, dvv
+
+
+_ATTENTION_FN = None
+
+
+def _attention_fn():
+    """The torch.autograd.Function behind attention(), built on first use (the
+    module itself does not import torch)."""
+    global _ATTENTION_FN
+    if _ATTENTION_FN is None:
+        import torch
+
+        class AttentionFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal, window, layout, dropout_p, seed, offset):
+                o, lse = fwd(q, k, v, scale=scale, causal=causal, window=window, layout=layout,
+                             dropout_p=dropout_p, seed=seed, offset=offset)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.args = (scale, causal, window, layout, dropout_p, seed, offset)
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                scale, causal, window, layout, dropout_p, seed, offset = ctx.args
+                # the incoming gradient may be a broadcast or otherwise strided view
+                dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), scale=scale, causal=causal,
+                                 window=window, layout=layout, dropout_p=dropout_p, seed=seed,
+                                 offset=offset)
+                return dq, dk, dv, None, None, None, None, None, None, None
+
+        _ATTENTION_FN = AttentionFn
+    return _ATTENTION_FN
+
+
+def attention(q, k, v, *, scale=None, causal=False, window=None, layout="bhsd", dropout_p=0.0,
+              seed=None, offset=0):
+    """Differentiable attention: fwd() as a torch autograd function whose
+    backward is bwd() (the same kernels, nothing recomputed on the host).
+    Arguments as for fwd(); returns O only (the LSE is kept for the backward).
+    With dropout_p > 0 and no seed, a seed is drawn from torch's default
+    generator, and the backward redraws the same keep mask from it."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    if dropout_p and seed is None:
+        import torch
+        seed = int(torch.randint(0, 2 ** 31 - 1, (1,)).item())
+    return _attention_fn().apply(q, k, v, float(scale), causal, window, layout, float(dropout_p),
+                                 0 if seed is None else int(seed), int(offset))
 
 
 def _decode_problem(B, Hq, Hkv, Nq, Nk, d, scale, causal, window, dtype):
