@@ -62,13 +62,19 @@ def test_window_fwd_bwd(cfg):
     parity.check_bwd(inp, grads, scale, True, kv_heads, Hq, Hkv, ids(cfg), window=W)
 
 
-def test_window_covering_the_sequence_is_the_causal_mask():
+@pytest.mark.parametrize("shape", [
+    (1, 4, 2, 333, 128),   # key groups in the forward and dQ
+    (1, 4, 2, 1000, 64),   # also the query split in dK/dV (ragged last block)
+    (1, 64, 8, 1000, 80),  # one group, one part
+])
+def test_window_covering_the_sequence_is_the_causal_mask(shape):
     """A band of N or more keys allows every j <= i: outputs are bit-identical
-    to the causal call."""
-    inp = parity.to_gpu(si.make_inputs(1, 4, 2, 333, 128, seed=41, with_do=True))
+    to the causal call, on every plan."""
+    N = shape[3]
+    inp = parity.to_gpu(si.make_inputs(*shape, seed=41, with_do=True))
     o_c, l_c = ea.fwd(inp["q"], inp["k"], inp["v"], causal=True)
     g_c = ea.bwd(inp["q"], inp["k"], inp["v"], o_c, l_c, inp["do"], causal=True)
-    for W in (333, 334, 1 << 20):
+    for W in (N, N + 1, 1 << 20):
         o_w, l_w = ea.fwd(inp["q"], inp["k"], inp["v"], window=W)
         g_w = ea.bwd(inp["q"], inp["k"], inp["v"], o_w, l_w, inp["do"], window=W)
         torch.cuda.synchronize()
