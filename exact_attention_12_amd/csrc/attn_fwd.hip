@@ -57,6 +57,9 @@
 //    combine exactly: M = max(m0, m1), l = sum_g 2^(m_g - M) l_g,
 //    O = sum_g 2^(m_g - M) O_g. (Two groups of 4 waves over 128 rows, two
 //    waves per SIMD, gained nothing: the groups then share each SIMD.)
+//  * d = 128 without dropout, one key group: fwd_m16_kernel runs the same
+//    step loop on 16x16x32 products (layout in its own comment), which the
+//    chip sustains at a higher clock than 32x32x16 ones.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -508,6 +511,332 @@ void fwd_kernel(FwdParams p) {
     }
 }
 
+// ------------------------------------------------------------------
+// d = 128 without dropout: the same step loop on 16x16x32 products.
+//
+// The chip sustains v_mfma_f32_16x16x32_bf16 at a higher clock than the
+// 32x32x16 product on the same random operands (the matrix cores are equally
+// busy, the power limit lets the clock stay ~12 % higher), so for the
+// product-heavy d = 128 loop the wave's work is cut into 16x16 tiles:
+//  * 16x16x32 operands and result (wave64): A[16x32]: lane l holds row l % 16,
+//    k = 8 (l / 16) .. +7; B[32x16]: lane l holds column l % 16, the same k;
+//    D[16x16]: lane l, register r holds D[4 (l / 16) + r][l % 16].
+//  * S^T = K Q^T per 64-key step: 4 key tiles x 2 query tiles of 16, 4
+//    contraction steps of 32 dims. A K operand (one 16-byte LDS row read)
+//    serves both query tiles. A lane then holds, for queries qw0 + l % 16 and
+//    qw0 + 16 + l % 16, keys 16 kt + 4 (l / 16) + r: the row maximum and sum
+//    combine the lane's 16 values and then the four 16-lane groups (two
+//    lane-swap steps).
+//  * O^T += V^T P^T over two 32-key halves: B element i of lane group g is
+//    key 4g + i (i < 4) or 16 + 4g + i - 4 (i >= 4) of the half, which is
+//    exactly what the lane holds of s[2 jj] and s[2 jj + 1], so the
+//    probabilities are packed in place. The V^T operand takes the same key
+//    order: two transposing reads of 4 keys (rows 4g .. 4g+3 and 16 + 4g ..)
+//    by 16 dims. O^T is 8 x 2 tiles of 16x16, one query per lane column.
+//  * The V tile pitch is an odd multiple of 32 bytes modulo 256: the two
+//    16-lane groups served together read 8 rows at one column block, which
+//    then land on 8 different 32-byte bank groups.
+// Everything else (online softmax with the lazy reference maximum, tile
+// loads straight to LDS, causal/window skipping, launch order) is the step
+// loop of fwd_kernel.
+constexpr int v16_pitch(int d) { return ((2 * d / 32) % 2 == 1 ? 2 * d : 2 * d + 32) / 2; }
+static_assert(v16_pitch(128) == 144 && (v16_pitch(128) * 2 / 32) % 2 == 1, "");
+// Head dims whose no-dropout step loop runs on 16x16x32 products (d = 64
+// is bound by its softmax work, where the two query tiles per lane cost more
+// than the products gain).
+template <int D> constexpr bool kProducts16 = D == 128;
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(e16x8 a, e16x8 b, f32x4 c) {
+    if constexpr (DT == kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Lanes l, l ^ 16, l ^ 32 and l ^ 48 combine a value (v_permlane32_swap,
+// then v_permlane16_swap).
+__device__ __forceinline__ float max_across_quarters(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum_across_quarters(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+template <int DT, int D, int MASK, int NW>
+__global__ __launch_bounds__(NW * 64, 2)
+void fwd_m16_kernel(FwdParams p) {
+    constexpr int BQ = NW * 32;
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
+    constexpr int BC = 64;
+    constexpr int KS = D / 32;   // contraction steps of S^T = K Q^T
+    constexpr int NDT = D / 16;  // 16-row tiles of O^T
+    constexpr int KP = k_pitch(D);
+    constexpr int VP = v16_pitch(D);
+    constexpr int CPR = D / 8;
+    constexpr int BUF = BC * (KP + VP);
+    static_assert(D % 32 == 0 && D <= 128 && FwdTile<D>::BLOCK_KV == BC, "16x16x32 step loop: 64-key tiles");
+
+    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int g = lane >> 4;  // 16-lane group
+    const int N = p.N;
+
+    const int bid = blockIdx.x;
+    const int bh = xcd_head(bid % p.BH, p.BH);
+    const int qb = causal_block(bid / p.BH, p.nqb, NW == 4 && gridDim.x <= 512, CAUSAL);
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hkv = hq / p.G;
+
+    const e16* Qh = static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h;
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
+    const long long sqn = p.sq.n, skn = p.sk.n, svn = p.sv.n;
+
+    const int q0 = qb * BQ;
+    const int qw0 = q0 + wave * 32;
+    const int qrow0 = qw0 + l16, qrow1 = qw0 + 16 + l16;
+
+    // Q operand (B of S^T): query qw0 + 16 qt + l16, dims 32 ks + 8 g .. +7.
+    e16x8 qf[2][KS];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qr = qt ? qrow1 : qrow0;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qt][ks] = qr < N ? *reinterpret_cast<const e16x8*>(Qh + qr * sqn + ks * 32 + g * 8) : e16x8{};
+    }
+
+    const int nkb = (N + BC - 1) / BC;
+    const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
+    const int W = WINDOW ? p.window : 0;
+    const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
+
+    // Tiles go straight from memory to LDS, as in fwd_kernel.
+    constexpr int CKK = KP / 8, CKV = VP / 8;
+    constexpr int NLK = BC * CKK / 64, NLV = BC * CKV / 64;
+    constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
+    static_assert(BC * CKK % 64 == 0 && BC * CKV % 64 == 0, "tile must be whole loads");
+    uint32_t offk[LPWK], offv[LPWV];
+    {
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKK, ch = chunk - row * CKK;
+            offk[i] = ch < CPR ? (uint32_t)row * sk2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKV, ch = chunk - row * CKV;
+            offv[i] = ch < CPR ? (uint32_t)row * sv2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+        }
+    }
+    auto issue_tile = [&](int kv0, int bufi) {
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
+        char* kb_lds = reinterpret_cast<char*>(smem + bufi * BUF);
+        char* vb_lds = kb_lds + BC * KP * 2;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int j = wave + i * NW;
+            if (NLK % NW == 0 || j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int j = wave + i * NW;
+            if (NLV % NW == 0 || j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
+        }
+    };
+    issue_tile(kb_begin * BC, kb_begin & 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    f32x4 oacc[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4{};
+    float m[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};  // per query tile, log2 domain
+    float l[2] = {0.0f, 0.0f};
+    const float c = p.c;
+    // Transposing V read: lane 4t+s of group g addresses key row 4g + t, dims 4s .. 4s+3.
+    const int v_row = 4 * g + (l16 >> 2);
+    const int v_col = 4 * (l16 & 3);
+
+    auto run_step = [&](int kb, int bufi, int kb_last, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        issue_tile(min(kb + 1, kb_last) * BC, bufi ^ 1);
+        const int kv0 = kb * BC;
+        const e16* Ks = smem + bufi * BUF;
+        const e16* Vs = Ks + BC * KP;
+        const bool active = !MASKED || !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
+        if (active) {
+            // s[kt][qt][r]: key kv0 + 16 kt + 4 g + r, query qw0 + 16 qt + l16.
+            f32x4 s[4][2];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s[kt][0] = s[kt][1] = f32x4{};
+            constexpr int NS = 4 * KS;
+            e16x8 kr[3];
+            auto rdk = [&](int idx) {
+                const int ks = idx / 4, kt = idx % 4;
+                kr[idx % 3] = lds_read8(Ks + (kt * 16 + l16) * KP + ks * 32 + g * 8);
+            };
+            rdk(0);
+            rdk(1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int idx = 0; idx < NS; ++idx) {
+                if (idx + 2 < NS) rdk(idx + 2);
+                const int ks = idx / 4, kt = idx % 4;
+                s[kt][0] = mfma16<DT>(kr[idx % 3], qf[0][ks], s[kt][0]);
+                s[kt][1] = mfma16<DT>(kr[idx % 3], qf[1][ks], s[kt][1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const bool need_mask = MASKED && ((CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N) ||
+                                              (WINDOW && kv0 < qw0 + 32 - W));
+            if (need_mask) {
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const int qr = qt ? qrow1 : qrow0;
+                    const int hi = (CAUSAL ? min(qr, N - 1) : N - 1) - kv0 - 4 * g;
+                    const int lo = (WINDOW ? qr - W + 1 : 0) - kv0 - 4 * g;
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int koff = kt * 16 + r;
+                            s[kt][qt][r] = (koff > hi || koff < lo) ? -__builtin_huge_valf() : s[kt][qt][r];
+                        }
+                }
+            }
+            // Lazy rescaling, per query tile, as in fwd_kernel.
+            float mb[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                float mx = s[0][qt][0];
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][qt][r]);
+                mb[qt] = max_across_quarters(mx) * c;
+                if (m[qt] == -__builtin_huge_valf()) m[qt] = mb[qt];
+            }
+            if (__any(mb[0] > m[0] + 8.0f || mb[1] > m[1] + 8.0f)) {
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const float m_new = fmaxf(m[qt], mb[qt]);
+                    const float alpha = (m_new == -__builtin_huge_valf()) ? 1.0f : fast_exp2(m[qt] - m_new);
+                    m[qt] = m_new;
+                    l[qt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) oacc[dt][qt] *= alpha;
+                }
+            }
+            const float mn0 = (m[0] == -__builtin_huge_valf()) ? 0.0f : m[0];
+            const float mn1 = (m[1] == -__builtin_huge_valf()) ? 0.0f : m[1];
+            float lsum0 = 0.0f, lsum1 = 0.0f;
+            // Probability e (0..15) of key half jj: query tile e / 8, B element
+            // i = e % 8, i.e. register i % 4 of s[2 jj + i / 4].
+            float pe[2][16];
+            auto exp1 = [&](int jj, int e) {
+                const int qt = e >> 3, i = e & 7;
+                const float x = fast_exp2(fmaf(s[2 * jj + (i >> 2)][qt][i & 3], c, qt ? -mn1 : -mn0));
+                if (qt)
+                    lsum1 += x;
+                else
+                    lsum0 += x;
+                pe[jj][e] = x;
+            };
+            auto pack = [&](int jj, int qt) {
+                const float* x = &pe[jj][qt * 8];
+                return cat8(cvt2<DT>(x[0], x[1]), cvt2<DT>(x[2], x[3]), cvt2<DT>(x[4], x[5]), cvt2<DT>(x[6], x[7]));
+            };
+            auto v_op = [&](int idx) {
+                const int jj = idx / NDT, dt = idx % NDT;
+                const e16* vp = Vs + (jj * 32 + v_row) * VP + v_col + dt * 16;
+                return join8(lds_read_tr4(vp), lds_read_tr4(vp + 16 * VP));
+            };
+            // The first half's probabilities, then its products with the
+            // second half's exponentials in their shadow; V^T fragments are
+            // read two ahead.
+            constexpr int NP = 2 * NDT;
+            constexpr int EPD = (16 + NDT - 1) / NDT;  // exponentials per first-half fragment
+            e16x8 va[3];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) exp1(0, e);
+            e16x8 pb[2][2];
+            pb[0][0] = pack(0, 0);
+            pb[0][1] = pack(0, 1);
+            va[0] = v_op(0);
+            va[1] = v_op(1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int idx = 0; idx < NP; ++idx) {
+                const int jj = idx / NDT, dt = idx % NDT;
+                if (idx + 2 < NP) va[(idx + 2) % 3] = v_op(idx + 2);
+                oacc[dt][0] = mfma16<DT>(va[idx % 3], pb[jj][0], oacc[dt][0]);
+                oacc[dt][1] = mfma16<DT>(va[idx % 3], pb[jj][1], oacc[dt][1]);
+                if (jj == 0) {
+#pragma unroll
+                    for (int j = 0; j < EPD; ++j)
+                        if (dt * EPD + j < 16) exp1(1, dt * EPD + j);
+                    if (dt == NDT - 1) {
+                        pb[1][0] = pack(1, 0);
+                        pb[1][1] = pack(1, 1);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            l[0] += lsum0;
+            l[1] += lsum1;
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
+        __syncthreads();
+    };
+    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
+    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
+    if (WINDOW) {
+        const int t = q0 + BQ - W;
+        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
+    }
+    ku_end = max(ku_end, ku_begin);
+    int kb = kb_begin;
+    for (; kb < ku_begin; ++kb) run_step(kb, kb & 1, kb_end - 1, std::true_type{});
+    for (; kb < ku_end; ++kb) run_step(kb, kb & 1, kb_end - 1, std::false_type{});
+    for (; kb < kb_end; ++kb) run_step(kb, kb & 1, kb_end - 1, std::true_type{});
+
+    // Epilogue: the four 16-lane groups' row sums, then O and LSE.
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qr = qt ? qrow1 : qrow0;
+        const float lt = sum_across_quarters(l[qt]);
+        const float inv = 1.0f / lt;
+        if (qr < N) {
+            e16* orow = static_cast<e16*>(p.o) + b * p.so.b + hq * p.so.h + qr * p.so.n;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                store4<DT>(orow + dt * 16 + 4 * g, oacc[dt][qt][0] * inv, oacc[dt][qt][1] * inv,
+                           oacc[dt][qt][2] * inv, oacc[dt][qt][3] * inv);
+            if (g == 0) p.lse[(size_t)bh * N + qr] = (m[qt] + log2f(lt)) * kLn2;
+        }
+    }
+}
+
 // Short sequences (at most kSplitMaxKeys keys, small grids): the keys of one
 // 32-row query tile are split over the workgroup's waves, one 64-key tile
 // each. Every wave issues all of its loads at once (its K tile straight into
@@ -755,6 +1084,16 @@ static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStr
                 return hipGetLastError();
             }
         }
+        if constexpr (kProducts16<D> && !DROP) {
+            if (plan.key_groups != 1) return hipErrorInvalidValue;
+            if (plan.waves == 8)
+                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p);
+            else if (plan.waves == 4)
+                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 4>), grid, block, 0, stream, p);
+            else
+                return hipErrorInvalidValue;
+            return hipGetLastError();
+        }
         if (plan.waves == 8) {
             hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP, 1>), grid, block, 0, stream, p);
             return hipGetLastError();
@@ -846,7 +1185,7 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
     plan->block_kv = BC;
     plan->threads = waves * 64;
     plan->workgroups = (long long)((N + BQ - 1) / BQ) * B * Hq;
-    plan->lds_bytes = 2 * BC * (k_pitch(D) + v_pitch(D)) * 2;
+    plan->lds_bytes = 2 * BC * (k_pitch(D) + (kProducts16<D> && !dropout ? v16_pitch(D) : v_pitch(D))) * 2;
 }
 
 bool fwd_plan(int B, int Hq, int N, int d, bool causal, bool dropout, FwdPlan* plan) {
