@@ -57,9 +57,9 @@
 //    combine exactly: M = max(m0, m1), l = sum_g 2^(m_g - M) l_g,
 //    O = sum_g 2^(m_g - M) O_g. (Two groups of 4 waves over 128 rows, two
 //    waves per SIMD, gained nothing: the groups then share each SIMD.)
-//  * d = 128 without dropout, one key group: fwd_m16_kernel runs the same
-//    step loop on 16x16x32 products (layout in its own comment), which the
-//    chip sustains at a higher clock than 32x32x16 ones.
+//  * d = 128 without dropout on the 8-wave plan: fwd_m16_kernel runs the
+//    same step loop on 16x16x32 products (layout in its own comment), which
+//    the chip sustains at a higher clock than 32x32x16 ones.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -512,7 +512,7 @@ void fwd_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------
-// d = 128 without dropout: the same step loop on 16x16x32 products.
+// d = 128 without dropout, 8 waves: the same step loop on 16x16x32 products.
 //
 // The chip sustains v_mfma_f32_16x16x32_bf16 at a higher clock than the
 // 32x32x16 product on the same random operands (the matrix cores are equally
@@ -541,9 +541,10 @@ void fwd_kernel(FwdParams p) {
 // loop of fwd_kernel.
 constexpr int v16_pitch(int d) { return ((2 * d / 32) % 2 == 1 ? 2 * d : 2 * d + 32) / 2; }
 static_assert(v16_pitch(128) == 144 && (v16_pitch(128) * 2 / 32) % 2 == 1, "");
-// Head dims whose no-dropout step loop runs on 16x16x32 products (d = 64
-// is bound by its softmax work, where the two query tiles per lane cost more
-// than the products gain).
+// Head dims whose no-dropout 8-wave step loop runs on 16x16x32 products.
+// (d = 64 is bound by its softmax work, where the two query tiles per lane
+// cost more than the products gain; so are the 4-wave plans of small grids,
+// which stay on fwd_kernel.)
 template <int D> constexpr bool kProducts16 = D == 128;
 
 template <int DT>
@@ -724,27 +725,40 @@ void fwd_m16_kernel(FwdParams p) {
                         }
                 }
             }
-            // Lazy rescaling, per query tile, as in fwd_kernel.
-            float mb[2];
+            // Lazy rescaling, per query tile, as in fwd_kernel. The reference
+            // maximum m is the same in the four 16-lane groups of a query, so
+            // when no lane's own maximum exceeds m + 8 (log2 units) neither
+            // does the row's, and the step keeps m without combining the
+            // groups' maxima; only then (or while m is still -inf) are they
+            // combined and the rescale decided as in fwd_kernel.
+            float mx[2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                float mx = s[0][qt][0];
+                mx[qt] = s[0][qt][0];
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][qt][r]);
-                mb[qt] = max_across_quarters(mx) * c;
-                if (m[qt] == -__builtin_huge_valf()) m[qt] = mb[qt];
+                    for (int r = 0; r < 4; ++r) mx[qt] = fmaxf(mx[qt], s[kt][qt][r]);
             }
-            if (__any(mb[0] > m[0] + 8.0f || mb[1] > m[1] + 8.0f)) {
+            const bool moves = mx[0] * c > m[0] + 8.0f || mx[1] * c > m[1] + 8.0f ||
+                               m[0] == -__builtin_huge_valf() || m[1] == -__builtin_huge_valf();
+            if (__any(moves)) {
+                float mb[2];
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
-                    const float m_new = fmaxf(m[qt], mb[qt]);
-                    const float alpha = (m_new == -__builtin_huge_valf()) ? 1.0f : fast_exp2(m[qt] - m_new);
-                    m[qt] = m_new;
-                    l[qt] *= alpha;
+                    mb[qt] = max_across_quarters(mx[qt]) * c;
+                    if (m[qt] == -__builtin_huge_valf()) m[qt] = mb[qt];
+                }
+                if (__any(mb[0] > m[0] + 8.0f || mb[1] > m[1] + 8.0f)) {
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) oacc[dt][qt] *= alpha;
+                    for (int qt = 0; qt < 2; ++qt) {
+                        const float m_new = fmaxf(m[qt], mb[qt]);
+                        const float alpha = (m_new == -__builtin_huge_valf()) ? 1.0f : fast_exp2(m[qt] - m_new);
+                        m[qt] = m_new;
+                        l[qt] *= alpha;
+#pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt) oacc[dt][qt] *= alpha;
+                    }
                 }
             }
             const float mn0 = (m[0] == -__builtin_huge_valf()) ? 0.0f : m[0];
@@ -1084,18 +1098,11 @@ static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStr
                 return hipGetLastError();
             }
         }
-        if constexpr (kProducts16<D> && !DROP) {
-            if (plan.key_groups != 1) return hipErrorInvalidValue;
-            if (plan.waves == 8)
-                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p);
-            else if (plan.waves == 4)
-                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 4>), grid, block, 0, stream, p);
-            else
-                return hipErrorInvalidValue;
-            return hipGetLastError();
-        }
         if (plan.waves == 8) {
-            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP, 1>), grid, block, 0, stream, p);
+            if constexpr (kProducts16<D> && !DROP)
+                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP, 1>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
     }
@@ -1185,7 +1192,7 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
     plan->block_kv = BC;
     plan->threads = waves * 64;
     plan->workgroups = (long long)((N + BQ - 1) / BQ) * B * Hq;
-    plan->lds_bytes = 2 * BC * (k_pitch(D) + (kProducts16<D> && !dropout ? v16_pitch(D) : v_pitch(D))) * 2;
+    plan->lds_bytes = 2 * BC * (k_pitch(D) + (kProducts16<D> && !dropout && waves == 8 ? v16_pitch(D) : v_pitch(D))) * 2;
 }
 
 bool fwd_plan(int B, int Hq, int N, int d, bool causal, bool dropout, FwdPlan* plan) {
