@@ -383,8 +383,9 @@ def cpu_model():
 
 
 def mfma_ceiling(steps):
-    """TFLOP/s of attn_probe_mfma_rate (independent v_mfma_f32_32x32x16_bf16
-    products, two waves per SIMD, no other work) on operands drawn like the
+    """TFLOP/s of attn_probe_mfma_rate and attn_probe_mfma16_rate (independent
+    v_mfma_f32_32x32x16_bf16 or v_mfma_f32_16x16x32_bf16 products, two waves
+    per SIMD, no other work) on operands drawn like the
     workloads' inputs (N(0,1) rounded to bf16) and on all-zero operands: the
     matrix-core rate the chip sustains under its power management for each
     operand pattern, which bounds every attention kernel's MFMA throughput."""
@@ -400,14 +401,16 @@ def mfma_ceiling(steps):
     for name, src in (("random", torch.randn(n, generator=g).to(torch.bfloat16).cuda()),
                       ("zeros", torch.zeros(n, dtype=torch.bfloat16, device="cuda"))):
         dst = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
-        for chains in (1, 2, 4, 8):
-            flops = ea.probe_mfma_rate(src, dst, blocks, iters, chains)  # warm-up
-            ms = time_loop(lambda: ea.probe_mfma_rate(src, dst, blocks, iters, chains), steps, stream)
-            out[f"{name}_chains{chains}"] = {
-                "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
-                "pct_of_bf16_peak": round(100.0 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
-    line = {"probe": "mfma_ceiling", "op": "v_mfma_f32_32x32x16_bf16", "waves_per_simd": 2,
-            "flops_per_call": blocks * 8 * 8 * iters * 32768.0, "steps": steps, **out}
+        for shape, tag in (("32x32x16", ""), ("16x16x32", "m16_")):
+            for chains in (1, 2, 4, 8):
+                run = lambda: ea.probe_mfma_rate(src, dst, blocks, iters, chains, shape)  # noqa: E731
+                flops = run()  # warm-up
+                ms = time_loop(run, steps, stream)
+                out[f"{tag}{name}_chains{chains}"] = {
+                    "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                    "pct_of_bf16_peak": round(100.0 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    line = {"probe": "mfma_ceiling", "op": "v_mfma_f32_32x32x16_bf16 (keys m16_*: v_mfma_f32_16x16x32_bf16)",
+            "waves_per_simd": 2, "flops_per_call": blocks * 8 * 8 * iters * 32768.0, "steps": steps, **out}
     print(json.dumps(line), flush=True)
 
 

@@ -164,6 +164,8 @@ def lib() -> ctypes.CDLL:
     L.attn_probe_mfma_src_elems.restype = sz
     L.attn_probe_mfma_rate.argtypes = [vp, vp, i, i, i, vp]
     L.attn_probe_mfma_rate.restype = i
+    L.attn_probe_mfma16_rate.argtypes = [vp, vp, i, i, i, vp]
+    L.attn_probe_mfma16_rate.restype = i
     _lib = L
     return L
 
@@ -563,17 +565,21 @@ def fwd_plan(B, Hq, Hkv, N, d, causal=False) -> dict:
     return {name: getattr(plan, name) for name, _ in AttnPlan._fields_}
 
 
-def probe_mfma_rate(src, dst, blocks, iters, chains=8):
-    """attn_probe_mfma_rate (include/attn_probe.h): enqueue the matrix-core
-    rate probe on the current stream; src holds probe_mfma_src_elems(blocks)
-    bf16 values, dst blocks * 512 floats. Returns the flops it enqueues."""
+def probe_mfma_rate(src, dst, blocks, iters, chains=8, shape="32x32x16"):
+    """attn_probe_mfma_rate or, for shape "16x16x32", attn_probe_mfma16_rate
+    (include/attn_probe.h): enqueue the matrix-core rate probe on the current
+    stream; src holds probe_mfma_src_elems(blocks) bf16 values, dst
+    blocks * 512 floats. Returns the flops it enqueues (the same for both
+    shapes)."""
     import torch
     if src.dtype != torch.bfloat16 or src.numel() < lib().attn_probe_mfma_src_elems(blocks):
         raise ValueError("src must hold probe_mfma_src_elems(blocks) bf16 values")
     if dst.dtype != torch.float32 or dst.numel() < blocks * 512:
         raise ValueError("dst must hold blocks * 512 floats")
-    _check(lib().attn_probe_mfma_rate(src.data_ptr(), dst.data_ptr(), blocks, iters, chains,
-                                      _stream_ptr(src.device)))
+    fn = {"32x32x16": lib().attn_probe_mfma_rate, "16x16x32": lib().attn_probe_mfma16_rate}.get(shape)
+    if fn is None:
+        raise ValueError("shape must be '32x32x16' or '16x16x32'")
+    _check(fn(src.data_ptr(), dst.data_ptr(), blocks, iters, chains, _stream_ptr(src.device)))
     return blocks * 8 * 8 * iters * 32768.0
 
 

@@ -58,8 +58,9 @@
 //    O = sum_g 2^(m_g - M) O_g. (Two groups of 4 waves over 128 rows, two
 //    waves per SIMD, gained nothing: the groups then share each SIMD.)
 //  * d = 128 without dropout on the 8-wave plan: fwd_m16_kernel runs the
-//    same step loop on 16x16x32 products (layout in its own comment), which
-//    the chip sustains at a higher clock than 32x32x16 ones.
+//    step loop on 16x16x32 products, which the chip sustains at a higher
+//    rate than 32x32x16 ones, pipelined across key blocks (layout and
+//    schedule in its own comment).
 #include <type_traits>
 
 #include "attn_device.h"
@@ -536,9 +537,17 @@ void fwd_kernel(FwdParams p) {
 //  * The V tile pitch is an odd multiple of 32 bytes modulo 256: the two
 //    16-lane groups served together read 8 rows at one column block, which
 //    then land on 8 different 32-byte bank groups.
+//  * The step loop is software pipelined across key blocks: step j computes
+//    the S^T products of block j + 1 while it turns block j's scores into
+//    probabilities and runs block j's O^T products (the region plan is in
+//    the kernel), so that every stretch of softmax work has matrix products
+//    of the same wave beside it. K therefore runs one tile ahead of V.
+//  * 16x16x32 products are what the chip runs fastest on random operands:
+//    the rate probe (include/attn_probe.h) sustains 2.15 PFLOP/s with 4
+//    independent accumulators per wave against 1.33 for 32x32x16.
 // Everything else (online softmax with the lazy reference maximum, tile
-// loads straight to LDS, causal/window skipping, launch order) is the step
-// loop of fwd_kernel.
+// loads straight to LDS, causal/window skipping, launch order) is as in
+// fwd_kernel.
 constexpr int v16_pitch(int d) { return ((2 * d / 32) % 2 == 1 ? 2 * d : 2 * d + 32) / 2; }
 static_assert(v16_pitch(128) == 144 && (v16_pitch(128) * 2 / 32) % 2 == 1, "");
 // Head dims whose no-dropout 8-wave step loop runs on 16x16x32 products.
@@ -584,10 +593,13 @@ void fwd_m16_kernel(FwdParams p) {
     constexpr int KP = k_pitch(D);
     constexpr int VP = v16_pitch(D);
     constexpr int CPR = D / 8;
-    constexpr int BUF = BC * (KP + VP);
     static_assert(D % 32 == 0 && D <= 128 && FwdTile<D>::BLOCK_KV == BC, "16x16x32 step loop: 64-key tiles");
 
-    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF];
+    // Two K and two V tile buffers, each its own LDS object (see below).
+    __shared__ __attribute__((aligned(16))) e16 sK0[BC * KP];
+    __shared__ __attribute__((aligned(16))) e16 sK1[BC * KP];
+    __shared__ __attribute__((aligned(16))) e16 sV0[BC * VP];
+    __shared__ __attribute__((aligned(16))) e16 sV1[BC * VP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -627,7 +639,15 @@ void fwd_m16_kernel(FwdParams p) {
     const int W = WINDOW ? p.window : 0;
     const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
 
-    // Tiles go straight from memory to LDS, as in fwd_kernel.
+    // Tiles go straight from memory to LDS, as in fwd_kernel, but K runs one
+    // tile ahead of V: step j reads K of block j + 1 (the next scores) and V
+    // of block j, and loads K of block j + 2 and V of block j + 1. Block t's
+    // K and V sit in buffer (t - kb_begin) & 1, which the step loop (unrolled
+    // by two) knows at compile time. Each buffer being its own __shared__
+    // object, the compiler can see that the transposing V reads of the
+    // current buffer do not alias the loads in flight into the other one;
+    // within one object it would make them wait for those loads (vmcnt 0)
+    // half-way through every step.
     constexpr int CKK = KP / 8, CKV = VP / 8;
     constexpr int NLK = BC * CKK / 64, NLV = BC * CKV / 64;
     constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
@@ -648,192 +668,294 @@ void fwd_m16_kernel(FwdParams p) {
             offv[i] = ch < CPR ? (uint32_t)row * sv2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
         }
     }
-    auto issue_tile = [&](int kv0, int bufi) {
-        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
-        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
-        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
-        char* kb_lds = reinterpret_cast<char*>(smem + bufi * BUF);
-        char* vb_lds = kb_lds + BC * KP * 2;
+    auto issue_k = [&](int kb, e16* buf) {
+        const int kv0 = kb * BC;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * (uint32_t)skn * 2u + D * 2);
+        char* dst = reinterpret_cast<char*>(buf);
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
             const int j = wave + i * NW;
-            if (NLK % NW == 0 || j < NLK) buf_load16_to_lds(rk, kb_lds + j * 1024, offk[i]);
+            if (NLK % NW == 0 || j < NLK) buf_load16_to_lds(rk, dst + j * 1024, offk[i]);
         }
+    };
+    auto issue_v = [&](int kb, e16* buf) {
+        const int kv0 = kb * BC;
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * (uint32_t)svn * 2u + D * 2);
+        char* dst = reinterpret_cast<char*>(buf);
 #pragma unroll
         for (int i = 0; i < LPWV; ++i) {
             const int j = wave + i * NW;
-            if (NLV % NW == 0 || j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
+            if (NLV % NW == 0 || j < NLV) buf_load16_to_lds(rv, dst + j * 1024, offv[i]);
         }
     };
-    issue_tile(kb_begin * BC, kb_begin & 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     f32x4 oacc[NDT][2];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x4{};
     float m[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()};  // per query tile, log2 domain
     float l[2] = {0.0f, 0.0f};
+    float mn[2] = {0.0f, 0.0f};  // m with -inf read as 0: the exponent offset
     const float c = p.c;
     // Transposing V read: lane 4t+s of group g addresses key row 4g + t, dims 4s .. 4s+3.
     const int v_row = 4 * g + (l16 >> 2);
     const int v_col = 4 * (l16 & 3);
 
-    auto run_step = [&](int kb, int bufi, int kb_last, auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        issue_tile(min(kb + 1, kb_last) * BC, bufi ^ 1);
+    // A wave computes the blocks from the workgroup's first to the last one
+    // that holds a key at or before its last query. (Under a sliding window
+    // the later waves' bands start a few blocks after the first; those blocks
+    // are masked to -inf in full and add nothing.)
+    const int kb_last_w = CAUSAL ? min(kb_end - 1, (qw0 + 31) / BC) : kb_end - 1;
+    auto needs_mask = [&](int kb) {
         const int kv0 = kb * BC;
-        const e16* Ks = smem + bufi * BUF;
-        const e16* Vs = Ks + BC * KP;
-        const bool active = !MASKED || !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1));
-        if (active) {
-            // s[kt][qt][r]: key kv0 + 16 kt + 4 g + r, query qw0 + 16 qt + l16.
-            f32x4 s[4][2];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) s[kt][0] = s[kt][1] = f32x4{};
-            constexpr int NS = 4 * KS;
-            e16x8 kr[3];
-            auto rdk = [&](int idx) {
-                const int ks = idx / 4, kt = idx % 4;
-                kr[idx % 3] = lds_read8(Ks + (kt * 16 + l16) * KP + ks * 32 + g * 8);
-            };
-            rdk(0);
-            rdk(1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int idx = 0; idx < NS; ++idx) {
-                if (idx + 2 < NS) rdk(idx + 2);
-                const int ks = idx / 4, kt = idx % 4;
-                s[kt][0] = mfma16<DT>(kr[idx % 3], qf[0][ks], s[kt][0]);
-                s[kt][1] = mfma16<DT>(kr[idx % 3], qf[1][ks], s[kt][1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const bool need_mask = MASKED && ((CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N) ||
-                                              (WINDOW && kv0 < qw0 + 32 - W));
-            if (need_mask) {
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    const int qr = qt ? qrow1 : qrow0;
-                    const int hi = (CAUSAL ? min(qr, N - 1) : N - 1) - kv0 - 4 * g;
-                    const int lo = (WINDOW ? qr - W + 1 : 0) - kv0 - 4 * g;
-#pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int koff = kt * 16 + r;
-                            s[kt][qt][r] = (koff > hi || koff < lo) ? -__builtin_huge_valf() : s[kt][qt][r];
-                        }
-                }
-            }
-            // Lazy rescaling, per query tile, as in fwd_kernel. The reference
-            // maximum m is the same in the four 16-lane groups of a query, so
-            // when no lane's own maximum exceeds m + 8 (log2 units) neither
-            // does the row's, and the step keeps m without combining the
-            // groups' maxima; only then (or while m is still -inf) are they
-            // combined and the rescale decided as in fwd_kernel.
-            float mx[2];
+        return (CAUSAL && kv0 + BC - 1 > qw0) || (kv0 + BC > N) || (WINDOW && kv0 < qw0 + 32 - W);
+    };
+    // s[kt][qt][r]: key kv0 + 16 kt + 4 g + r, query qw0 + 16 qt + l16.
+    using Scores = f32x4[4][2];
+    // Masks block kb's scores, then takes each query tile's maximum and
+    // decides the lazy rescale (as fwd_kernel): the reference m moves only
+    // when some row's block maximum exceeds it by more than 8 (log2 units).
+    // The lanes' own maxima are combined over the four 16-lane groups only
+    // when one of them could move it.
+    auto finish_scores = [&](Scores& s, int kb) {
+        if (needs_mask(kb)) {
+            const int kv0 = kb * BC;
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                mx[qt] = s[0][qt][0];
+                const int qr = qt ? qrow1 : qrow0;
+                const int hi = (CAUSAL ? min(qr, N - 1) : N - 1) - kv0 - 4 * g;
+                const int lo = (WINDOW ? qr - W + 1 : 0) - kv0 - 4 * g;
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) mx[qt] = fmaxf(mx[qt], s[kt][qt][r]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int koff = kt * 16 + r;
+                        s[kt][qt][r] = (koff > hi || koff < lo) ? -__builtin_huge_valf() : s[kt][qt][r];
+                    }
             }
-            const bool moves = mx[0] * c > m[0] + 8.0f || mx[1] * c > m[1] + 8.0f ||
-                               m[0] == -__builtin_huge_valf() || m[1] == -__builtin_huge_valf();
-            if (__any(moves)) {
-                float mb[2];
+        }
+        float mx[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            mx[qt] = s[0][qt][0];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx[qt] = fmaxf(mx[qt], s[kt][qt][r]);
+        }
+        const bool moves = mx[0] * c > m[0] + 8.0f || mx[1] * c > m[1] + 8.0f ||
+                           m[0] == -__builtin_huge_valf() || m[1] == -__builtin_huge_valf();
+        if (__any(moves)) {
+            float mb[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                mb[qt] = max_across_quarters(mx[qt]) * c;
+                if (m[qt] == -__builtin_huge_valf()) m[qt] = mb[qt];
+            }
+            if (__any(mb[0] > m[0] + 8.0f || mb[1] > m[1] + 8.0f)) {
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
-                    mb[qt] = max_across_quarters(mx[qt]) * c;
-                    if (m[qt] == -__builtin_huge_valf()) m[qt] = mb[qt];
-                }
-                if (__any(mb[0] > m[0] + 8.0f || mb[1] > m[1] + 8.0f)) {
+                    const float m_new = fmaxf(m[qt], mb[qt]);
+                    const float alpha = (m_new == -__builtin_huge_valf()) ? 1.0f : fast_exp2(m[qt] - m_new);
+                    m[qt] = m_new;
+                    l[qt] *= alpha;
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) {
-                        const float m_new = fmaxf(m[qt], mb[qt]);
-                        const float alpha = (m_new == -__builtin_huge_valf()) ? 1.0f : fast_exp2(m[qt] - m_new);
-                        m[qt] = m_new;
-                        l[qt] *= alpha;
-#pragma unroll
-                        for (int dt = 0; dt < NDT; ++dt) oacc[dt][qt] *= alpha;
-                    }
+                    for (int dt = 0; dt < NDT; ++dt) oacc[dt][qt] *= alpha;
                 }
             }
-            const float mn0 = (m[0] == -__builtin_huge_valf()) ? 0.0f : m[0];
-            const float mn1 = (m[1] == -__builtin_huge_valf()) ? 0.0f : m[1];
-            float lsum0 = 0.0f, lsum1 = 0.0f;
-            // Probability e (0..15) of key half jj: query tile e / 8, B element
-            // i = e % 8, i.e. register i % 4 of s[2 jj + i / 4].
-            float pe[2][16];
-            auto exp1 = [&](int jj, int e) {
-                const int qt = e >> 3, i = e & 7;
-                const float x = fast_exp2(fmaf(s[2 * jj + (i >> 2)][qt][i & 3], c, qt ? -mn1 : -mn0));
-                if (qt)
-                    lsum1 += x;
-                else
-                    lsum0 += x;
-                pe[jj][e] = x;
-            };
-            auto pack = [&](int jj, int qt) {
-                const float* x = &pe[jj][qt * 8];
-                return cat8(cvt2<DT>(x[0], x[1]), cvt2<DT>(x[2], x[3]), cvt2<DT>(x[4], x[5]), cvt2<DT>(x[6], x[7]));
-            };
-            auto v_op = [&](int idx) {
-                const int jj = idx / NDT, dt = idx % NDT;
-                const e16* vp = Vs + (jj * 32 + v_row) * VP + v_col + dt * 16;
-                return join8(lds_read_tr4(vp), lds_read_tr4(vp + 16 * VP));
-            };
-            // The first half's probabilities, then its products with the
-            // second half's exponentials in their shadow; V^T fragments are
-            // read two ahead.
-            constexpr int NP = 2 * NDT;
-            constexpr int EPD = (16 + NDT - 1) / NDT;  // exponentials per first-half fragment
-            e16x8 va[3];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) exp1(0, e);
-            e16x8 pb[2][2];
-            pb[0][0] = pack(0, 0);
-            pb[0][1] = pack(0, 1);
-            va[0] = v_op(0);
-            va[1] = v_op(1);
+            for (int qt = 0; qt < 2; ++qt) mn[qt] = (m[qt] == -__builtin_huge_valf()) ? 0.0f : m[qt];
+        }
+    };
+
+    // One step j, in four regions pinned in order by scheduling barriers:
+    //   R1: 12 of the 16 S^T product pairs of block j + 1 (K read two pairs
+    //       ahead), with the 16 exponentials of block j's first key half;
+    //   R2: the 8 O^T product pairs of the first half (V^T read two ahead),
+    //       with 10 exponentials of the second half;
+    //   R3: the last 4 S^T pairs of block j + 1, with the last 6;
+    //   R4: the 8 O^T pairs of the second half, then block j + 1's mask,
+    //       maxima and rescale decision.
+    // A pair is the two products (query tiles) sharing one A operand. So
+    // every region issues softmax work under its own matrix products instead
+    // of between them. CUR: this wave computes block j (its scores are in
+    // `sc`); NXT: it computes block j + 1 (into `sn`).
+    auto step = [&](int j, Scores& sc, Scores& sn, const e16* Ks, const e16* Vs) {
+        constexpr bool CUR = true, NXT = true;
+        constexpr int NS = 4 * KS;  // S^T product pairs
+        e16x8 kr[3];
+        auto rdk = [&](int idx) {
+            const int ks = idx / 4, kt = idx % 4;
+            kr[idx % 3] = lds_read8(Ks + (kt * 16 + l16) * KP + ks * 32 + g * 8);
+        };
+        auto sprod = [&](int idx) {
+            const int ks = idx / 4, kt = idx % 4;
+            if (idx + 2 < NS) rdk(idx + 2);
+            sn[kt][0] = mfma16<DT>(kr[idx % 3], qf[0][ks], sn[kt][0]);
+            sn[kt][1] = mfma16<DT>(kr[idx % 3], qf[1][ks], sn[kt][1]);
+        };
+        float lsum0 = 0.0f, lsum1 = 0.0f;
+        // Probability u (0..31) of the step: key half jj = u / 16 and e = u %
+        // 16, query tile e / 8, B element i = e % 8, i.e. register i % 4 of
+        // sc[2 jj + i / 4]. Each is computed in three stages a slot apart
+        // (a slot being one product pair): the exponent's FMA (A), the
+        // exponential (B), then the row sum and, for odd e, the rounding of
+        // the pair to 16 bits (C), so that no stage waits on the one before
+        // it and the products issue without stalls.
+        float ta[32], xb[32];
+        e16x2 pp[2][8];
+        auto stage_a = [&](int u) {
+            const int jj = u >> 4, e = u & 15, qt = e >> 3, i = e & 7;
+            ta[u] = fmaf(sc[2 * jj + (i >> 2)][qt][i & 3], c, -mn[qt]);
+        };
+        auto stage_b = [&](int u) { xb[u] = fast_exp2(ta[u]); };
+        auto stage_c = [&](int u) {
+            const int jj = u >> 4, e = u & 15;
+            if (e >> 3)
+                lsum1 += xb[u];
+            else
+                lsum0 += xb[u];
+            if (e & 1) pp[jj][e >> 1] = cvt2<DT>(xb[u - 1], xb[u]);
+        };
+        // The slot that holds probabilities [lo, hi) starts those two further
+        // on (A), takes the next ones through their exponential (B) and
+        // finishes its own (C), in that order (a slot of two holds both
+        // stages of some probabilities); the first slot also primes the
+        // pipeline.
+        auto units = [&](int lo, int hi) {
+            if (lo == 0) {
+                stage_a(0);
+                stage_a(1);
+                stage_b(0);
+            }
+            for (int u = lo + 2; u < hi + 2 && u < 32; ++u) stage_a(u);
+            for (int u = lo + 1; u < hi + 1 && u < 32; ++u) stage_b(u);
+            for (int u = lo; u < hi; ++u) stage_c(u);
+        };
+        e16x8 pb[2][2];
+        auto pack = [&](int jj, int qt) {
+            const e16x2* x = &pp[jj][qt * 4];
+            pb[jj][qt] = cat8(x[0], x[1], x[2], x[3]);
+        };
+        e16x8 va[3];
+        auto v_op = [&](int idx) {
+            const int jj = idx / NDT, dt = idx % NDT;
+            const e16* vp = Vs + (jj * 32 + v_row) * VP + v_col + dt * 16;
+            va[idx % 3] = join8(lds_read_tr4(vp), lds_read_tr4(vp + 16 * VP));
+        };
+        constexpr int NP = 2 * NDT;  // O^T product pairs
+        auto oprod = [&](int idx) {
+            const int jj = idx / NDT, dt = idx % NDT;
+            if (idx + 2 < NP) v_op(idx + 2);
+            oacc[dt][0] = mfma16<DT>(va[idx % 3], pb[jj][0], oacc[dt][0]);
+            oacc[dt][1] = mfma16<DT>(va[idx % 3], pb[jj][1], oacc[dt][1]);
+        };
+        constexpr int S1 = 12;       // S^T pairs in R1 (the rest in R3)
+        static_assert(NS > S1 && NP >= 4, "region split assumes d = 128");
+        constexpr int E2 = 10;       // second-half exponentials in R2 (the rest in R3)
+        if constexpr (NXT) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) sn[kt][0] = sn[kt][1] = f32x4{};
+            rdk(0);
+            rdk(1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // R1
+        if constexpr (CUR) {
+#pragma unroll
+            for (int i = 0; i < S1; ++i) {
+                if constexpr (NXT) sprod(i);
+                units((i * 16) / S1, ((i + 1) * 16) / S1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            pack(0, 0);
+            pack(0, 1);
+            v_op(0);
+            v_op(1);
             __builtin_amdgcn_sched_barrier(0);
+            // R2
 #pragma unroll
-            for (int idx = 0; idx < NP; ++idx) {
-                const int jj = idx / NDT, dt = idx % NDT;
-                if (idx + 2 < NP) va[(idx + 2) % 3] = v_op(idx + 2);
-                oacc[dt][0] = mfma16<DT>(va[idx % 3], pb[jj][0], oacc[dt][0]);
-                oacc[dt][1] = mfma16<DT>(va[idx % 3], pb[jj][1], oacc[dt][1]);
-                if (jj == 0) {
+            for (int i = 0; i < NDT; ++i) {
+                oprod(i);
+                units(16 + (i * E2) / NDT, 16 + ((i + 1) * E2) / NDT);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // R3
+            constexpr int S3 = NS - S1;
 #pragma unroll
-                    for (int j = 0; j < EPD; ++j)
-                        if (dt * EPD + j < 16) exp1(1, dt * EPD + j);
-                    if (dt == NDT - 1) {
-                        pb[1][0] = pack(1, 0);
-                        pb[1][1] = pack(1, 1);
-                    }
-                }
+            for (int i = 0; i < S3; ++i) {
+                if constexpr (NXT) sprod(S1 + i);
+                units(16 + E2 + (i * (16 - E2)) / S3, 16 + E2 + ((i + 1) * (16 - E2)) / S3);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            pack(1, 0);
+            pack(1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // R4
+#pragma unroll
+            for (int i = NDT; i < NP; ++i) {
+                oprod(i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             l[0] += lsum0;
             l[1] += lsum1;
+        } else if constexpr (NXT) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                sprod(i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
+        if constexpr (NXT) finish_scores(sn, j + 1);
+    };
+
+    // Prologue: K and V of the first block and K of the second; the first
+    // block's scores.
+    Scores sA, sB;
+    issue_k(kb_begin, sK0);
+    issue_v(kb_begin, sV0);
+    if (kb_begin + 1 < kb_end) issue_k(kb_begin + 1, sK1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    {
+        // The S^T products of the first block alone (step j = kb_begin - 1
+        // without a current block), reading K of kb_begin.
+        const e16* Ks = sK0;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sA[kt][0] = sA[kt][1] = f32x4{};
+#pragma unroll
+        for (int idx = 0; idx < 4 * KS; ++idx) {
+            const int ks = idx / 4, kt = idx % 4;
+            const e16x8 kr = lds_read8(Ks + (kt * 16 + l16) * KP + ks * 32 + g * 8);
+            sA[kt][0] = mfma16<DT>(kr, qf[0][ks], sA[kt][0]);
+            sA[kt][1] = mfma16<DT>(kr, qf[1][ks], sA[kt][1]);
+        }
+        finish_scores(sA, kb_begin);
+    }
+    __syncthreads();  // K of kb_begin is read; step kb_begin refills its buffer
+
+    // Step j with (j - kb_begin) & 1 == PAR: K of j + 1 is in buffer 1 - PAR,
+    // V of j in buffer PAR; K of j + 2 goes to buffer PAR, V of j + 1 to 1 - PAR.
+    auto run = [&](int j, Scores& sc, Scores& sn, auto par_tag) {
+        constexpr int PAR = decltype(par_tag)::value;
+        e16* const Kn = PAR ? sK0 : sK1;
+        e16* const Kl = PAR ? sK1 : sK0;
+        e16* const Vc = PAR ? sV1 : sV0;
+        e16* const Vl = PAR ? sV0 : sV1;
+        if (j + 1 < kb_end) issue_v(j + 1, Vl);
+        if (j + 2 < kb_end) issue_k(j + 2, Kl);
+        // On its last block (and on the grid's last) a wave's step still
+        // runs the next block's products, on whatever the K buffer holds;
+        // those scores are masked and never used.
+        if (j <= kb_last_w) step(j, sc, sn, Kn, Vc);
+        __builtin_amdgcn_s_waitcnt(0);  // K of j + 2 and V of j + 1 have landed
         __syncthreads();
     };
-    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
-    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
-    if (WINDOW) {
-        const int t = q0 + BQ - W;
-        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
-    }
-    ku_end = max(ku_end, ku_begin);
     int kb = kb_begin;
-    for (; kb < ku_begin; ++kb) run_step(kb, kb & 1, kb_end - 1, std::true_type{});
-    for (; kb < ku_end; ++kb) run_step(kb, kb & 1, kb_end - 1, std::false_type{});
-    for (; kb < kb_end; ++kb) run_step(kb, kb & 1, kb_end - 1, std::true_type{});
-
+    for (; kb + 1 < kb_end; kb += 2) {
+        run(kb, sA, sB, std::integral_constant<int, 0>{});
+        run(kb + 1, sB, sA, std::integral_constant<int, 1>{});
+    }
+    if (kb < kb_end) run(kb, sA, sB, std::integral_constant<int, 0>{});
     // Epilogue: the four 16-lane groups' row sums, then O and LSE.
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {

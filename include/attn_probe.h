@@ -1,7 +1,7 @@
 /*
  * attn_probe.h - measurement helper of libattn.so (not part of the attention
  * computation): the rate at which the MI355X matrix cores run
- * v_mfma_f32_32x32x16_bf16 on given operands. bench.py uses it to state the
+ * v_mfma_f32_32x32x16_bf16 or v_mfma_f32_16x16x32_bf16 on given operands. bench.py uses it to state the
  * ceiling that the attention kernels' achieved MFMA throughput is compared
  * with, since the chip's clock under sustained matrix work depends on the
  * operands' bit patterns (power management).
@@ -36,6 +36,16 @@ size_t attn_probe_mfma_src_elems(int blocks);
  */
 attn_status attn_probe_mfma_rate(const void* src, float* dst, int blocks, int iters, int chains,
                                  hipStream_t stream);
+
+/*
+ * The same probe on v_mfma_f32_16x16x32_bf16 (16 * 16 * 32 * 2 flops each):
+ * each wave issues 16 * iters products round-robin into `chains` (1, 2, 4 or
+ * 8) independent 16x16 accumulators, so the flops per call are those of
+ * attn_probe_mfma_rate with the same blocks and iters. Same arguments,
+ * ownership and errors.
+ */
+attn_status attn_probe_mfma16_rate(const void* src, float* dst, int blocks, int iters, int chains,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

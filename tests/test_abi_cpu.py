@@ -413,11 +413,13 @@ def test_noalloc_rejects_problems_past_its_scratch(L, B, Hq, N):
     assert noalloc(L, B=B, Hq=Hq, Hkv=1, N=N) == 14
 
 
-def test_mfma_probe_validates(L):
+@pytest.mark.parametrize("probe", ["attn_probe_mfma_rate", "attn_probe_mfma16_rate"])
+def test_mfma_probe_validates(L, probe):
+    fn = getattr(L, probe)
     assert L.attn_probe_mfma_src_elems(3) == 3 * 512 * 16
-    assert L.attn_probe_mfma_rate(None, P, 4, 8, 8, None) == 1
-    assert L.attn_probe_mfma_rate(P, None, 4, 8, 8, None) == 1
-    assert L.attn_probe_mfma_rate(P, P, 0, 8, 8, None) == 2
-    assert L.attn_probe_mfma_rate(P, P, 4, 0, 8, None) == 2
-    assert L.attn_probe_mfma_rate(P, P, (1 << 20) + 1, 8, 8, None) == 2
-    assert L.attn_probe_mfma_rate(P, P, 4, 8, 3, None) == 2
+    assert fn(None, P, 4, 8, 8, None) == 1
+    assert fn(P, None, 4, 8, 8, None) == 1
+    assert fn(P, P, 0, 8, 8, None) == 2
+    assert fn(P, P, 4, 0, 8, None) == 2
+    assert fn(P, P, (1 << 20) + 1, 8, 8, None) == 2
+    assert fn(P, P, 4, 8, 3, None) == 2
