@@ -185,10 +185,11 @@ def summarize_pmc(fetch_dir, write_dir, out_dir, workload, mib):
     for kernel in ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel",
                    "decode_split_kernel", "decode_merge_kernel"):
         # the dK/dV pass runs the 64-keys-per-wave kernel on large d = 128 grids,
-        # the forward the 16x16x32-product kernel on large d = 128 grids and the
-        # key-split kernel on short sequences
+        # the forward and the dQ pass their 16x16x32-product kernels on large
+        # d = 128 grids, the forward the key-split kernel on short sequences
         prefixes = [f"{kernel}<"] + (["bwd_dkdv_wide_kernel<"] if kernel == "bwd_dkdv_kernel" else []) + \
-            (["fwd_m16_kernel<", "fwd_split_kernel<"] if kernel == "fwd_kernel" else [])
+            (["fwd_m16_kernel<", "fwd_split_kernel<"] if kernel == "fwd_kernel" else []) + \
+            (["bwd_dq_m16_kernel<"] if kernel == "bwd_dq_kernel" else [])
         hits = [(pf, k) for pf in prefixes for k in fetch if pf in k]
         if not hits:
             continue

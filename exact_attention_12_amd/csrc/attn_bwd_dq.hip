@@ -403,6 +403,359 @@ void bwd_dq_kernel(BwdParams p) {
     }
 }
 
+// ------------------------------------------------- dQ on 16x16x32 products
+//
+// d = 128 without dropout, one key group: the same pass on
+// v_mfma_f32_16x16x32 products, which the chip sustains at a higher rate
+// than 32x32x16 ones on random operands (the rate probe of attn_probe.h),
+// in the layout of the forward's fwd_m16_kernel:
+//  * a wave holds two 16-query tiles (qt). S^T = K Q^T and dP^T = V dO^T of
+//    a 64-key step are 4 key tiles (kt) x 2 query tiles of 16x16; lane l
+//    then holds, for query qw0 + 16 qt + l % 16, keys 16 kt + 4 (l / 16) + r
+//    (r = 0..3), and its LSE and -D_i are per-lane scalars.
+//  * dQ^T += K^T dS^T over the step's two 32-key halves: the lane's dS^T
+//    values are already the B operand (key order 4g..4g+3, 16+4g..16+4g+3
+//    in 16-lane group g), and K^T is read transposed in the same order.
+//  * The K tile is read row-wise (S^T) and transposed (K^T). Its pitch is an
+//    odd multiple of 32 bytes (the forward's V tile: the transposing read's
+//    two 16-lane groups served together hit 8 different 32-byte bank
+//    groups) and its 16-byte chunks are XOR-swizzled by bit 3 of the row,
+//    which moves rows r and r + 8 of a row read to different banks while a
+//    transposing read's 4 rows share one swizzle value. The V tile is read
+//    row-wise only (pitch an odd multiple of 16 bytes).
+//  * Each of the two K and two V buffers is its own LDS object, with the
+//    buffer known at compile time, so the transposing reads of the current
+//    buffer do not wait for the loads in flight into the other one.
+//  * A step runs in four regions pinned by scheduling barriers: the S^T and
+//    dP^T products of the first key half; those of the second half with the
+//    first half's dS^T in their shadow; the first half's dQ^T products with
+//    the second half's dS^T; the second half's dQ^T products. Each dS^T value
+//    goes through three stages a product pair apart (exponent FMA,
+//    exponential with the mask, product with dP^T + (-D_i) and rounding).
+template <int DT>
+__device__ __forceinline__ f32x4 dq_mfma16(e16x8 a, e16x8 b, f32x4 c) {
+    if constexpr (DT == kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kDq16KPitch = 144;  // elements: 288 bytes, 9 x 32
+static_assert((kDq16KPitch * 2 / 32) % 2 == 1 && kDq16KPitch >= 128 + 8, "");
+
+template <int DT, int MASK>
+__global__ __launch_bounds__(256, 2)
+void bwd_dq_m16_kernel(BwdParams p) {
+    constexpr int D = 128;
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
+    constexpr int NW = 4;
+    constexpr int BQ = NW * 32;
+    constexpr int BC = 64;
+    constexpr int KS = D / 32;     // contraction steps of S^T and dP^T
+    constexpr int NDT = D / 16;    // 16-row tiles of dQ^T
+    constexpr int KP = kDq16KPitch;
+    constexpr int VP = k_pitch(D);
+
+    __shared__ __attribute__((aligned(16))) e16 sK0[BC * KP];
+    __shared__ __attribute__((aligned(16))) e16 sK1[BC * KP];
+    __shared__ __attribute__((aligned(16))) e16 sV0[BC * VP];
+    __shared__ __attribute__((aligned(16))) e16 sV1[BC * VP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
+    const int N = p.N;
+
+    const int BH = p.B * p.Hq;
+    const int nqb = (N + BQ - 1) / BQ;
+    const int bid = blockIdx.x;
+    const int bh = xcd_head(bid % BH, BH);
+    const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
+    const int b = bh / p.Hq;
+    const int hq = bh - b * p.Hq;
+    const int hkv = hq / p.G;
+    const size_t row_off = (size_t)bh * N;
+    const e16* Kh = static_cast<const e16*>(p.k) + b * p.sk.b + hkv * p.sk.h;
+    const e16* Vh = static_cast<const e16*>(p.v) + b * p.sv.b + hkv * p.sv.h;
+    const long long skn = p.sk.n, svn = p.sv.n;
+
+    const int q0 = qb * BQ;
+    const int qw0 = q0 + wave * 32;
+    const int qrow[2] = {qw0 + l16, qw0 + 16 + l16};
+
+    // Q and dO operands (B of S^T and dP^T): query qrow[qt], dims 32 ks + 8 g .. +7.
+    e16x8 qf[2][KS], gf[2][KS];
+    float lse2[2], ndel[2];  // ndel = -D_i, as the preprocess stores it
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qr = qrow[qt];
+        if (qr < N) {
+            const e16* qp = static_cast<const e16*>(p.q) + b * p.sq.b + hq * p.sq.h + qr * p.sq.n + g * 8;
+            const e16* gp = static_cast<const e16*>(p.dout) + b * p.sdo.b + hq * p.sdo.h + qr * p.sdo.n + g * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[qt][ks] = *reinterpret_cast<const e16x8*>(qp + ks * 32);
+                gf[qt][ks] = *reinterpret_cast<const e16x8*>(gp + ks * 32);
+            }
+            lse2[qt] = p.lse[row_off + qr] * kLog2e;
+            ndel[qt] = p.delta[row_off + qr];
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) { qf[qt][ks] = e16x8{}; gf[qt][ks] = e16x8{}; }
+            lse2[qt] = __builtin_huge_valf();
+            ndel[qt] = 0.0f;
+        }
+    }
+
+    const int nkb = (N + BC - 1) / BC;
+    const int kb_end = CAUSAL ? min(nkb, (q0 + BQ - 1) / BC + 1) : nkb;
+    const int W = WINDOW ? p.window : 0;
+    const int kb_begin = WINDOW ? max(0, q0 - W + 1) / BC : 0;
+    // Blocks needing no per-element mask, as in bwd_dq_kernel (keys past N
+    // stay masked: their zero scores would give exp2(-LSE2)).
+    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
+    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
+    if (WINDOW) {
+        const int t = q0 + BQ - W;
+        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
+    }
+    ku_end = max(ku_end, ku_begin);
+
+    // Tile loads straight to LDS; slot s of K row r holds chunk s ^ ((r >> 3) & 1).
+    constexpr int CKK = KP / 8, CKV = VP / 8;
+    constexpr int NLK = BC * CKK / 64, NLV = BC * CKV / 64;
+    constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
+    static_assert(BC * CKK % 64 == 0 && BC * CKV % 64 == 0, "tile must be whole loads");
+    uint32_t offk[LPWK], offv[LPWV];
+    {
+        const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKK;
+            const int lc = (chunk - row * CKK) ^ ((row >> 3) & 1);
+            offk[i] = lc < D / 8 ? (uint32_t)row * sk2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int chunk = (wave + i * NW) * 64 + lane;
+            const int row = chunk / CKV;
+            const int lc = chunk - row * CKV;
+            offv[i] = lc < D / 8 ? (uint32_t)row * sv2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
+        }
+    }
+    auto issue = [&](int kb, e16* kbuf, e16* vbuf) {
+        const int kv0 = kb * BC;
+        const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * (uint32_t)skn * 2u + D * 2);
+        const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * (uint32_t)svn * 2u + D * 2);
+#pragma unroll
+        for (int i = 0; i < LPWK; ++i) {
+            const int j = wave + i * NW;
+            if (NLK % NW == 0 || j < NLK) buf_load16_to_lds(rk, reinterpret_cast<char*>(kbuf) + j * 1024, offk[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < LPWV; ++i) {
+            const int j = wave + i * NW;
+            if (NLV % NW == 0 || j < NLV) buf_load16_to_lds(rv, reinterpret_cast<char*>(vbuf) + j * 1024, offv[i]);
+        }
+    };
+
+    // Per-lane read offsets (elements); the other tiles are immediate offsets.
+    //  K rows (S^T operand): row 16 kt + l16, chunk 4 ks + g (swizzled).
+    //  V rows (dP^T operand): row 16 kt + l16, dims 32 ks + 8 g.
+    //  K^T (transposing read): lane 4t + s of group g reads key row 4 g + t
+    //  (+ 32 jj, + 16 for the second half of the operand), dims 16 dt + 4 s.
+    const int krd = l16 * KP + 8 * (g ^ ((l16 >> 3) & 1));
+    const int vrd = l16 * VP + 8 * g;
+    const int ktr = (4 * g + (l16 >> 2)) * KP + 8 * (((l16 & 3) >> 1) ^ (g >> 1)) + 4 * (l16 & 1);
+
+    f32x4 dq[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dq[dt][0] = dq[dt][1] = f32x4{};
+    const float c = p.c;
+
+    auto step = [&](int kb, const e16* Ks, const e16* Vs, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const int kv0 = kb * BC;
+        // s[kt][qt][r], dp[kt][qt][r]: key kv0 + 16 kt + 4 g + r, query qrow[qt].
+        f32x4 s[4][2], dp[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) s[kt][0] = s[kt][1] = dp[kt][0] = dp[kt][1] = f32x4{};
+        // Product pair idx of key half jj: ks = idx / 4, kt = 2 jj + (idx / 2) % 2,
+        // S^T (idx even, K operand) or dP^T (idx odd, V operand).
+        e16x8 op[3];
+        auto rd_row = [&](int jj, int idx) {
+            const int ks = idx >> 2, kt = 2 * jj + ((idx >> 1) & 1);
+            op[idx % 3] = (idx & 1) ? lds_read8(Vs + vrd + kt * 16 * VP + ks * 32)
+                                    : lds_read8(Ks + krd + kt * 16 * KP + ks * 32);
+        };
+        auto sprod = [&](int jj, int idx) {
+            const int ks = idx >> 2, kt = 2 * jj + ((idx >> 1) & 1);
+            if (idx + 2 < 16) rd_row(jj, idx + 2);
+            if (idx & 1) {
+                dp[kt][0] = dq_mfma16<DT>(op[idx % 3], gf[0][ks], dp[kt][0]);
+                dp[kt][1] = dq_mfma16<DT>(op[idx % 3], gf[1][ks], dp[kt][1]);
+            } else {
+                s[kt][0] = dq_mfma16<DT>(op[idx % 3], qf[0][ks], s[kt][0]);
+                s[kt][1] = dq_mfma16<DT>(op[idx % 3], qf[1][ks], s[kt][1]);
+            }
+        };
+        // Masks: key offset kt * 16 + r (from kv0 + 4 g) against the query's bounds.
+        int hi[2], lo[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            hi[qt] = (CAUSAL ? min(qrow[qt], N - 1) : N - 1) - kv0 - 4 * g;
+            lo[qt] = (WINDOW ? qrow[qt] - W + 1 : 0) - kv0 - 4 * g;
+        }
+        // dS^T value u (0..31): half jj = u / 16, query tile qt = (u / 8) % 2,
+        // i = u % 8: key tile 2 jj + i / 4, register i % 4, i.e. B element i.
+        float ta[32], xb[32];
+        e16x2 pp[2][8];
+        auto stage_a = [&](int u) {
+            const int jj = u >> 4, qt = (u >> 3) & 1, i = u & 7;
+            ta[u] = fmaf(s[2 * jj + (i >> 2)][qt][i & 3], c, -lse2[qt]);
+        };
+        auto stage_b = [&](int u) {
+            const int jj = u >> 4, qt = (u >> 3) & 1, i = u & 7;
+            const int koff = (2 * jj + (i >> 2)) * 16 + (i & 3);
+            float x = fast_exp2(ta[u]);
+            if (MASKED && (koff > hi[qt] || (WINDOW && koff < lo[qt]))) x = 0.0f;
+            xb[u] = x;
+        };
+        auto stage_c = [&](int u) {
+            const int jj = u >> 4, qt = (u >> 3) & 1, i = u & 7;
+            const float d = xb[u] * (dp[2 * jj + (i >> 2)][qt][i & 3] + ndel[qt]);
+            if (i & 1)
+                pp[jj][(u & 15) >> 1] = cvt2<DT>(ta[u - 1], d);
+            else
+                ta[u] = d;  // the even value waits here for its pair
+        };
+        auto units = [&](int lo_u, int hi_u, int start, int end) {
+            if (lo_u == start) {
+                stage_a(start);
+                stage_a(start + 1);
+                stage_b(start);
+            }
+#pragma unroll
+            for (int u = lo_u + 2; u < hi_u + 2 && u < end; ++u) stage_a(u);
+#pragma unroll
+            for (int u = lo_u + 1; u < hi_u + 1 && u < end; ++u) stage_b(u);
+#pragma unroll
+            for (int u = lo_u; u < hi_u; ++u) stage_c(u);
+        };
+        e16x8 pb[2][2];
+        auto pack = [&](int jj, int qt) {
+            const e16x2* x = &pp[jj][qt * 4];
+            pb[jj][qt] = cat8(x[0], x[1], x[2], x[3]);
+        };
+        // K^T operand of half jj, dims 16 dt .. +15.
+        e16x8 kt_op[3];
+        auto rd_tr = [&](int jj, int dt) {
+            const e16* kp = Ks + ktr + jj * 32 * KP + dt * 16;
+            kt_op[dt % 3] = join8(lds_read_tr4(kp), lds_read_tr4(kp + 16 * KP));
+        };
+        auto dqprod = [&](int jj, int dt) {
+            if (dt + 2 < NDT) rd_tr(jj, dt + 2);
+            dq[dt][0] = dq_mfma16<DT>(kt_op[dt % 3], pb[jj][0], dq[dt][0]);
+            dq[dt][1] = dq_mfma16<DT>(kt_op[dt % 3], pb[jj][1], dq[dt][1]);
+        };
+
+        // R1: S^T and dP^T of the first key half.
+        rd_row(0, 0);
+        rd_row(0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+            sprod(0, idx);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // R2: those of the second half, with the first half's dS^T.
+        rd_row(1, 0);
+        rd_row(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+            sprod(1, idx);
+            units(idx, idx + 1, 0, 16);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pack(0, 0);
+        pack(0, 1);
+        rd_tr(0, 0);
+        rd_tr(0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // R3: dQ^T products of the first half, with the second half's dS^T.
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            dqprod(0, dt);
+            units(16 + 2 * dt, 18 + 2 * dt, 16, 32);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pack(1, 0);
+        pack(1, 1);
+        rd_tr(1, 0);
+        rd_tr(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // R4: dQ^T products of the second half.
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            dqprod(1, dt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Block t's tiles sit in buffer (t - ku_begin) & 1. The mask-free blocks
+    // run in pairs whose buffers are known at compile time; the masked
+    // blocks before and after them (and a last unpaired mask-free block,
+    // for which the masks change nothing) pick their buffers at run time.
+    auto run_masked = [&](int kb) {
+        const bool par = (kb - ku_begin) & 1;
+        if (kb + 1 < kb_end) issue(kb + 1, par ? sK0 : sK1, par ? sV0 : sV1);
+        step(kb, par ? sK1 : sK0, par ? sV1 : sV0, std::true_type{});
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
+        __syncthreads();
+    };
+    auto run_pair = [&](int kb) {
+        if (kb + 1 < kb_end) issue(kb + 1, sK1, sV1);
+        step(kb, sK0, sV0, std::false_type{});
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kb + 2 < kb_end) issue(kb + 2, sK0, sV0);
+        step(kb + 1, sK1, sV1, std::false_type{});
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    {
+        const bool par = (kb_begin - ku_begin) & 1;
+        issue(kb_begin, par ? sK1 : sK0, par ? sV1 : sV0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int kb = kb_begin;
+    for (; kb < ku_begin; ++kb) run_masked(kb);
+    for (; kb + 1 < ku_end; kb += 2) run_pair(kb);
+    for (; kb < kb_end; ++kb) run_masked(kb);
+
+    // dQ = scale * sum_j dS_ij k_j; dq[dt][qt][r] is dim 16 dt + 4 g + r of query qrow[qt].
+    const float sc = p.scale;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qr = qrow[qt];
+        if (qr < N) {
+            e16* dqrow = static_cast<e16*>(p.dq) + b * p.sdq.b + hq * p.sdq.h + qr * p.sdq.n;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                store4<DT>(dqrow + dt * 16 + 4 * g, dq[dt][qt][0] * sc, dq[dt][qt][1] * sc,
+                           dq[dt][qt][2] * sc, dq[dt][qt][3] * sc);
+        }
+    }
+}
+
 template <int DT, int D, int MASK>
 static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
     const dim3 block(256);
@@ -414,6 +767,9 @@ static hipError_t launch_dq_dc(const BwdParams& p, hipStream_t stream) {
             const dim3 grid((unsigned)((p.N + 63) / 64 * p.B * p.Hq));
             hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, false, 2>), grid, block, 0, stream, p);
         }
+    } else if constexpr (D == 128) {
+        const dim3 grid((unsigned)((p.N + 127) / 128 * p.B * p.Hq));
+        hipLaunchKernelGGL((bwd_dq_m16_kernel<DT, MASK>), grid, block, 0, stream, p);
     } else {
         const dim3 grid((unsigned)((p.N + 127) / 128 * p.B * p.Hq));
         hipLaunchKernelGGL((bwd_dq_kernel<DT, D, MASK, false, 1>), grid, block, 0, stream, p);

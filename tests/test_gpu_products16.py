@@ -1,5 +1,5 @@
-"""The d = 128 forward on 16x16x32 products against the fp64 oracle (needs an
-MI355X).
+"""The d = 128 forward and dQ pass on 16x16x32 products against the fp64
+oracle (needs an MI355X).
 
 Without dropout, grids large enough for the 8-wave plan run the forward's
 step loop on 16x16x32 products (fwd_m16_kernel): each wave holds two 16-query
@@ -8,6 +8,9 @@ probabilities of a 32-key half are packed as the B operand in the key order
 (4g .. 4g+3, 16+4g .. 16+4g+3) that the V^T operand is read in. The row
 maximum and sum combine the four groups; the reference maximum is only
 re-derived across the groups when some lane's own maximum could move it.
+The dQ pass of these shapes (one key group: grids too large for key groups)
+runs bwd_dq_m16_kernel, the same layout for S^T, dP^T and dQ^T += K^T dS^T,
+with the K tile read both row-wise and transposed through a chunk swizzle.
 These cases check that each shape takes that plan and cover the three masks
 (a window of 1 leaves most of a wave's rows with no allowed key in its first
 tiles), ragged N with a lone row in the last block, GQA and MQA, bf16 and
