@@ -954,13 +954,15 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
         // the probability overwrites the score.
         auto p_pair = [&](int u, int e) {
             const int r = u * 8 + 2 * e;
-            const float2 l2 = *reinterpret_cast<const float2*>(Ls + qoff(r) + 4 * h);
+            // (two float reads: the compiler cannot track a struct float2 read
+            // of LDS and would make it wait for the next step's loads)
+            const float l2[2] = {Ls[qoff(r) + 4 * h], Ls[qoff(r) + 4 * h + 1]};
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float pe[2];
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
-                    pe[w] = fast_exp2(fmaf(s[j][r + w], c, -(w ? l2.y : l2.x)));
+                    pe[w] = fast_exp2(fmaf(s[j][r + w], c, -(w ? l2[1] : l2[0])));
                     const int kq = kq0 + 32 * j;
                     if (MASKED && CAUSAL && kq > qoff(r + w)) pe[w] = 0.0f;
                     if (MASKED && WINDOW && qoff(r + w) > kq + W - 1) pe[w] = 0.0f;
@@ -976,13 +978,13 @@ void bwd_dkdv_wide_kernel(BwdParams p) {
             const int r = u * 8 + 2 * e;
             if constexpr (DROP) {
                 // dS = P ((dP M / (1-p)) - D_i)
-                const float2 nd = *reinterpret_cast<const float2*>(Ds + qoff(r) + 4 * h);
+                const float nd[2] = {Ds[qoff(r) + 4 * h], Ds[qoff(r) + 4 * h + 1]};
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int w = 0; w < 2; ++w)
                         dp[j][r + w] = (((keep[j] >> (r + w)) & 1u) ? dp[j][r + w] * p.drop.scale : 0.0f) +
-                                       (w ? nd.y : nd.x);
+                                       (w ? nd[1] : nd[0]);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
