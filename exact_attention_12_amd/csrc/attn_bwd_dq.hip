@@ -416,13 +416,12 @@ void bwd_dq_kernel(BwdParams p) {
 //  * dQ^T += K^T dS^T over the step's two 32-key halves: the lane's dS^T
 //    values are already the B operand (key order 4g..4g+3, 16+4g..16+4g+3
 //    in 16-lane group g), and K^T is read transposed in the same order.
-//  * The K tile is read row-wise (S^T) and transposed (K^T). Its pitch is an
-//    odd multiple of 32 bytes (the forward's V tile: the transposing read's
-//    two 16-lane groups served together hit 8 different 32-byte bank
-//    groups) and its 16-byte chunks are XOR-swizzled by bit 3 of the row,
-//    which moves rows r and r + 8 of a row read to different banks while a
-//    transposing read's 4 rows share one swizzle value. The V tile is read
-//    row-wise only (pitch an odd multiple of 16 bytes).
+//  * The K tile is read row-wise (S^T) and transposed (K^T), the V tile
+//    row-wise. Both have the forward's 16x16x32 pitch of 144 elements (288
+//    bytes), which serves both reads of this layout without bank conflicts
+//    (measured with SQ_LDS_BANK_CONFLICT; a 136-element pitch, or this one
+//    with its chunks swizzled by bit 3 of the row, doubles the LDS cycles
+//    of the row reads).
 //  * Each of the two K and two V buffers is its own LDS object, with the
 //    buffer known at compile time, so the transposing reads of the current
 //    buffer do not wait for the loads in flight into the other one.
@@ -442,8 +441,8 @@ __device__ __forceinline__ f32x4 dq_mfma16(e16x8 a, e16x8 b, f32x4 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-constexpr int kDq16KPitch = 144;  // elements: 288 bytes, 9 x 32
-static_assert((kDq16KPitch * 2 / 32) % 2 == 1 && kDq16KPitch >= 128 + 8, "");
+constexpr int kDq16Pitch = 144;  // elements: 288 bytes, 9 x 32
+static_assert((kDq16Pitch * 2 / 32) % 2 == 1 && kDq16Pitch >= 128 + 8, "");
 
 template <int DT, int MASK>
 __global__ __launch_bounds__(256, 2)
@@ -456,8 +455,8 @@ void bwd_dq_m16_kernel(BwdParams p) {
     constexpr int BC = 64;
     constexpr int KS = D / 32;     // contraction steps of S^T and dP^T
     constexpr int NDT = D / 16;    // 16-row tiles of dQ^T
-    constexpr int KP = kDq16KPitch;
-    constexpr int VP = k_pitch(D);
+    constexpr int KP = kDq16Pitch;
+    constexpr int VP = kDq16Pitch;
 
     __shared__ __attribute__((aligned(16))) e16 sK0[BC * KP];
     __shared__ __attribute__((aligned(16))) e16 sK1[BC * KP];
@@ -526,7 +525,7 @@ void bwd_dq_m16_kernel(BwdParams p) {
     }
     ku_end = max(ku_end, ku_begin);
 
-    // Tile loads straight to LDS; slot s of K row r holds chunk s ^ ((r >> 3) & 1).
+    // Tile loads straight to LDS.
     constexpr int CKK = KP / 8, CKV = VP / 8;
     constexpr int NLK = BC * CKK / 64, NLV = BC * CKV / 64;
     constexpr int LPWK = (NLK + NW - 1) / NW, LPWV = (NLV + NW - 1) / NW;
@@ -538,7 +537,7 @@ void bwd_dq_m16_kernel(BwdParams p) {
         for (int i = 0; i < LPWK; ++i) {
             const int chunk = (wave + i * NW) * 64 + lane;
             const int row = chunk / CKK;
-            const int lc = (chunk - row * CKK) ^ ((row >> 3) & 1);
+            const int lc = chunk - row * CKK;
             offk[i] = lc < D / 8 ? (uint32_t)row * sk2 + (uint32_t)lc * 16u : 0xFFFFFFF0u;
         }
 #pragma unroll
@@ -566,13 +565,13 @@ void bwd_dq_m16_kernel(BwdParams p) {
     };
 
     // Per-lane read offsets (elements); the other tiles are immediate offsets.
-    //  K rows (S^T operand): row 16 kt + l16, chunk 4 ks + g (swizzled).
+    //  K rows (S^T operand): row 16 kt + l16, dims 32 ks + 8 g.
     //  V rows (dP^T operand): row 16 kt + l16, dims 32 ks + 8 g.
     //  K^T (transposing read): lane 4t + s of group g reads key row 4 g + t
     //  (+ 32 jj, + 16 for the second half of the operand), dims 16 dt + 4 s.
-    const int krd = l16 * KP + 8 * (g ^ ((l16 >> 3) & 1));
+    const int krd = l16 * KP + 8 * g;
     const int vrd = l16 * VP + 8 * g;
-    const int ktr = (4 * g + (l16 >> 2)) * KP + 8 * (((l16 & 3) >> 1) ^ (g >> 1)) + 4 * (l16 & 1);
+    const int ktr = (4 * g + (l16 >> 2)) * KP + 4 * (l16 & 3);
 
     f32x4 dq[NDT][2];
 #pragma unroll

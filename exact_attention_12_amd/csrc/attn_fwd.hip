@@ -534,9 +534,12 @@ void fwd_kernel(FwdParams p) {
 //    probabilities are packed in place. The V^T operand takes the same key
 //    order: two transposing reads of 4 keys (rows 4g .. 4g+3 and 16 + 4g ..)
 //    by 16 dims. O^T is 8 x 2 tiles of 16x16, one query per lane column.
-//  * The V tile pitch is an odd multiple of 32 bytes modulo 256: the two
-//    16-lane groups served together read 8 rows at one column block, which
-//    then land on 8 different 32-byte bank groups.
+//  * Both tiles have a pitch of 144 elements (288 bytes, an odd multiple of
+//    32). Measured with SQ_LDS_BANK_CONFLICT on the part, that pitch serves
+//    both reads of this layout without conflicts: the 16-byte row reads of
+//    16 rows x 4 chunks (the S^T operand) and the transposing reads of 4 rows
+//    x 32 bytes per 16-lane group (V^T). The 136-element pitch that the
+//    32x32x16 kernels' row reads use takes twice the LDS cycles here.
 //  * The step loop is software pipelined across key blocks: step j computes
 //    the S^T products of block j + 1 while it turns block j's scores into
 //    probabilities and runs block j's O^T products (the region plan is in
@@ -548,8 +551,8 @@ void fwd_kernel(FwdParams p) {
 // Everything else (online softmax with the lazy reference maximum, tile
 // loads straight to LDS, causal/window skipping, launch order) is as in
 // fwd_kernel.
-constexpr int v16_pitch(int d) { return ((2 * d / 32) % 2 == 1 ? 2 * d : 2 * d + 32) / 2; }
-static_assert(v16_pitch(128) == 144 && (v16_pitch(128) * 2 / 32) % 2 == 1, "");
+constexpr int m16_pitch(int d) { return ((2 * d / 32) % 2 == 1 ? 2 * d : 2 * d + 32) / 2; }
+static_assert(m16_pitch(128) == 144 && (m16_pitch(128) * 2 / 32) % 2 == 1, "");
 // Head dims whose no-dropout 8-wave step loop runs on 16x16x32 products.
 // (d = 64 is bound by its softmax work, where the two query tiles per lane
 // cost more than the products gain; so are the 4-wave plans of small grids,
@@ -590,8 +593,8 @@ void fwd_m16_kernel(FwdParams p) {
     constexpr int BC = 64;
     constexpr int KS = D / 32;   // contraction steps of S^T = K Q^T
     constexpr int NDT = D / 16;  // 16-row tiles of O^T
-    constexpr int KP = k_pitch(D);
-    constexpr int VP = v16_pitch(D);
+    constexpr int KP = m16_pitch(D);
+    constexpr int VP = m16_pitch(D);
     constexpr int CPR = D / 8;
     static_assert(D % 32 == 0 && D <= 128 && FwdTile<D>::BLOCK_KV == BC, "16x16x32 step loop: 64-key tiles");
 
@@ -1314,7 +1317,7 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
     plan->block_kv = BC;
     plan->threads = waves * 64;
     plan->workgroups = (long long)((N + BQ - 1) / BQ) * B * Hq;
-    plan->lds_bytes = 2 * BC * (k_pitch(D) + (kProducts16<D> && !dropout && waves == 8 ? v16_pitch(D) : v_pitch(D))) * 2;
+    plan->lds_bytes = 2 * BC * (kProducts16<D> && !dropout && waves == 8 ? 2 * m16_pitch(D) : k_pitch(D) + v_pitch(D)) * 2;
 }
 
 bool fwd_plan(int B, int Hq, int N, int d, bool causal, bool dropout, FwdPlan* plan) {

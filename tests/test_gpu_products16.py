@@ -28,7 +28,7 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 D = 128
-LDS_BYTES = 2 * 64 * ((D + 8) + 144) * 2  # two K/V buffers, V pitch 288 bytes
+LDS_BYTES = 2 * 64 * (144 + 144) * 2  # two K and two V buffers, pitch 288 bytes
 
 # B, Hq, Hkv, N, mask, dtype, layout
 CASES = [
