@@ -91,7 +91,14 @@ void fwd_kernel(FwdParams p) {
     constexpr int BUF = BC * (KP + VP);
     static_assert(KG == 1 || (KG == 2 && BC == 64 && !DROP), "key groups: d <= 128, no dropout");
 
-    __shared__ __attribute__((aligned(16))) e16 smem[2 * BUF * KG];
+    // Buffer j of key group g sits at sBj + g * BUF. The two buffers are
+    // separate LDS objects: when the step loop names them at compile time
+    // (the mask-free steps run in pairs), the compiler can see that the
+    // transposing reads of the current buffer do not alias the loads in
+    // flight into the other one, instead of waiting for those loads (vmcnt
+    // 0) in the middle of every step.
+    __shared__ __attribute__((aligned(16))) e16 sB0[BUF * KG];
+    __shared__ __attribute__((aligned(16))) e16 sB1[BUF * KG];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,8 +134,8 @@ void fwd_kernel(FwdParams p) {
         for (int i = tid; i < 2 * KG * BC * PADC; i += T) {
             const int row = i / PADC;
             const int col = D + i % PADC;
-            const int bufi = row / BC;
-            smem[bufi * BUF + BC * KP + (row % BC) * VP + col] = (e16)0;
+            const int bufi = row / BC;  // 2 * group + buffer
+            ((bufi & 1) ? sB1 : sB0)[(bufi >> 1) * BUF + BC * KP + (row % BC) * VP + col] = (e16)0;
         }
     }
 
@@ -168,7 +175,7 @@ void fwd_kernel(FwdParams p) {
         }
     };
     auto store_tile = [&](int bufi) {
-        e16* Ks = smem + bufi * BUF;
+        e16* Ks = bufi ? sB1 : sB0;
         e16* Vs = Ks + BC * KP;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
@@ -211,12 +218,13 @@ void fwd_kernel(FwdParams p) {
             offv[i] = ch < CPR ? (uint32_t)row * sv2 + (uint32_t)ch * 16u : 0xFFFFFFF0u;
         }
     }
-    e16* const gsm = smem + grp * 2 * BUF;  // this group's two tile buffers
+    e16* const g0 = sB0 + grp * BUF;  // this group's two tile buffers
+    e16* const g1 = sB1 + grp * BUF;
     auto issue_tile = [&](int kv0, int bufi) {
         const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
         const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
         const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
-        char* kb_lds = reinterpret_cast<char*>(gsm + bufi * BUF);
+        char* kb_lds = reinterpret_cast<char*>(bufi ? g1 : g0);
         char* vb_lds = kb_lds + BC * KP * 2;
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
@@ -235,15 +243,27 @@ void fwd_kernel(FwdParams p) {
     const int kmid = kb_begin + (kb_end - kb_begin + 1) / 2;
     const int gs = KG == 1 ? kb_begin : (grp == 0 ? kb_begin : kmid);
     const int ge = KG == 1 ? kb_end : (grp == 0 ? kmid : kb_end);
+    // Key blocks [ku_begin, ku_end) need neither the per-wave skip nor a
+    // mask: every key is at or before the workgroup's first query (kv0 + BC
+    // - 1 <= q0), inside its last query's band (kv0 >= q0 + BQ - W) and
+    // before N. They run in a copy of the step without those tests. With
+    // one key group, block kb's tile sits in buffer (kb - ku_begin) & 1.
+    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
+    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
+    if (WINDOW) {
+        const int t = q0 + BQ - W;
+        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
+    }
+    ku_end = max(ku_end, ku_begin);
     if constexpr (DIRECT) {
         if (KG == 1)
-            issue_tile(kb_begin * BC, kb_begin & 1);
+            issue_tile(kb_begin * BC, (kb_begin - ku_begin) & 1);
         else if (gs < ge)
             issue_tile(gs * BC, 0);
         __builtin_amdgcn_s_waitcnt(0);
     } else {
         load_tile(kb_begin * BC);
-        store_tile(kb_begin & 1);
+        store_tile((kb_begin - ku_begin) & 1);
     }
     __syncthreads();
 
@@ -275,7 +295,7 @@ void fwd_kernel(FwdParams p) {
         }
 
         const int kv0 = kb * BC;
-        const e16* Ks = gsm + bufi * BUF;
+        const e16* Ks = bufi ? g1 : g0;
         const e16* Vs = Ks + BC * KP;
         const bool active = has && (!MASKED || !CAUSAL || (kv0 <= qw0 + 31 && (!WINDOW || kv0 + BC - 1 >= qw0 - W + 1)));
         if (active) {
@@ -433,23 +453,23 @@ void fwd_kernel(FwdParams p) {
             store_tile(bufi ^ 1);
         __syncthreads();
     };
-    // Key blocks [ku_begin, ku_end) need neither the per-wave skip nor a
-    // mask: every key is at or before the workgroup's first query (kv0 + BC
-    // - 1 <= q0), inside its last query's band (kv0 >= q0 + BQ - W) and
-    // before N. They run in a copy of the step without those tests.
-    int ku_begin = kb_begin, ku_end = min(kb_end, N / BC);
-    if (CAUSAL) ku_end = min(ku_end, (q0 + 1) / BC);
-    if (WINDOW) {
-        const int t = q0 + BQ - W;
-        ku_begin = min(kb_end, max(kb_begin, t > 0 ? (t + BC - 1) / BC : 0));
-    }
-    ku_end = max(ku_end, ku_begin);
     float lt;
     if constexpr (KG == 1) {
+        // Mask-free blocks in pairs (buffers known at compile time); a last
+        // unpaired one joins the masked blocks after them, whose masks then
+        // change nothing. With dropout the second copy of the step costs
+        // registers (spills), so there the buffers stay chosen at run time.
         int kb = kb_begin;
-        for (; kb < ku_begin; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::true_type{});
-        for (; kb < ku_end; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::false_type{});
-        for (; kb < kb_end; ++kb) run_step(kb, kb & 1, kb_end - 1, true, std::true_type{});
+        for (; kb < ku_begin; ++kb) run_step(kb, (kb - ku_begin) & 1, kb_end - 1, true, std::true_type{});
+        if constexpr (DROP) {
+            for (; kb < ku_end; ++kb) run_step(kb, (kb - ku_begin) & 1, kb_end - 1, true, std::false_type{});
+        } else {
+            for (; kb + 1 < ku_end; kb += 2) {
+                run_step(kb, 0, kb_end - 1, true, std::false_type{});
+                run_step(kb + 1, 1, kb_end - 1, true, std::false_type{});
+            }
+        }
+        for (; kb < kb_end; ++kb) run_step(kb, (kb - ku_begin) & 1, kb_end - 1, true, std::true_type{});
         lt = sum_across_halves(l);  // the two half-row sums
     } else {
         // Both groups step together (one barrier per step); group 0 has the
@@ -468,8 +488,8 @@ void fwd_kernel(FwdParams p) {
         // waited for its own loads before the last barrier).
         const float lg = sum_across_halves(l);
         constexpr int OSZ = WG * NDT * 16 * 64;
-        static_assert((OSZ + 2 * WG * 64) * 4 <= 2 * KG * BUF * 2, "merge data must fit the tile buffers");
-        float* xs = reinterpret_cast<float*>(smem);
+        static_assert((OSZ + 2 * WG * 64) * 4 <= KG * BUF * 2, "merge data must fit the first tile buffers");
+        float* xs = reinterpret_cast<float*>(sB0);
         if (grp == 1) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
