@@ -130,3 +130,19 @@ def test_traffic_summary_finds_the_wide_dkdv_kernel(tmp_path, monkeypatch):
     _write_counters(tmp_path / "w", [(cal, "WRITE_SIZE", 4096.0, 0, 1), (dk, "WRITE_SIZE", 100.0, 0, 1)])
     bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path), "c5_bwd_d128", 4)
     assert bench.read_traffic("bwd_dkdv_kernel", "c5_bwd_d128") == pytest.approx((500.0 * 2 + 100.0) * 1024.0)
+
+
+@pytest.mark.parametrize("kernel,symbol", [
+    ("fwd_kernel", "void attn::fwd_m16_kernel<0, 128, 1, 8>(attn::FwdParams)"),
+    ("fwd_kernel", "void attn::fwd_split_kernel<0, 64, 0, 8>(attn::FwdParams)"),
+    ("bwd_dq_kernel", "void attn::bwd_dq_m16_kernel<0, 1>(attn::BwdParams)"),
+])
+def test_traffic_summary_finds_the_16x16x32_and_split_kernels(tmp_path, monkeypatch, kernel, symbol):
+    # the forward and dQ pass run other kernels than their 32x32x16 step loops
+    # on some plans; the traffic summary must count them under the pass's name
+    monkeypatch.setattr(bench, "traffic_file", lambda k, wl: str(tmp_path / f"traffic_{k}_{wl}.txt"))
+    cal = "void at::native::vectorized_elementwise_kernel<neg_kernel>"
+    _write_counters(tmp_path / "f", [(cal, "FETCH_SIZE", 2048.0, 0, 1), (symbol, "FETCH_SIZE", 300.0, 0, 1)])
+    _write_counters(tmp_path / "w", [(cal, "WRITE_SIZE", 4096.0, 0, 1), (symbol, "WRITE_SIZE", 50.0, 0, 1)])
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path), "c5_bwd_d128", 4)
+    assert bench.read_traffic(kernel, "c5_bwd_d128") == pytest.approx((300.0 * 2 + 50.0) * 1024.0)
