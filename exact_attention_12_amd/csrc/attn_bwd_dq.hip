@@ -712,9 +712,16 @@ void bwd_dq_m16_kernel(BwdParams p) {
     // run in pairs whose buffers are known at compile time; the masked
     // blocks before and after them (and a last unpaired mask-free block,
     // for which the masks change nothing) pick their buffers at run time.
+    // (loads go through a branch on the buffer, not a select of addresses:
+    // each then names its LDS object, which unoptimised builds need)
     auto run_masked = [&](int kb) {
         const bool par = (kb - ku_begin) & 1;
-        if (kb + 1 < kb_end) issue(kb + 1, par ? sK0 : sK1, par ? sV0 : sV1);
+        if (kb + 1 < kb_end) {
+            if (par)
+                issue(kb + 1, sK0, sV0);
+            else
+                issue(kb + 1, sK1, sV1);
+        }
         step(kb, par ? sK1 : sK0, par ? sV1 : sV0, std::true_type{});
         __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
         __syncthreads();
@@ -729,10 +736,10 @@ void bwd_dq_m16_kernel(BwdParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    {
-        const bool par = (kb_begin - ku_begin) & 1;
-        issue(kb_begin, par ? sK1 : sK0, par ? sV1 : sV0);
-    }
+    if ((kb_begin - ku_begin) & 1)
+        issue(kb_begin, sK1, sV1);
+    else
+        issue(kb_begin, sK0, sV0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int kb = kb_begin;

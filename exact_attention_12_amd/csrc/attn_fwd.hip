@@ -220,11 +220,11 @@ void fwd_kernel(FwdParams p) {
     }
     e16* const g0 = sB0 + grp * BUF;  // this group's two tile buffers
     e16* const g1 = sB1 + grp * BUF;
-    auto issue_tile = [&](int kv0, int bufi) {
+    auto issue_into = [&](int kv0, e16* buf) {
         const uint32_t sk2 = (uint32_t)skn * 2u, sv2 = (uint32_t)svn * 2u;
         const auto rk = buf_rsrc(Kh + (long long)kv0 * skn, (uint32_t)(N - kv0 - 1) * sk2 + D * 2);
         const auto rv = buf_rsrc(Vh + (long long)kv0 * svn, (uint32_t)(N - kv0 - 1) * sv2 + D * 2);
-        char* kb_lds = reinterpret_cast<char*>(bufi ? g1 : g0);
+        char* kb_lds = reinterpret_cast<char*>(buf);
         char* vb_lds = kb_lds + BC * KP * 2;
 #pragma unroll
         for (int i = 0; i < LPWK; ++i) {
@@ -236,6 +236,15 @@ void fwd_kernel(FwdParams p) {
             const int j = gw + i * WG;
             if (NLV % WG == 0 || j < NLV) buf_load16_to_lds(rv, vb_lds + j * 1024, offv[i]);
         }
+    };
+    // A branch rather than a select of the two buffers' addresses: each load
+    // then names its LDS object (a selected generic address would have to be
+    // cast back to LDS at run time, which unoptimised builds cannot emit).
+    auto issue_tile = [&](int kv0, int bufi) {
+        if (bufi)
+            issue_into(kv0, g1);
+        else
+            issue_into(kv0, g0);
     };
 
     // Key tiles of this group: [gs, ge). With one group that is the whole

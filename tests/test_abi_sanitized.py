@@ -28,8 +28,10 @@ def test_abi_validation_under_asan_and_ubsan():
         pytest.skip("no ROCm toolchain")
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    # device code with the library's own device flags (build.DEVICE_FLAGS)
+    from exact_attention_12_amd import build
     common = ["-x", "hip", "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
-              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+              "-I", os.path.join(ROOT, "include"), "-I", CSRC, *build.DEVICE_FLAGS]
     with tempfile.TemporaryDirectory() as tmp:
         objs = []
         procs = []
