@@ -47,7 +47,8 @@
  *   Scale: the factor applied to Q K^T before the softmax, finite and > 0
  *     (callers usually pass 1/sqrt(d)).
  *   Memory: every pointer is a device pointer owned by the caller; the
- *     library never allocates, frees or synchronises. Buffers must stay alive
+ *     library never allocates, frees or synchronises (attn_bwd_noalloc uses
+ *     a fixed array of its own instead of a caller workspace). Buffers must stay alive
  *     until the stream has run the enqueued work. Outputs are overwritten,
  *     never accumulated into. Device pointers must be 16-byte aligned.
  *   Streams: `stream` is a hipStream_t (NULL means the default stream). All
@@ -55,8 +56,10 @@
  *   Errors: every argument is checked on the host before anything is
  *     enqueued; on any error nothing is launched and outputs are untouched.
  *     Device-side faults surface at the caller's next synchronisation.
- *   Threads: the library holds no mutable global state; concurrent calls on
- *     different streams are safe.
+ *   Threads: apart from attn_bwd_noalloc's fixed scratch array (whose
+ *     concurrent use races, see there) and a per-thread copy of the last HIP
+ *     error string, the library holds no mutable global state; concurrent
+ *     calls of every other entry point on different streams are safe.
  */
 #ifndef ATTN_H
 #define ATTN_H
