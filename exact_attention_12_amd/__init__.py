@@ -73,6 +73,7 @@ class AttnPlan(ctypes.Structure):
         ("lds_bytes", ctypes.c_int),
         ("key_splits", ctypes.c_int),
         ("key_groups", ctypes.c_int),
+        ("products16", ctypes.c_int),
     ]
 
 

@@ -624,6 +624,7 @@ attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn
     plan->lds_bytes = fp.lds_bytes;
     plan->key_splits = fp.key_splits;
     plan->key_groups = fp.key_groups;
+    plan->products16 = fp.m16;
     return ATTN_OK;
 }
 

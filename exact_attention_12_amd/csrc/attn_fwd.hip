@@ -57,10 +57,11 @@
 //    combine exactly: M = max(m0, m1), l = sum_g 2^(m_g - M) l_g,
 //    O = sum_g 2^(m_g - M) O_g. (Two groups of 4 waves over 128 rows, two
 //    waves per SIMD, gained nothing: the groups then share each SIMD.)
-//  * d = 128 without dropout on the 8-wave plan: fwd_m16_kernel runs the
-//    step loop on 16x16x32 products, which the chip sustains at a higher
-//    rate than 32x32x16 ones, pipelined across key blocks (layout and
-//    schedule in its own comment).
+//  * d = 128 without dropout on the grids that other head dims run on 8
+//    waves: fwd_m16_kernel runs the step loop on 16x16x32 products, which
+//    the chip sustains at a higher rate than 32x32x16 ones, pipelined across
+//    key blocks (layout and schedule in its own comment), in workgroups of
+//    4 waves (128 rows).
 #include <type_traits>
 
 #include "attn_device.h"
@@ -542,7 +543,7 @@ void fwd_kernel(FwdParams p) {
 }
 
 // ------------------------------------------------------------------
-// d = 128 without dropout, 8 waves: the same step loop on 16x16x32 products.
+// d = 128 without dropout, large grids: the same step loop on 16x16x32 products.
 //
 // The chip sustains v_mfma_f32_16x16x32_bf16 at a higher clock than the
 // 32x32x16 product on the same random operands (the matrix cores are equally
@@ -582,9 +583,9 @@ void fwd_kernel(FwdParams p) {
 // fwd_kernel.
 constexpr int m16_pitch(int d) { return ((2 * d / 32) % 2 == 1 ? 2 * d : 2 * d + 32) / 2; }
 static_assert(m16_pitch(128) == 144 && (m16_pitch(128) * 2 / 32) % 2 == 1, "");
-// Head dims whose no-dropout 8-wave step loop runs on 16x16x32 products.
-// (d = 64 is bound by its softmax work, where the two query tiles per lane
-// cost more than the products gain; so are the 4-wave plans of small grids,
+// Head dims whose no-dropout step loop runs on 16x16x32 products on large
+// grids. (d = 64 is bound by its softmax work, where the two query tiles per
+// lane cost more than the products gain; so are the plans of small grids,
 // which stay on fwd_kernel.)
 template <int D> constexpr bool kProducts16 = D == 128;
 
@@ -1252,11 +1253,16 @@ static hipError_t launch_fwd_dmd(const FwdParams& p, const FwdPlan& plan, hipStr
                 return hipGetLastError();
             }
         }
+        if (plan.waves == 4 && plan.m16) {
+            if constexpr (kProducts16<D> && !DROP) {
+                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 4>), grid, block, 0, stream, p);
+                return hipGetLastError();
+            } else {
+                return hipErrorInvalidValue;
+            }
+        }
         if (plan.waves == 8) {
-            if constexpr (kProducts16<D> && !DROP)
-                hipLaunchKernelGGL((fwd_m16_kernel<DT, D, MASK, 8>), grid, block, 0, stream, p);
-            else
-                hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP, 1>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((fwd_kernel<DT, D, MASK, 8, DROP, 1>), grid, block, 0, stream, p);
             return hipGetLastError();
         }
     }
@@ -1300,13 +1306,19 @@ static hipError_t launch_fwd_t(const FwdParams& p, int d, int mask, const FwdPla
 // Tile plan. 8 waves (256 rows) per workgroup share one K/V pipeline, which
 // halves global-load issue and LDS stores per row; used while that still
 // gives every CU a workgroup. Shorter sequences use 4 waves (twice the
-// workgroups); d > 128 always uses 4.
+// workgroups); d > 128 always uses 4. d = 128 without dropout runs those
+// large grids on the 16x16x32 kernel with 4 waves instead: its 254 VGPRs
+// leave room for 8 waves per CU, so two 128-row workgroups share a CU and
+// each one's prologue and epilogue overlap the other's step loop (1-1.5 %
+// faster than one 256-row workgroup per CU on the causal 4096- and
+// 16384-key shapes, the same on the grouped 8192-key one).
 template <int D>
 static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* plan) {
     const long long wg256 = (long long)((N + 255) / 256) * B * Hq;
     const long long wg128 = (long long)((N + 127) / 128) * B * Hq;
     plan->key_splits = 1;
     plan->key_groups = 1;
+    plan->m16 = 0;
     // Short sequences whose grid of 128-row workgroups would leave CUs idle:
     // the key-split kernel (one workgroup per 32 rows, waves over the keys).
     if (D <= kSplitMaxD && !dropout && N <= kSplitMaxKeys && wg128 < kSplitMaxGrid) {
@@ -1338,7 +1350,11 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
             return;
         }
     }
-    const int waves = (D <= 128 && wg256 >= (causal ? 512 : 256)) ? 8 : 4;
+    int waves = (D <= 128 && wg256 >= (causal ? 512 : 256)) ? 8 : 4;
+    if (kProducts16<D> && !dropout && waves == 8) {
+        waves = 4;
+        plan->m16 = 1;
+    }
     const int BQ = waves * 32;
     plan->rows_per_wave = 32;
     plan->waves = waves;
@@ -1346,7 +1362,7 @@ static void plan_d(int B, int Hq, int N, bool causal, bool dropout, FwdPlan* pla
     plan->block_kv = BC;
     plan->threads = waves * 64;
     plan->workgroups = (long long)((N + BQ - 1) / BQ) * B * Hq;
-    plan->lds_bytes = 2 * BC * (kProducts16<D> && !dropout && waves == 8 ? 2 * m16_pitch(D) : k_pitch(D) + v_pitch(D)) * 2;
+    plan->lds_bytes = 2 * BC * (plan->m16 ? 2 * m16_pitch(D) : k_pitch(D) + v_pitch(D)) * 2;
 }
 
 bool fwd_plan(int B, int Hq, int N, int d, bool causal, bool dropout, FwdPlan* plan) {

@@ -183,6 +183,7 @@ struct FwdPlan {
     int lds_bytes;
     int key_splits;     // > 1: the key-split kernel, its waves each take 64 keys of one 32-row tile
     int key_groups;     // 2: the step-loop kernel with its 4 waves in two groups over one 64-row block's keys
+    int m16;            // 1: the 16x16x32 step loop (fwd_m16_kernel) on a 4-wave plan
 };
 
 // SIMDs of the part (256 compute units x 4), for the load estimate below.

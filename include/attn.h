@@ -379,6 +379,10 @@ typedef struct attn_plan {
                         half of the block's key tiles, the two softmax states
                         combined in LDS (small grids, where the longest
                         block's key loop would decide the time); else 1 */
+    int products16;  /* 1: the step loop on v_mfma_f32_16x16x32 products
+                        (d = 128 without dropout on grids of 512 or more
+                        256-row blocks, causal; 256 unmasked); 0: on
+                        32x32x16 products */
 } attn_plan;
 
 attn_status attn_fwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, attn_plan* plan);

@@ -165,6 +165,16 @@ def test_fwd_plan(L):
                   (4, 16, 16, 2048, 64, False), (1, 16, 16, 4096, 80, True), (1, 16, 16, 4096, 128, True),
                   (1, 2, 2, 4096, 192, True), (1, 2, 2, 4096, 256, False)]:
         assert ea.fwd_plan(*shape)["key_groups"] == 1, shape
+    # d = 128 on those grids: the 16x16x32 step loop, 128-row workgroups of 4 waves;
+    # other head dims: 8 waves on 32x32x16 products
+    for shape in [(2, 32, 32, 4096, 128, True), (1, 16, 16, 16384, 128, True), (1, 64, 8, 8192, 128, True),
+                  (2, 64, 8, 1024, 128, False)]:
+        p = ea.fwd_plan(*shape)
+        assert p["products16"] == 1 and p["threads"] == 256 and p["block_q"] == 128, shape
+        assert p["lds_bytes"] == 2 * 64 * (144 + 144) * 2, shape
+    for shape in [(2, 32, 32, 4096, 64, True), (2, 32, 32, 4096, 80, True), (1, 32, 32, 1000, 128, True),
+                  (1, 8, 8, 400, 128)]:
+        assert ea.fwd_plan(*shape)["products16"] == 0, shape
     for N, nw in [(1, 2), (64, 2), (128, 2), (129, 4), (256, 4), (257, 8), (512, 8)]:
         assert ea.fwd_plan(1, 2, 1, N, 80, True)["key_splits"] == nw, N
     for d in ea.SUPPORTED_HEAD_DIMS:

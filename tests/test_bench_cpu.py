@@ -133,7 +133,7 @@ def test_traffic_summary_finds_the_wide_dkdv_kernel(tmp_path, monkeypatch):
 
 
 @pytest.mark.parametrize("kernel,symbol", [
-    ("fwd_kernel", "void attn::fwd_m16_kernel<0, 128, 1, 8>(attn::FwdParams)"),
+    ("fwd_kernel", "void attn::fwd_m16_kernel<0, 128, 1, 4>(attn::FwdParams)"),
     ("fwd_kernel", "void attn::fwd_split_kernel<0, 64, 0, 8>(attn::FwdParams)"),
     ("bwd_dq_kernel", "void attn::bwd_dq_m16_kernel<0, 1>(attn::BwdParams)"),
 ])

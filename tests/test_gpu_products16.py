@@ -1,8 +1,9 @@
 """The d = 128 forward and dQ pass on 16x16x32 products against the fp64
 oracle (needs an MI355X).
 
-Without dropout, grids large enough for the 8-wave plan run the forward's
-step loop on 16x16x32 products (fwd_m16_kernel): each wave holds two 16-query
+Without dropout, grids large enough for the 8-wave plan at other head dims
+run the forward's step loop on 16x16x32 products (fwd_m16_kernel, 4 waves
+per workgroup, two workgroups per CU): each wave holds two 16-query
 tiles, its lanes hold 16 keys of a query in four 16-lane groups, and the
 probabilities of a 32-key half are packed as the B operand in the key order
 (4g .. 4g+3, 16+4g .. 16+4g+3) that the V^T operand is read in. The row
@@ -16,7 +17,7 @@ These cases check that each shape takes that plan and cover the three masks
 tiles), ragged N with a lone row in the last block, GQA and MQA, bf16 and
 fp16, BHSD and BSHD; the backward runs on this forward's LSE and is checked
 too. The rows whose running maximum moves again and again along the
-sequence are covered on this plan by the rescale tests' 8-wave cases."""
+sequence are covered on this plan by the rescale tests' m16 cases."""
 
 import pytest
 import torch
@@ -68,7 +69,8 @@ def test_products16_forward(cfg):
     parity.log(f"16x16x32 forward case {ids(cfg)}")
     kw, causal, window = mask_args(mask)
     plan = ea.fwd_plan(B, Hq, Hkv, N, D, causal)
-    assert plan["key_splits"] == 1 and plan["key_groups"] == 1 and plan["threads"] == 512, plan
+    assert plan["key_splits"] == 1 and plan["key_groups"] == 1, plan
+    assert plan["products16"] == 1 and plan["threads"] == 256 and plan["block_q"] == 128, plan
     assert plan["lds_bytes"] == LDS_BYTES, plan
     inp = si.make_inputs(B, Hq, Hkv, N, D, seed=8100 + N + Hkv, with_do=True, dtype=dt)
     g = {key: si.in_layout(t.cuda(), layout) for key, t in inp.items()}
@@ -88,10 +90,10 @@ def test_products16_forward(cfg):
     parity.check_bwd(inp, grads, scale, causal, kv_heads, Hq, Hkv, ids(cfg), window=window)
 
 
-def test_products16_plan_only_on_8_waves():
-    # the 4-wave plans of smaller grids stay on the 32x32x16 kernel (its V pitch)
+def test_products16_plan_only_on_large_grids():
+    # the plans of smaller grids stay on the 32x32x16 kernel (its V pitch)
     p = ea.fwd_plan(1, 32, 32, 1000, D, True)
-    assert p["threads"] == 256 and p["key_groups"] == 1, p
+    assert p["threads"] == 256 and p["key_groups"] == 1 and p["products16"] == 0, p
     assert p["lds_bytes"] == 2 * 64 * ((D + 8) + 160) * 2, p
 
 

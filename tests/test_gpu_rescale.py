@@ -24,8 +24,9 @@ compared with the oracle element by element (O, LSE) and per tensor (dQ, dK,
 dV), at d = 64 and 128, with no mask, causal and sliding-window masks, in
 bf16 and fp16, on the three plans of the step-loop forward: two key groups
 of 4 waves over a 128-row block (small grids, where each group keeps its own
-reference maximum and the two are combined at the end), and one group of 4
-or of 8 waves (larger grids).
+reference maximum and the two are combined at the end), one group of 4 or
+of 8 waves (larger grids), and at d = 128 on the larger grids one group of 4
+waves on 16x16x32 products.
 """
 
 import numpy as np
@@ -45,7 +46,8 @@ LAZY = 8.0     # the reference maximum moves when a block beats it by more than 
 
 CASES = [
     # B, Hq, Hkv, N, d, mask, dtype, plan the shape selects (kg2: two key
-    # groups of 4 waves; w4, w8: one group of 4 or 8 waves)
+    # groups of 4 waves; w4, w8: one group of 4 or 8 waves; m16: one group
+    # of 4 waves on 16x16x32 products)
     (1, 4, 2, 1000, 64, "causal", "bf16", "kg2"),
     (1, 4, 2, 1000, 128, "causal", "bf16", "kg2"),
     (1, 2, 1, 777, 128, "none", "bf16", "kg2"),
@@ -55,9 +57,9 @@ CASES = [
     (1, 4, 4, 999, 128, "causal", "fp16", "kg2"),
     (1, 124, 31, 1000, 128, "causal", "bf16", "w4"),
     (1, 124, 4, 1000, 64, 200, "fp16", "w4"),
-    (2, 64, 8, 1024, 128, "causal", "bf16", "w8"),
+    (2, 64, 8, 1024, 128, "causal", "bf16", "m16"),
     (1, 64, 8, 1024, 64, "none", "bf16", "w8"),
-    (2, 64, 16, 1024, 128, 200, "bf16", "w8"),
+    (2, 64, 16, 1024, 128, 200, "bf16", "m16"),
 ]
 
 
@@ -105,7 +107,8 @@ def test_rescale_fwd_bwd(cfg):
     else:
         kw, causal, window = dict(window=mask), True, mask
     fp = ea.fwd_plan(B, Hq, Hkv, N, d, causal)
-    got = "kg2" if fp["key_groups"] == 2 else "w{}".format(fp["threads"] // 64)
+    got = ("kg2" if fp["key_groups"] == 2 else "m16" if fp["products16"] else
+           "w{}".format(fp["threads"] // 64))
     assert fp["key_splits"] == 1 and got == plan, f"shape selects the {got} forward plan"
 
     # a band holds fewer keys, so the norms grow faster there
